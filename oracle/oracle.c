@@ -1,0 +1,285 @@
+/*
+ * CPU oracle for the W4A8 linear layer — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or constant with the
+ * HIP library: everything below is written out from the definitions, with
+ * plain loops, so that it can be checked by eye.
+ *
+ * What it computes (the layer the pages describe):
+ *   "The 4-bit CPU path", section "W4A8": GPTQ-packed int4 weights times
+ *   activations quantised to int8; the kernel uses the checkpoint's integer
+ *   zero points (or the constant 8 for a symmetric grid).
+ *   "The 4-bit CPU path", section "Building a checkpoint": group size 128.
+ *   "EgoPQ Real-Serving Handoff", section "2. External Artifacts": the native
+ *   packed path needs exact per-group scale and zero metadata, and is not
+ *   interchangeable with a float fake-quant path — so the oracle is the exact
+ *   integer path, not a float emulation.
+ *   "Serve a pre-quantized int8 weight-only DiT ...", comments "Directive ..."
+ *   and "Round two ...": isolate one linear against a reference
+ *   dequant-then-matmul, and make sure that reference applies the activation
+ *   scale.
+ *
+ * Readings taken where the pages are silent (each also listed in the design doc):
+ *   - activations: symmetric per-token (per-row) int8, scale sa = absmax/127
+ *     in float32 with IEEE division; codes rint(x/sa) (ties to even) clamped
+ *     to [-127, 127]; an all-zero row gives sa = 0 and codes 0;
+ *   - weights: W[n][k] = s[n][g] * (q[n][k] - z[n][g]) with q, z integers in
+ *     0..15, s float32, g = k / group over contiguous groups of K;
+ *   - per group an exact integer P[m][n][g] = sum_k qa[m][k]*(q[n][k]-z[n][g]);
+ *   - y[m][n] = sa[m] * sum_g s[n][g] * P[m][n][g], evaluated here in float64
+ *     and NOT rounded (the bf16 output is compared against this value).
+ *
+ * The quantisation decision (which int8 code) is taken in float32, the
+ * precision the GPU kernel takes it in; everything after the integer products
+ * is float64.
+ *
+ * Parity pins live in tests/test_oracle_pins.py (brute force, closed forms,
+ * invariants, planted mutants).  Compile-time ORACLE_MUTANT values plant one
+ * plausible mistake each, so the tests can show every mistake is caught.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_NONFINITE (-2)
+#define ORACLE_RANGE (-3)
+
+/* Largest |P| one group of 128 can reach: 128 * 127 * 15. */
+#define ORACLE_P_BOUND 243840
+
+int oracle_version(void) { return 1 + 100 * ORACLE_MUTANT; }
+
+static float widen_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Symmetric per-token int8 quantisation of one float32 row. */
+static int quant_row(const float* x, int64_t K, int8_t* qa, float* sa_out) {
+    float amax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        if (!isfinite(x[k])) return ORACLE_NONFINITE;
+        float a = fabsf(x[k]);
+        if (a > amax) amax = a;
+    }
+#if ORACLE_MUTANT == 3
+    float sa = amax / 128.0f;            /* planted: wrong symmetric range */
+#else
+    float sa = amax / 127.0f;
+#endif
+    *sa_out = sa;
+    for (int64_t k = 0; k < K; ++k) {
+        if (amax == 0.0f) {
+            qa[k] = 0;
+            continue;
+        }
+        float t = x[k] / sa;
+#if ORACLE_MUTANT == 2
+        float r = roundf(t);             /* planted: ties away from zero */
+#else
+        float r = rintf(t);              /* default mode: ties to even */
+#endif
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        qa[k] = (int8_t)r;
+    }
+    return ORACLE_OK;
+}
+
+int oracle_quant_act_f32(const float* x, int64_t M, int64_t K, int8_t* qa, float* sa) {
+    if (!x || !qa || !sa || M < 0 || K <= 0) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+    for (int64_t m = 0; m < M; ++m) {
+        int r = quant_row(x + m * K, K, qa + m * K, sa + m);
+        if (r != ORACLE_OK) rc = r;
+    }
+    return rc;
+}
+
+int oracle_quant_act_bf16(const uint16_t* x, int64_t M, int64_t K, int8_t* qa, float* sa) {
+    if (!x || !qa || !sa || M < 0 || K <= 0) return ORACLE_BAD_ARG;
+    float* row = (float*)malloc((size_t)K * sizeof(float));
+    if (!row) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) row[k] = widen_bf16(x[m * K + k]);
+        int r = quant_row(row, K, qa + m * K, sa + m);
+        if (r != ORACLE_OK) rc = r;
+    }
+    free(row);
+    return rc;
+}
+
+/* One exact per-group integer dot product. */
+static int64_t group_dot(const int8_t* qa_row, const uint8_t* q_row, int zero,
+                         int64_t k0, int32_t group) {
+    int64_t p = 0;
+    for (int64_t k = k0; k < k0 + group; ++k) {
+#if ORACLE_MUTANT == 1
+        p += (int64_t)qa_row[k] * (int64_t)q_row[k];          /* planted: zero point dropped */
+#elif ORACLE_MUTANT == 6
+        int64_t kk = (k + 1 < k0 + group) ? k + 1 : k0;       /* planted: weights shifted by one k */
+        p += (int64_t)qa_row[k] * ((int64_t)q_row[kk] - zero);
+#else
+        p += (int64_t)qa_row[k] * ((int64_t)q_row[k] - (int64_t)zero);
+#endif
+    }
+    return p;
+}
+
+static int zero_at(const uint8_t* z, int64_t N, int64_t G, int64_t n, int64_t g) {
+#if ORACLE_MUTANT == 4
+    /* planted: zero plane read transposed ([G][N] instead of [N][G]) */
+    int64_t idx = g * N + n;
+    return z[idx % (N * G)];
+#else
+    (void)N;
+    return z[n * G + g];
+#endif
+}
+
+/*
+ * P[m][n][g] for rows m0..m1-1 (stored at P[(m-m0)][n][g]).
+ * Codes q[N][K] and zeros z[N][G] are one unsigned value per byte.
+ */
+int oracle_group_partials(const int8_t* qa, const uint8_t* q, const uint8_t* z,
+                          int64_t M, int64_t N, int64_t K, int32_t group,
+                          int64_t m0, int64_t m1, int32_t* P) {
+    if (!qa || !q || !z || !P || group <= 0 || K % group || M < 0 || N < 0) return ORACLE_BAD_ARG;
+    if (m0 < 0 || m1 > M || m0 > m1) return ORACLE_BAD_ARG;
+    int64_t G = K / group;
+    int rc = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t p = group_dot(qa + m * K, q + n * K, zero_at(z, N, G, n, g), g * group, group);
+                if (p > ORACLE_P_BOUND || p < -ORACLE_P_BOUND) {
+#pragma omp atomic write
+                    rc = ORACLE_RANGE;
+                }
+                P[((m - m0) * N + n) * G + g] = (int32_t)p;
+            }
+        }
+    }
+    return rc;
+}
+
+/*
+ * y[m][n] (float64, unrounded) for rows m0..m1-1 and columns n0..n1-1,
+ * stored at y[(m-m0)*(n1-n0) + (n-n0)].
+ */
+int oracle_linear(const int8_t* qa, const float* sa, const uint8_t* q, const uint8_t* z,
+                  const float* s, int64_t M, int64_t N, int64_t K, int32_t group,
+                  int64_t m0, int64_t m1, int64_t n0, int64_t n1, double* y) {
+    if (!qa || !sa || !q || !z || !s || !y) return ORACLE_BAD_ARG;
+    if (group <= 0 || K % group || m0 < 0 || m1 > M || m0 > m1 || n0 < 0 || n1 > N || n0 > n1)
+        return ORACLE_BAD_ARG;
+    int64_t G = K / group;
+    int64_t W = n1 - n0;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = n0; n < n1; ++n) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t p = group_dot(qa + m * K, q + n * K, zero_at(z, N, G, n, g), g * group, group);
+                acc += (double)s[n * G + g] * (double)p;
+            }
+#if ORACLE_MUTANT == 5
+            y[(m - m0) * W + (n - n0)] = acc;                  /* planted: activation scale missing */
+#else
+            y[(m - m0) * W + (n - n0)] = (double)sa[m] * acc;
+#endif
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The packed weight format of the HIP library, written out from its
+ * specification (layout version 1) so that the library's packing can be
+ * compared byte for byte.  With G = K/128, NB = N/16:
+ *   codes plane,  N*K/2 bytes at offset 0:
+ *     block (nb, g) = 1024 bytes at ((nb*G + g) * 1024); inside it, lane
+ *     L = 16*j + c (j = 0..3, c = 0..15) owns bytes [16L, 16L+16); byte i of
+ *     that run holds q[16nb+c][128g+16j+i] in its low nibble and
+ *     q[16nb+c][128g+64+16j+i] in its high nibble;
+ *   zeros plane,  N*G/2 bytes at Z0 = round_up(N*K/2, 256):
+ *     block (nb, g) = 8 bytes at Z0 + (nb*G + g)*8; byte c/2 holds
+ *     z[16nb+c][g] in its low nibble for even c, high nibble for odd c;
+ *   scales plane, 4*N*G bytes at S0 = round_up(Z0 + N*G/2, 256):
+ *     float32 at index (nb*G + g)*16 + c equals s[16nb+c][g], bit for bit.
+ */
+static int64_t round_up256(int64_t v) { return (v + 255) / 256 * 256; }
+
+int64_t oracle_layout_bytes(int64_t N, int64_t K) {
+    int64_t G = K / 128;
+    int64_t z0 = round_up256(N * K / 2);
+    int64_t s0 = round_up256(z0 + N * G / 2);
+    return s0 + 4 * N * G;
+}
+
+int oracle_layout_pack(const uint8_t* q, const uint8_t* z, const float* s,
+                       int64_t N, int64_t K, uint8_t* out) {
+    if (!q || !z || !s || !out || N <= 0 || K <= 0 || N % 16 || K % 128) return ORACLE_BAD_ARG;
+    int64_t G = K / 128, NB = N / 16;
+    int64_t z0 = round_up256(N * K / 2);
+    int64_t s0 = round_up256(z0 + N * G / 2);
+    memset(out, 0, (size_t)oracle_layout_bytes(N, K));
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g) {
+            uint8_t* blk = out + (nb * G + g) * 1024;
+            for (int j = 0; j < 4; ++j)
+                for (int c = 0; c < 16; ++c)
+                    for (int i = 0; i < 16; ++i) {
+                        int64_t n = 16 * nb + c;
+                        uint8_t lo = q[n * K + 128 * g + 16 * j + i] & 0x0F;
+                        uint8_t hi = q[n * K + 128 * g + 64 + 16 * j + i] & 0x0F;
+                        blk[16 * (16 * j + c) + i] = (uint8_t)(lo | (hi << 4));
+                    }
+            uint8_t* zb = out + z0 + (nb * G + g) * 8;
+            for (int c = 0; c < 16; ++c) {
+                uint8_t v = z[(16 * nb + c) * G + g] & 0x0F;
+                zb[c / 2] |= (uint8_t)((c % 2) ? (v << 4) : v);
+            }
+            float* sb = (float*)(out + s0) + (nb * G + g) * 16;
+            for (int c = 0; c < 16; ++c) sb[c] = s[(16 * nb + c) * G + g];
+        }
+    return ORACLE_OK;
+}
+
+int oracle_layout_unpack(const uint8_t* in, int64_t N, int64_t K,
+                         uint8_t* q, uint8_t* z, float* s) {
+    if (!in || !q || !z || !s || N <= 0 || K <= 0 || N % 16 || K % 128) return ORACLE_BAD_ARG;
+    int64_t G = K / 128, NB = N / 16;
+    int64_t z0 = round_up256(N * K / 2);
+    int64_t s0 = round_up256(z0 + N * G / 2);
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g) {
+            const uint8_t* blk = in + (nb * G + g) * 1024;
+            for (int j = 0; j < 4; ++j)
+                for (int c = 0; c < 16; ++c)
+                    for (int i = 0; i < 16; ++i) {
+                        int64_t n = 16 * nb + c;
+                        uint8_t b = blk[16 * (16 * j + c) + i];
+                        q[n * K + 128 * g + 16 * j + i] = b & 0x0F;
+                        q[n * K + 128 * g + 64 + 16 * j + i] = b >> 4;
+                    }
+            const uint8_t* zb = in + z0 + (nb * G + g) * 8;
+            for (int c = 0; c < 16; ++c)
+                z[(16 * nb + c) * G + g] = (c % 2) ? (zb[c / 2] >> 4) : (zb[c / 2] & 0x0F);
+            const float* sb = (const float*)(in + s0) + (nb * G + g) * 16;
+            for (int c = 0; c < 16; ++c) s[(16 * nb + c) * G + g] = sb[c];
+        }
+    return ORACLE_OK;
+}
