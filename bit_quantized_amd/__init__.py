@@ -1,0 +1,11 @@
+"""MI355X (gfx950) W4A8 linear layer: per-token int8 activations x GPTQ int4
+weights (group 128, asymmetric scale and zero) -> bf16, in hand-written HIP.
+
+The public API is the C ABI in include/w4a8.h; this package is its thin
+Python binding (torch for device memory and streams only).
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, GROUP, PATH_AUTO, PATH_GEMV, PATH_PREFILL, PATH_SKINNY, PackedWeight, W4A8Error,
+    gemm, gemm_debug, linear, load, pack_weights, packed_weight_bytes, quant_act, select_path,
+    unpack_weights, workspace_bytes,
+)

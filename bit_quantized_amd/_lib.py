@@ -1,0 +1,217 @@
+"""ctypes binding of libw4a8.so (include/w4a8.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the layer runs in the library's HIP kernels.  If the
+library is not built this module raises — there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a8.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED_SHAPE = -2
+ERR_MISALIGNED = -3
+ERR_BUFFER_TOO_SMALL = -4
+ERR_DEVICE = -5
+
+BF16 = 0
+F32 = 1
+
+PATH_AUTO = 0
+PATH_GEMV = 1
+PATH_SKINNY = 2
+PATH_PREFILL = 3
+
+GROUP = 128
+
+# Every symbol include/w4a8.h declares, with its ctypes signature.
+_i32, _i64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "w4a8_abi_version": (ctypes.c_int, []),
+    "w4a8_layout_version": (ctypes.c_int, []),
+    "w4a8_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w4a8_last_error": (ctypes.c_char_p, []),
+    "w4a8_packed_weight_bytes": (_sz, [_i64, _i64, _i32]),
+    "w4a8_pack_weights": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a8_unpack_weights": (ctypes.c_int, [_vp, _sz, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
+    "w4a8_quant_act": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "w4a8_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "w4a8_select_path": (ctypes.c_int, [_i64, _i64, _i64]),
+    "w4a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
+    "w4a8_gemm_debug": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _i32, _i64,
+                                       _i64, _vp, _vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"w4a8 status {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_quantized_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        lib = load()
+        raise W4A8Error(rc, lib.w4a8_last_error().decode())
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+@dataclass
+class PackedWeight:
+    """A packed weight buffer with the identity that gives it meaning."""
+    buf: torch.Tensor          # uint8, w4a8_packed_weight_bytes(N, K, group)
+    N: int
+    K: int
+    group: int
+    layout_version: int
+
+    def check(self):
+        v = load().w4a8_layout_version()
+        if self.layout_version != v:
+            raise ValueError(f"packed with layout {self.layout_version}, library has {v}")
+
+
+def packed_weight_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return int(load().w4a8_packed_weight_bytes(N, K, group))
+
+
+def pack_weights(q: torch.Tensor, z: torch.Tensor, s: torch.Tensor, group: int = GROUP,
+                 out: torch.Tensor | None = None) -> PackedWeight:
+    """q uint8 [N][K] codes 0..15, z uint8 [N][K/group], s float32 [N][K/group]."""
+    lib = load()
+    _need_cuda(q, z, s)
+    if q.dtype != torch.uint8 or z.dtype != torch.uint8 or s.dtype != torch.float32:
+        raise TypeError("q, z must be uint8 and s float32")
+    N, K = q.shape
+    nbytes = lib.w4a8_packed_weight_bytes(N, K, group)
+    if nbytes == 0:
+        _check(lib.w4a8_pack_weights(None, None, None, N, K, group, None, 0, None))
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib.w4a8_pack_weights(_p(q), _p(z), _p(s), N, K, group, _p(out), out.numel(),
+                                 _stream(q.device)))
+    return PackedWeight(out, N, K, group, lib.w4a8_layout_version())
+
+
+def unpack_weights(w: PackedWeight):
+    lib = load()
+    w.check()
+    G = w.K // w.group
+    dev = w.buf.device
+    q = torch.empty((w.N, w.K), dtype=torch.uint8, device=dev)
+    z = torch.empty((w.N, G), dtype=torch.uint8, device=dev)
+    s = torch.empty((w.N, G), dtype=torch.float32, device=dev)
+    _check(lib.w4a8_unpack_weights(_p(w.buf), w.buf.numel(), w.N, w.K, w.group, _p(q), _p(z),
+                                   _p(s), _stream(dev)))
+    return q, z, s
+
+
+def quant_act(x: torch.Tensor, qa: torch.Tensor | None = None, sa: torch.Tensor | None = None):
+    """x bfloat16 or float32 [M][K] -> (qa int8 [M][K], sa float32 [M])."""
+    lib = load()
+    _need_cuda(x)
+    M, K = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError(x.dtype)
+    qa = torch.empty((M, K), dtype=torch.int8, device=x.device) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=x.device) if sa is None else sa
+    _check(lib.w4a8_quant_act(_p(x), dt, M, K, _p(qa), _p(sa), _stream(x.device)))
+    return qa, sa
+
+
+def workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    return int(load().w4a8_gemm_workspace_bytes(M, N, K, group))
+
+
+def select_path(M: int, N: int, K: int) -> int:
+    return int(load().w4a8_select_path(M, N, K))
+
+
+def _workspace(M, w: PackedWeight, workspace):
+    need = workspace_bytes(M, w.N, w.K, w.group)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.buf.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gemm(qa: torch.Tensor, sa: torch.Tensor, w: PackedWeight, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 y [M][N] from quantised activations and a packed weight."""
+    lib = load()
+    w.check()
+    _need_cuda(qa, sa)
+    M, K = qa.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=qa.device) if out is None else out
+    ws, wsb = _workspace(M, w, workspace)
+    _check(lib.w4a8_gemm(_p(qa), _p(sa), _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, _p(out),
+                         _p(ws), wsb, _stream(qa.device)))
+    return out
+
+
+def gemm_debug(qa, sa, w: PackedWeight, path: int = PATH_AUTO, rows=None, want_y: bool = True,
+               workspace=None):
+    """(partials int32 [rows][N][G], y bf16 [M][N] or None) from a forced path."""
+    lib = load()
+    w.check()
+    M, K = qa.shape
+    m0, m1 = rows if rows is not None else (0, M)
+    G = w.K // w.group
+    P = torch.empty((m1 - m0, w.N, G), dtype=torch.int32, device=qa.device)
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=qa.device) if want_y else None
+    ws, wsb = _workspace(M, w, workspace)
+    _check(lib.w4a8_gemm_debug(_p(qa), _p(sa), _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group,
+                               path, m0, m1, _p(P) if P.numel() else None, _p(y), _p(ws), wsb,
+                               _stream(qa.device)))
+    return P, y
+
+
+def linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None) -> torch.Tensor:
+    """Quantise activations per token, then the W4A8 GEMM (two launches)."""
+    qa, sa = quant_act(x)
+    return gemm(qa, sa, w, out=out, workspace=workspace)

@@ -1,0 +1,265 @@
+// Public C ABI (include/w4a8.h): host-side validation, path choice and
+// launches.  Every check runs before anything is enqueued, so a rejected call
+// launches nothing and writes nothing.  No C++ exception crosses the ABI.
+//
+// "The 4-bit CPU path", section "The weight layout, measured": a shape that
+// does not tile the packed block is refused instead of being misread.
+// "Serve a pre-quantized int8 weight-only DiT ...", comment "Amendment ...":
+// a path is only advertised where its kernel runs; the debug entry point lets
+// tests force every path at every bucket edge.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/w4a8.h"
+#include "w4a8_internal.h"
+
+using namespace w4a8;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return W4A8_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_weight_shape(int64_t N, int64_t K, int32_t group) {
+  if (N <= 0 || K <= 0) return fail(W4A8_ERR_INVALID_ARG, "N=%lld and K=%lld must be positive",
+                                    (long long)N, (long long)K);
+  if (group != kGroup)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "group=%d unsupported (only 128)", (int)group);
+  if (K % kGroup)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (N % kBlockCols)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
+                "N=%lld is not a multiple of 16 (no partial channel blocks)", (long long)N);
+  if (N > (int64_t)1 << 26 || K > (int64_t)1 << 24 || N * K > ((int64_t)1 << 40))
+    return fail(W4A8_ERR_INVALID_ARG, "N=%lld K=%lld too large", (long long)N, (long long)K);
+  return W4A8_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(W4A8_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Overlap test for [p, p+n) and [q, q+m).
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+int pick_path(int64_t M) {
+  if (M == 1) return W4A8_PATH_GEMV;
+  if (M <= 16) return W4A8_PATH_SKINNY;
+  return W4A8_PATH_PREFILL;
+}
+
+int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
+  if (path == W4A8_PATH_GEMV) return gemv_ksplit(M, N, K);
+  if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
+  return 1;
+}
+
+size_t workspace_for(int path, int64_t M, int64_t N, int64_t K) {
+  const int ks = ksplit_for(path, M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+int run_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
+             int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int64_t m_begin,
+             int64_t m_end, int32_t* partials, uint16_t* y, void* workspace,
+             size_t workspace_bytes, void* stream, bool debug) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (!qa || !sa || !packed) return fail(W4A8_ERR_INVALID_ARG, "null input pointer");
+  if (!debug && !y) return fail(W4A8_ERR_INVALID_ARG, "null output pointer");
+  if (!aligned16(qa) || !aligned16(sa) || !aligned16(packed) || (y && !aligned16(y)))
+    return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const size_t need = (size_t)packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  if (path == W4A8_PATH_AUTO) path = pick_path(M);
+  if (path == W4A8_PATH_GEMV && M != 1)
+    return fail(W4A8_ERR_INVALID_ARG, "GEMV path needs M == 1 (M=%lld)", (long long)M);
+  if (path == W4A8_PATH_SKINNY && M > 16)
+    return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
+  if (path < W4A8_PATH_GEMV || path > W4A8_PATH_PREFILL)
+    return fail(W4A8_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (debug) {
+    if (m_begin < 0 || m_end > M || m_begin > m_end)
+      return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
+                  (long long)m_begin, (long long)m_end, (long long)M);
+    if (partials && !aligned16(partials))
+      return fail(W4A8_ERR_MISALIGNED, "partials must be 16-byte aligned");
+  }
+  const int ks = ksplit_for(path, M, N, K);
+  const size_t ws_need = workspace_for(path, M, N, K);
+  if (ws_need && (!workspace || workspace_bytes < ws_need))
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                ws_need);
+  if (ws_need && !aligned16(workspace))
+    return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const size_t ybytes = (size_t)M * (size_t)N * 2;
+  if (y && (overlaps(y, ybytes, qa, (size_t)M * K) || overlaps(y, ybytes, sa, (size_t)M * 4) ||
+            overlaps(y, ybytes, packed, need) ||
+            (ws_need && overlaps(y, ybytes, workspace, ws_need))))
+    return fail(W4A8_ERR_INVALID_ARG, "output aliases an input or the workspace");
+
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
+  GemmArgs a;
+  a.qa = qa;
+  a.sa = sa;
+  a.w.codes = base;
+  a.w.zeros = base + zeros_offset(N, K);
+  a.w.scales = reinterpret_cast<const float*>(base + scales_offset(N, K));
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.partials = debug ? partials : nullptr;
+  a.m_begin = debug ? m_begin : 0;
+  a.m_end = debug ? m_end : 0;
+  a.workspace = static_cast<float*>(workspace);
+  a.ksplit = ks;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // start from a clean error state
+  hipError_t e;
+  if (path == W4A8_PATH_GEMV)
+    e = launch_gemv(a, st);
+  else if (path == W4A8_PATH_SKINNY)
+    e = launch_skinny(a, st);
+  else
+    e = launch_prefill(a, st);
+  if (e == hipSuccess && ks > 1 && y) e = launch_splitk_reduce(a.workspace, ks, sa, M, N, y, st);
+  return device_status(e, "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_abi_version(void) { return W4A8_ABI_VERSION; }
+int w4a8_layout_version(void) { return W4A8_LAYOUT_VERSION; }
+
+const char* w4a8_status_string(int status) {
+  switch (status) {
+    case W4A8_OK: return "ok";
+    case W4A8_ERR_INVALID_ARG: return "invalid argument";
+    case W4A8_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case W4A8_ERR_MISALIGNED: return "misaligned pointer";
+    case W4A8_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case W4A8_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* w4a8_last_error(void) { return g_err; }
+
+size_t w4a8_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
+  if (check_weight_shape(N, K, group)) return 0;
+  return (size_t)packed_bytes(N, K);
+}
+
+int w4a8_pack_weights(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
+                      int32_t group, void* packed, size_t packed_bytes_, void* stream) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (!q || !z || !s || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(packed) || !aligned16(s))
+    return fail(W4A8_ERR_MISALIGNED, "q, s and packed must be 16-byte aligned");
+  const size_t need = (size_t)packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  const size_t G = (size_t)(K / kGroup);
+  if (overlaps(packed, need, q, (size_t)(N * K)) || overlaps(packed, need, z, (size_t)N * G) ||
+      overlaps(packed, need, s, (size_t)N * G * 4))
+    return fail(W4A8_ERR_INVALID_ARG, "packed buffer aliases an input");
+  (void)hipGetLastError();
+  return device_status(launch_pack(q, z, s, N, K, static_cast<uint8_t*>(packed),
+                                   static_cast<hipStream_t>(stream)),
+                       "pack launch");
+}
+
+int w4a8_unpack_weights(const void* packed, size_t packed_bytes_, int64_t N, int64_t K,
+                        int32_t group, uint8_t* q, uint8_t* z, float* s, void* stream) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (!q || !z || !s || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q) || !aligned16(packed) || !aligned16(s))
+    return fail(W4A8_ERR_MISALIGNED, "q, s and packed must be 16-byte aligned");
+  const size_t need = (size_t)packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  (void)hipGetLastError();
+  return device_status(launch_unpack(static_cast<const uint8_t*>(packed), N, K, q, z, s,
+                                     static_cast<hipStream_t>(stream)),
+                       "unpack launch");
+}
+
+int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
+                   void* stream) {
+  if (!x || !qa || !sa) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
+    return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
+  if (M <= 0 || M > ((int64_t)1 << 24) || K <= 0 || K > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld K=%lld out of range", (long long)M, (long long)K);
+  if (K % kGroup)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (!aligned16(x) || !aligned16(qa) || !aligned16(sa))
+    return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const size_t xb = (size_t)M * K * (x_dtype == W4A8_BF16 ? 2 : 4);
+  if (overlaps(qa, (size_t)M * K, x, xb) || overlaps(sa, (size_t)M * 4, x, xb) ||
+      overlaps(qa, (size_t)M * K, sa, (size_t)M * 4))
+    return fail(W4A8_ERR_INVALID_ARG, "outputs alias the input or each other");
+  (void)hipGetLastError();
+  return device_status(launch_quant(x, x_dtype, M, K, qa, sa, static_cast<hipStream_t>(stream)),
+                       "quant launch");
+}
+
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (check_weight_shape(N, K, group) || M <= 0) return 0;
+  size_t need = 0;
+  for (int p = W4A8_PATH_GEMV; p <= W4A8_PATH_PREFILL; ++p) {
+    if (p == W4A8_PATH_GEMV && M != 1) continue;
+    if (p == W4A8_PATH_SKINNY && M > 16) continue;
+    const size_t w = workspace_for(p, M, N, K);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
+int w4a8_select_path(int64_t M, int64_t, int64_t) { return M <= 0 ? 0 : pick_path(M); }
+
+int w4a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
+              int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return run_gemm(qa, sa, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO, 0, 0, nullptr, y,
+                  workspace, workspace_bytes, stream, false);
+}
+
+int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
+                    int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int64_t m_begin,
+                    int64_t m_end, int32_t* partials, uint16_t* y_or_null, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run_gemm(qa, sa, packed, packed_bytes_, M, N, K, group, path, m_begin, m_end, partials,
+                  y_or_null, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

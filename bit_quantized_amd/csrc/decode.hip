@@ -1,0 +1,255 @@
+// Decode-side kernels: the M == 1 GEMV, the 2 <= M <= 16 skinny GEMM, and
+// the deterministic split-K reduction both use when N alone cannot fill the
+// chip.
+//
+// "The 4-bit CPU path", section "W4A16": a kernel whose cost is dominated by
+// touching each weight once per call is "fine for decode"; these kernels
+// stream every packed weight byte exactly once with 1 KiB-per-wavefront
+// coalesced loads and unpack the nibbles in registers.
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+namespace {
+
+constexpr int kThreads = 256;  // 4 wavefronts
+constexpr int kWaves = kThreads / 64;
+
+// Balanced split of [0, n) into `parts` contiguous slices.
+__device__ __forceinline__ int64_t slice_begin(int64_t n, int parts, int idx) {
+  return n * idx / parts;
+}
+
+__device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, float v) {
+  if (a.ksplit == 1) {
+    if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(a.sa[m] * v);
+  } else {
+    a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + n] = v;
+  }
+}
+
+// ------------------------------------------------------------------ M == 1
+//
+// Wavefront lane l = 16*j + c owns output channel c of the block and the 32
+// input channels {16j..16j+15} u {64+16j..64+16j+15} of every group it
+// visits: one 16-byte load per group, eight signed 4-way dot products against
+// the matching activation bytes, one int32 per lane per group.  The four
+// lanes of a channel hold disjoint quarters of the group; since the rescale
+// by s[n][g] is linear they are rescaled separately and summed once at the
+// end with cross-lane shuffles (the exact group sum is formed only for the
+// debug partials).
+template <bool DEBUG>
+__global__ void __launch_bounds__(kThreads)
+gemv_kernel(GemmArgs a) {
+  __shared__ float red[kWaves][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15, j = lane >> 4;
+  const int64_t nb = blockIdx.x;
+  const int64_t G = a.K / kGroup;
+  const int parts = a.ksplit * kWaves;
+  const int pidx = blockIdx.y * kWaves + wave;
+  const int64_t gb = slice_begin(G, parts, pidx), ge = slice_begin(G, parts, pidx + 1);
+  const uint8_t* codes = a.w.codes + nb * G * kBlockBytes + 16 * lane;
+  const uint8_t* zeros = a.w.zeros + nb * G * kZeroBlockBytes;
+  const float* scales = a.w.scales + nb * G * 16 + c;
+  const int8_t* act = a.qa + 16 * j;
+
+  float accf = 0.0f;
+  constexpr int U = 8;
+  for (int64_t g0 = gb; g0 < ge; g0 += U) {
+    uint4 wv[U], alo[U], ahi[U];
+    float sv[U];
+    uint32_t zv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u < ge) {
+        const int64_t g = g0 + u;
+        wv[u] = *reinterpret_cast<const uint4*>(codes + g * kBlockBytes);
+        alo[u] = *reinterpret_cast<const uint4*>(act + g * kGroup);
+        ahi[u] = *reinterpret_cast<const uint4*>(act + g * kGroup + 64);
+        sv[u] = scales[g * 16];
+        zv[u] = zero_of(zeros + g * kZeroBlockBytes, c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u < ge) {
+        const uint32_t zz = zv[u] * 0x01010101u;
+        const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        const uint32_t al[4] = {alo[u].x, alo[u].y, alo[u].z, alo[u].w};
+        const uint32_t ah[4] = {ahi[u].x, ahi[u].y, ahi[u].z, ahi[u].w};
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = sub_zero_bytes(d[w] & 0x0F0F0F0Fu, zz);
+          const uint32_t hi = sub_zero_bytes((d[w] >> 4) & 0x0F0F0F0Fu, zz);
+          acc = __builtin_amdgcn_sdot4((int)lo, (int)al[w], acc, false);
+          acc = __builtin_amdgcn_sdot4((int)hi, (int)ah[w], acc, false);
+        }
+        if (DEBUG) {
+          int p = acc + __shfl_xor(acc, 16);
+          p += __shfl_xor(p, 32);
+          if (j == 0 && a.partials && a.m_begin == 0 && a.m_end > 0)
+            a.partials[(16 * nb + c) * G + (g0 + u)] = p;
+        }
+        accf += sv[u] * (float)acc;
+      }
+    }
+  }
+  accf += __shfl_xor(accf, 16);
+  accf += __shfl_xor(accf, 32);
+  if (j == 0) red[wave][c] = accf;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float t = red[0][c];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += red[w][c];
+    store_out(a, 0, 16 * nb + c, t);
+  }
+}
+
+// ------------------------------------------------------------- 2 <= M <= 16
+//
+// One v_mfma_i32_16x16x64_i8 pair per 16-channel block and group.  A is the
+// activation tile (rows >= M read as zero), B the unpacked q - z bytes.  Lane
+// l supplies A row l%16 and B column l%16 with the same 16 input channels
+// (16j..16j+15 for the first step, 64+16j.. for the second, j = l/16); the
+// instruction sums over all 64 slots, so the group's exact int32 product
+// comes out per (row, column) without any cross-lane work.  Result layout:
+// lane l holds column l%16, rows 4*(l/16) .. 4*(l/16)+3.
+template <bool DEBUG>
+__global__ void __launch_bounds__(kThreads)
+skinny_kernel(GemmArgs a) {
+  __shared__ float red[kWaves][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, j = lane >> 4;
+  const int64_t nb = blockIdx.x;
+  const int64_t G = a.K / kGroup;
+  const int parts = a.ksplit * kWaves;
+  const int pidx = blockIdx.y * kWaves + wave;
+  const int64_t gb = slice_begin(G, parts, pidx), ge = slice_begin(G, parts, pidx + 1);
+  const uint8_t* codes = a.w.codes + nb * G * kBlockBytes + 16 * lane;
+  const uint8_t* zeros = a.w.zeros + nb * G * kZeroBlockBytes;
+  const float* scales = a.w.scales + nb * G * 16 + r16;
+  const bool row_ok = r16 < a.M;
+  const int8_t* act = a.qa + (row_ok ? r16 : 0) * a.K + 16 * j;
+
+  float accf[4] = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  for (int64_t g0 = gb; g0 < ge; g0 += U) {
+    uint4 wv[U];
+    v4i a0[U], a1[U];
+    float sv[U];
+    uint32_t zv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u < ge) {
+        const int64_t g = g0 + u;
+        wv[u] = *reinterpret_cast<const uint4*>(codes + g * kBlockBytes);
+        if (row_ok) {
+          a0[u] = *reinterpret_cast<const v4i*>(act + g * kGroup);
+          a1[u] = *reinterpret_cast<const v4i*>(act + g * kGroup + 64);
+        } else {
+          a0[u] = v4i{0, 0, 0, 0};
+          a1[u] = v4i{0, 0, 0, 0};
+        }
+        sv[u] = scales[g * 16];
+        zv[u] = zero_of(zeros + g * kZeroBlockBytes, r16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + u < ge) {
+        const uint32_t zz = zv[u] * 0x01010101u;
+        const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        v4i b0, b1;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          b0[w] = (int)sub_zero_bytes(d[w] & 0x0F0F0F0Fu, zz);
+          b1[w] = (int)sub_zero_bytes((d[w] >> 4) & 0x0F0F0F0Fu, zz);
+        }
+        v4i acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[u], b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], b1, acc, 0, 0, 0);
+        if (DEBUG && a.partials) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = 4 * j + r;
+            if (m < a.M && m >= a.m_begin && m < a.m_end)
+              a.partials[((m - a.m_begin) * a.N + 16 * nb + r16) * G + (g0 + u)] = acc[r];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accf[r] += sv[u] * (float)acc[r];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = accf[r];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float t = red[0][r][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t += red[w][r][lane];
+      const int64_t m = 4 * j + r;
+      if (m < a.M) store_out(a, m, 16 * nb + r16, t);
+    }
+  }
+}
+
+// y[m][n] = bf16(sa[m] * sum_k ws[k][m][n]), summed in split order.
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __restrict__ sa,
+                     int64_t M, int64_t N, uint16_t* __restrict__ y) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M * N) return;
+  const int64_t m = t / N;
+  float v = ws[t];
+  for (int k = 1; k < ksplit; ++k) v += ws[k * M * N + t];
+  y[t] = f32_to_bf16_rne(sa[m] * v);
+}
+
+// Split K until the grid has about 4 workgroups per compute unit, keeping at
+// least 2 groups per wavefront.
+int pick_ksplit(int64_t N, int64_t K) {
+  const int64_t nb = N / kBlockCols, G = K / kGroup;
+  int ks = 1;
+  while (nb * ks < 1024 && G >= (int64_t)ks * 2 * kWaves * 2) ks *= 2;
+  return ks;
+}
+
+}  // namespace
+
+int gemv_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
+int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
+
+hipError_t launch_gemv(const GemmArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
+  if (a.partials)
+    hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
+  if (a.partials)
+    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
+                                int64_t N, uint16_t* y, hipStream_t st) {
+  const int64_t total = M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     st, ws, ksplit, sa, M, N, y);
+  return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,0 +1,202 @@
+// Prefill GEMM (M > 16) on the int8 matrix cores.
+//
+// "The 4-bit CPU path", section "W4A16": a per-row dequantising kernel is
+// "ruinous for prefill", so large batches take a separate GEMM path; here
+// that path keeps the weights as 4-bit codes in LDS, unpacks them in
+// registers to q - z bytes and runs v_mfma_i32_16x16x64_i8 per group, so the
+// weights are never expanded in HBM.
+//
+// Tile: 128 tokens x 128 output channels per 256-thread workgroup, four
+// wavefronts of 64 x 64.  Per group of 128 input channels the workgroup
+// stages the activation tile (128 x 128 int8) and eight packed code blocks
+// (8 KiB) in LDS, double-buffered, with the next group's global loads in
+// flight while the current group computes.
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = 128;                 // tokens per tile
+constexpr int BN = 128;                 // output channels per tile
+constexpr int NCB = BN / kBlockCols;    // packed blocks per tile
+constexpr int kAStride = kGroup + 16;   // LDS row pitch of the activation tile (bank spread)
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + BM * kAStride;
+constexpr int kSOff = kBOff + NCB * kBlockBytes;
+constexpr int kZOff = kSOff + NCB * 16 * 4;
+constexpr int kBufBytes = kZOff + NCB * kZeroBlockBytes;
+
+struct Stage {
+  uint4 a[4];
+  uint4 b[2];
+  float s;
+  uint2 z;
+};
+
+__device__ __forceinline__ void load_stage(const GemmArgs& a, int64_t m0, int64_t cb0, int64_t NB,
+                                           int64_t G, int64_t g, Stage& st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ch = tid + kThreads * i;
+    const int64_t m = m0 + (ch >> 3);
+    if (m < a.M)
+      st.a[i] = *reinterpret_cast<const uint4*>(a.qa + m * a.K + g * kGroup + (ch & 7) * 16);
+    else
+      st.a[i] = make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = tid + kThreads * i;
+    const int64_t nb = cb0 + (ch >> 6);
+    if (nb < NB)
+      st.b[i] = *reinterpret_cast<const uint4*>(a.w.codes + (nb * G + g) * kBlockBytes +
+                                                (ch & 63) * 16);
+    else
+      st.b[i] = make_uint4(0, 0, 0, 0);
+  }
+  if (tid < NCB * 16) {
+    const int64_t nb = cb0 + (tid >> 4);
+    st.s = nb < NB ? a.w.scales[(nb * G + g) * 16 + (tid & 15)] : 0.0f;
+  } else if (tid < NCB * 16 + NCB) {
+    const int64_t nb = cb0 + (tid - NCB * 16);
+    st.z = nb < NB ? *reinterpret_cast<const uint2*>(a.w.zeros + (nb * G + g) * kZeroBlockBytes)
+                   : make_uint2(0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ch = tid + kThreads * i;
+    *reinterpret_cast<uint4*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ch = tid + kThreads * i;
+    *reinterpret_cast<uint4*>(buf + kBOff + ch * 16) = st.b[i];
+  }
+  if (tid < NCB * 16) {
+    reinterpret_cast<float*>(buf + kSOff)[tid] = st.s;
+  } else if (tid < NCB * 16 + NCB) {
+    *reinterpret_cast<uint2*>(buf + kZOff + (tid - NCB * 16) * kZeroBlockBytes) = st.z;
+  }
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+// run of tiles (output-channel major) so the packed weights a tile column
+// needs are fetched into one XCD's L2 only.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
+  const int64_t xcd = b % 8, local = b / 8;
+  const int64_t per = T / 8, rem = T % 8;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+template <bool DEBUG>
+__global__ void __launch_bounds__(kThreads)
+prefill_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r16 = lane & 15, j = lane >> 4;
+  const int64_t G = a.K / kGroup;
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (NB + NCB - 1) / NCB;
+  const int64_t t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int64_t tm = t % tiles_m, tn = t / tiles_m;
+  const int64_t m0 = tm * BM, cb0 = tn * NCB;
+
+  float accf[4][4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
+
+  Stage st;
+  load_stage(a, m0, cb0, NB, G, 0, st);
+  store_stage(smem[0], st);
+  __syncthreads();
+
+  for (int64_t g = 0; g < G; ++g) {
+    const bool more = g + 1 < G;
+    if (more) load_stage(a, m0, cb0, NB, G, g + 1, st);
+    const uint8_t* buf = smem[g & 1];
+
+    v4i b0[4], b1[4];
+    float sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cb = wn * 4 + u;
+      const uint4 wv = *reinterpret_cast<const uint4*>(buf + kBOff + cb * kBlockBytes + lane * 16);
+      const uint32_t zz = zero_of(buf + kZOff + cb * kZeroBlockBytes, r16) * 0x01010101u;
+      const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        b0[u][w] = (int)sub_zero_bytes(d[w] & 0x0F0F0F0Fu, zz);
+        b1[u][w] = (int)sub_zero_bytes((d[w] >> 4) & 0x0F0F0F0Fu, zz);
+      }
+      sv[u] = reinterpret_cast<const float*>(buf + kSOff)[cb * 16 + r16];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
+      const v4i a0 = *reinterpret_cast<const v4i*>(arow);
+      const v4i a1 = *reinterpret_cast<const v4i*>(arow + 64);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v4i acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[u], acc, 0, 0, 0);
+        if (DEBUG && a.partials) {
+          const int64_t nb = cb0 + wn * 4 + u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+            if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
+              a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[r];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[r];
+      }
+    }
+    if (more) store_stage(smem[(g + 1) & 1], st);
+    __syncthreads();
+  }
+
+  if (!a.y) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+      if (m >= a.M) continue;
+      const float sam = a.sa[m];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t nb = cb0 + wn * 4 + u;
+        if (nb < NB) a.y[m * a.N + nb * 16 + r16] = f32_to_bf16_rne(sam * accf[i][u][r]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((NB + NCB - 1) / NCB);
+  if (a.partials)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP translation units of libw4a8.
+// Device helpers here are used by the kernels only; nothing in this file is
+// part of the public ABI (include/w4a8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+constexpr int kGroup = 128;          // input channels per quantisation group
+constexpr int kBlockCols = 16;       // output channels per packed block
+constexpr int kBlockBytes = 1024;    // 16 channels x 128 codes x 4 bits
+constexpr int kZeroBlockBytes = 8;   // 16 zero points x 4 bits
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+struct PackedView {
+  const uint8_t* codes;   // [N/16][G][1024]
+  const uint8_t* zeros;   // [N/16][G][8]
+  const float* scales;    // [N/16][G][16]
+};
+
+inline int64_t round_up256(int64_t v) { return (v + 255) / 256 * 256; }
+inline int64_t zeros_offset(int64_t N, int64_t K) { return round_up256(N * K / 2); }
+inline int64_t scales_offset(int64_t N, int64_t K) {
+  return round_up256(zeros_offset(N, K) + N * (K / kGroup) / 2);
+}
+inline int64_t packed_bytes(int64_t N, int64_t K) {
+  return scales_offset(N, K) + 4 * N * (K / kGroup);
+}
+
+// ---------------------------------------------------------------- device helpers
+
+// float32 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Four unsigned 4-bit codes (one per byte, 0..15) minus a zero point z
+// (0..15) as four signed bytes q - z in [-15, 15].  Setting bit 7 of every
+// byte first makes each byte >= 128 > z, so the 32-bit subtraction never
+// borrows across bytes; flipping bit 7 back maps 128 + v to v mod 256.
+__device__ __forceinline__ uint32_t sub_zero_bytes(uint32_t nib4, uint32_t zz) {
+  return ((nib4 | 0x80808080u) - zz) ^ 0x80808080u;
+}
+
+// Zero point of column c in a zeros block.
+__device__ __forceinline__ uint32_t zero_of(const uint8_t* zblk, int c) {
+  uint32_t b = zblk[c >> 1];
+  return (c & 1) ? (b >> 4) : (b & 0xFu);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the
+// caller (abi.hip) before any of these runs.
+
+hipError_t launch_pack(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
+                       uint8_t* packed, hipStream_t st);
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q, uint8_t* z,
+                         float* s, hipStream_t st);
+hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
+                        hipStream_t st);
+
+struct GemmArgs {
+  const int8_t* qa;
+  const float* sa;
+  PackedView w;
+  int64_t M, N, K;
+  uint16_t* y;            // may be null in debug mode
+  int32_t* partials;      // debug only, may be null
+  int64_t m_begin, m_end; // debug row window
+  float* workspace;       // split-K partial sums
+  int ksplit;
+};
+
+int gemv_ksplit(int64_t M, int64_t N, int64_t K);
+int skinny_ksplit(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st);
+hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
+hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
+                                int64_t N, uint16_t* y, hipStream_t st);
+
+}  // namespace w4a8

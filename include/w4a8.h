@@ -1,0 +1,168 @@
+/*
+ * w4a8.h — C ABI of the MI355X (gfx950) W4A8 linear-layer library.
+ *
+ * The layer: activations quantised per token to symmetric int8, multiplied by
+ * GPTQ-style int4 weights that carry a scale and an integer zero point per
+ * group of 128 input channels; every group is accumulated exactly in int32,
+ * rescaled by sa[m] * s[n][g], and the result is written as bfloat16.
+ *
+ * Passages this interface follows:
+ *   "The 4-bit CPU path", section "W4A8": the kernel takes GPTQ-packed int4
+ *     weights and quantises activations to int8; it uses the checkpoint's
+ *     zero points (the constant 8 is only a symmetric-grid special case).
+ *   "The 4-bit CPU path", section "Building a checkpoint": group size 128.
+ *   "The 4-bit CPU path", section "The weight layout, measured": layout
+ *     transforms happen once, at load; shapes that do not tile the layout's
+ *     block are refused rather than misread.
+ *   "The 4-bit CPU path", section "W4A16": small and large batches take
+ *     different kernels (here the M buckets GEMV / SKINNY / PREFILL).
+ *   "EgoPQ Real-Serving Handoff", section "2. External Artifacts": the packed
+ *     path needs the exact per-group scale and zero metadata.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device memory on the current device;
+ *     the caller allocates and owns every buffer.  The library allocates and
+ *     frees nothing in these calls and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work: they never synchronise the device.
+ *   - Return value: W4A8_OK (0) or a negative W4A8_ERR_* status.  All
+ *     argument checks run on the host before anything is enqueued: a rejected
+ *     call launches nothing and writes nothing.  A failed launch returns
+ *     W4A8_ERR_DEVICE.  w4a8_last_error() gives a thread-local message.
+ *   - Device pointers must be 16-byte aligned.  Outputs must not alias inputs.
+ *   - Inputs must be finite; non-finite activations give undefined codes.
+ *   - All calls are deterministic: the same inputs give bitwise-identical
+ *     outputs (reductions run in a fixed order; no floating-point atomics).
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A8_ABI_VERSION 1
+#define W4A8_LAYOUT_VERSION 1
+
+/* status codes */
+#define W4A8_OK 0
+#define W4A8_ERR_INVALID_ARG (-1)       /* null pointer, M/N/K out of range, bad enum */
+#define W4A8_ERR_UNSUPPORTED_SHAPE (-2) /* group != 128, K % 128 != 0, N % 16 != 0 */
+#define W4A8_ERR_MISALIGNED (-3)        /* a device pointer is not 16-byte aligned */
+#define W4A8_ERR_BUFFER_TOO_SMALL (-4)  /* packed or workspace buffer smaller than required */
+#define W4A8_ERR_DEVICE (-5)            /* the HIP runtime reported an error */
+
+/* activation dtypes for w4a8_quant_act */
+#define W4A8_BF16 0
+#define W4A8_F32 1
+
+/* GEMM paths (M buckets).  AUTO picks GEMV for M == 1, SKINNY for
+ * 2 <= M <= 16, PREFILL for M > 16; the choice depends on (M, N, K) only. */
+#define W4A8_PATH_AUTO 0
+#define W4A8_PATH_GEMV 1
+#define W4A8_PATH_SKINNY 2
+#define W4A8_PATH_PREFILL 3
+
+int w4a8_abi_version(void);
+/* Bumped whenever the packed weight format changes; a packed buffer is only
+ * meaningful together with (N, K, group, layout version). */
+int w4a8_layout_version(void);
+const char* w4a8_status_string(int status);
+/* Message for the last failing call on this thread ("" if none). */
+const char* w4a8_last_error(void);
+
+/*
+ * Size in bytes of the packed weight buffer for an N x K weight with the
+ * given group size; 0 if the shape is unsupported.
+ */
+size_t w4a8_packed_weight_bytes(int64_t N, int64_t K, int32_t group);
+
+/*
+ * w4a8_pack_weights — load-time conversion of GPTQ metadata into the gfx950
+ * packed format (layout version 1).
+ *   q  device uint8 [N][K], int4 codes 0..15, one per byte, row-major
+ *   z  device uint8 [N][K/group], integer zero points 0..15
+ *   s  device float [N][K/group], per-group scales (copied bit for bit)
+ *   packed  device buffer of at least w4a8_packed_weight_bytes(N, K, group)
+ * Requirements: group == 128, K % 128 == 0, N % 16 == 0, N, K > 0.
+ * Only the low 4 bits of q and z are used (callers pass 0..15).
+ *
+ * Format (G = K/128, NB = N/16), three planes in one buffer:
+ *   codes,  N*K/2 bytes at offset 0: block (nb, g) is 1024 bytes at
+ *     (nb*G + g)*1024; inside it lane L = 16*j + c (j = 0..3, c = 0..15)
+ *     owns bytes [16L, 16L+16), and byte i of that run holds
+ *     q[16nb+c][128g+16j+i] in its low nibble and q[16nb+c][128g+64+16j+i]
+ *     in its high nibble;
+ *   zeros,  N*G/2 bytes at Z0 = round_up(N*K/2, 256): block (nb, g) is 8
+ *     bytes at Z0 + (nb*G + g)*8; byte c/2 holds z[16nb+c][g] in its low
+ *     nibble (even c) or high nibble (odd c);
+ *   scales, 4*N*G bytes at S0 = round_up(Z0 + N*G/2, 256): float at index
+ *     (nb*G + g)*16 + c is s[16nb+c][g].
+ * One 64-lane wavefront load of a codes block gives every lane the operands
+ * of two int8 matrix-core steps (or eight 4-way dot products) for one output
+ * channel and 32 input channels of one group.
+ */
+int w4a8_pack_weights(const uint8_t* q, const uint8_t* z, const float* s,
+                      int64_t N, int64_t K, int32_t group,
+                      void* packed, size_t packed_bytes, void* stream);
+
+/* Inverse of w4a8_pack_weights (for tests and inspection): writes q, z, s in
+ * the logical layouts described above. */
+int w4a8_unpack_weights(const void* packed, size_t packed_bytes,
+                        int64_t N, int64_t K, int32_t group,
+                        uint8_t* q, uint8_t* z, float* s, void* stream);
+
+/*
+ * w4a8_quant_act — per-token symmetric int8 activation quantisation
+ * ("The 4-bit CPU path", section "W4A8": activations are quantised to int8).
+ *   x   device [M][K], bfloat16 (x_dtype = W4A8_BF16) or float (W4A8_F32)
+ *   qa  device int8 [M][K]: qa = clamp(rint(x / sa), -127, 127), ties to even
+ *   sa  device float [M]:   sa = max_k |x[m][k]| / 127 (IEEE float division);
+ *       an all-zero row gives sa = 0 and qa = 0
+ * Requirements: M >= 1, K >= 128, K % 128 == 0.
+ */
+int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                   int8_t* qa, float* sa, void* stream);
+
+/* Workspace bytes any path of w4a8_gemm / w4a8_gemm_debug may need for these
+ * shapes (split-K partial sums); 0 if none. */
+size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+
+/* The path W4A8_PATH_AUTO takes for these shapes. */
+int w4a8_select_path(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w4a8_gemm — y[m][n] = bf16_rne( sa[m] * sum_g s[n][g] * P[m][n][g] ),
+ *   P[m][n][g] = sum_{k in group g} qa[m][k] * (q[n][k] - z[n][g])  (exact int32)
+ *   qa  device int8 [M][K] and sa device float [M] (from w4a8_quant_act)
+ *   packed  device buffer from w4a8_pack_weights for the same (N, K, group)
+ *   y   device bfloat16 bits [M][N], row-major
+ *   workspace  device scratch of w4a8_gemm_workspace_bytes(M, N, K, group)
+ *     bytes (may be NULL when that is 0); contents on entry are ignored
+ * The float rescale is accumulated in float32; the result is rounded to
+ * bfloat16 with round-to-nearest-even.
+ */
+int w4a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
+              int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a8_gemm_debug — the same kernels as w4a8_gemm, with a forced path and the
+ * per-group int32 partials written out for rows [m_begin, m_end):
+ *   partials  device int32 [m_end - m_begin][N][K/group] (may be NULL)
+ *   y_or_null device bfloat16 [M][N] or NULL (then y is not written)
+ * path must be AUTO, GEMV (requires M == 1), SKINNY (M <= 16) or PREFILL.
+ */
+int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
+                    int64_t M, int64_t N, int64_t K, int32_t group, int32_t path,
+                    int64_t m_begin, int64_t m_end, int32_t* partials, uint16_t* y_or_null,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

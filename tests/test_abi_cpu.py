@@ -1,0 +1,126 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host (no GPU needed: a
+rejected call returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_amd import _lib
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    from bit_quantized_amd import _lib
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_versions_and_status(lib):
+    assert lib.w4a8_abi_version() == 1
+    assert lib.w4a8_layout_version() == 1
+    assert lib.w4a8_status_string(0) == b"ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert lib.w4a8_status_string(s) != b"unknown status"
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (256, 256), (512, 3584), (18944, 3584), (3584, 18944),
+                                 (48, 384)])
+def test_packed_size_matches_spec(lib, N, K):
+    assert lib.w4a8_packed_weight_bytes(N, K, 128) == oracle.layout_bytes(N, K)
+
+
+def test_packed_size_unsupported(lib):
+    assert lib.w4a8_packed_weight_bytes(80 + 4, 128, 128) == 0
+    assert lib.w4a8_packed_weight_bytes(64, 100, 128) == 0
+    assert lib.w4a8_packed_weight_bytes(64, 256, 64) == 0
+    assert lib.w4a8_packed_weight_bytes(0, 256, 128) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(1 << 24)
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def test_pack_rejections(lib):
+    f = lib.w4a8_pack_weights
+    big = 1 << 30
+    assert f(FAKE, FAKE, FAKE, 16, 100, 128, FAKE2, big, None) == -2     # K % 128
+    assert f(FAKE, FAKE, FAKE, 20, 128, 128, FAKE2, big, None) == -2     # N tail
+    assert f(FAKE, FAKE, FAKE, 16, 128, 64, FAKE2, big, None) == -2      # group
+    assert f(None, FAKE, FAKE, 16, 128, 128, FAKE2, big, None) == -1
+    assert f(MIS, FAKE, FAKE, 16, 128, 128, FAKE2, big, None) == -3
+    assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, 100, None) == -4
+    assert b"too small" in lib.w4a8_last_error() or b"need" in lib.w4a8_last_error()
+
+
+def test_quant_rejections(lib):
+    f = lib.w4a8_quant_act
+    assert f(FAKE, 0, 0, 128, FAKE2, FAKE2, None) == -1
+    assert f(FAKE, 7, 1, 128, FAKE2, FAKE2, None) == -1
+    assert f(FAKE, 0, 1, 130, FAKE2, FAKE2, None) == -2
+    assert f(MIS, 0, 1, 128, FAKE2, ctypes.c_void_p((1 << 24) + 4096), None) == -3
+    assert f(FAKE, 0, 4, 128, FAKE, FAKE2, None) == -1                  # qa aliases x
+
+
+def test_gemm_rejections(lib):
+    f = lib.w4a8_gemm
+    pb = lib.w4a8_packed_weight_bytes(256, 256, 128)
+    y = ctypes.c_void_p(1 << 28)
+    args = dict(qa=FAKE, sa=ctypes.c_void_p((1 << 20) + 65536), packed=FAKE2, pb=pb)
+
+    def call(M=4, N=256, K=256, group=128, pb=pb, y=y, qa=FAKE, ws=None, wsb=0):
+        return f(qa, args["sa"], args["packed"], pb, M, N, K, group, y, ws, wsb, None)
+
+    assert call(M=0) == -1
+    assert call(N=250) == -2
+    assert call(K=200) == -2
+    assert call(group=32) == -2
+    assert call(pb=pb - 1) == -4
+    assert call(qa=None) == -1
+    assert call(qa=MIS) == -3
+    assert call(y=None) == -1
+    assert call(y=FAKE2) == -1                                            # y aliases packed
+    # split-K workspace required but missing
+    need = lib.w4a8_gemm_workspace_bytes(4, 256, 18944, 128)
+    assert need > 0
+    pb2 = lib.w4a8_packed_weight_bytes(256, 18944, 128)
+    assert f(FAKE, args["sa"], FAKE2, pb2, 4, 256, 18944, 128, y, None, 0, None) == -4
+
+
+def test_debug_path_rejections(lib):
+    f = lib.w4a8_gemm_debug
+    pb = lib.w4a8_packed_weight_bytes(256, 256, 128)
+    sa = ctypes.c_void_p((1 << 20) + 65536)
+    y = ctypes.c_void_p(1 << 28)
+    P = ctypes.c_void_p(1 << 29)
+    assert f(FAKE, sa, FAKE2, pb, 4, 256, 256, 128, 1, 0, 4, P, y, None, 0, None) == -1  # GEMV M!=1
+    assert f(FAKE, sa, FAKE2, pb, 17, 256, 256, 128, 2, 0, 4, P, y, None, 0, None) == -1  # SKINNY M>16
+    assert f(FAKE, sa, FAKE2, pb, 4, 256, 256, 128, 9, 0, 4, P, y, None, 0, None) == -1   # bad path
+    assert f(FAKE, sa, FAKE2, pb, 4, 256, 256, 128, 3, 2, 5, P, y, None, 0, None) == -1   # window
+
+
+def test_select_path(lib):
+    assert lib.w4a8_select_path(1, 18944, 3584) == 1
+    assert lib.w4a8_select_path(2, 3584, 18944) == 2
+    assert lib.w4a8_select_path(16, 3584, 18944) == 2
+    assert lib.w4a8_select_path(17, 3584, 18944) == 3
+    assert lib.w4a8_select_path(2048, 18944, 3584) == 3

@@ -1,0 +1,309 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: bit-exact for packing, activation codes/scales and per-group int32
+partials; max|y - y_ref| <= 4e-3 * max|y_ref| per tensor for the bf16 output
+(y_ref is the oracle's unrounded float64 value).  Inputs come from the seeded
+generator only.  Following "Serve a pre-quantized int8 weight-only DiT ...",
+comment "Directive ...", one linear is isolated and M is swept across the
+kernels' bucket and tile edges.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL = 4e-3
+
+
+@pytest.fixture(scope="module")
+def w4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_quantized_amd as w4
+    w4.load()
+    return w4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def x_tensor(lin):
+    x = lin["x"]
+    if x.dtype == np.uint16:
+        return dev(x.view(np.int16)).view(torch.bfloat16)
+    return dev(x)
+
+
+def to_f32(y):
+    return y.float().cpu().numpy()
+
+
+def _setup(w4, spec):
+    lin = synth.make_linear(spec)
+    W = w4.pack_weights(dev(lin["q"]), dev(lin["z"]), dev(lin["s"]))
+    qa_ref, sa_ref = oracle.quant_act(lin["x"])
+    return lin, W, qa_ref, sa_ref
+
+
+def _check_y(y, lin, qa_ref, sa_ref, rows=None):
+    m0, m1 = rows if rows else (0, lin["spec"].M)
+    ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1))
+    got = to_f32(y)[m0:m1]
+    ok, err, bound = oracle.tolerance_ok(got, ref, REL)
+    assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+    return err / max(bound / REL, 1e-30)
+
+
+# ----------------------------------------------------------------- packing
+
+@pytest.mark.parametrize("N,K", [(256, 256), (48, 384), (512, 3584), (3584, 18944)])
+def test_pack_bytes_and_round_trip(w4, N, K):
+    say(f"pack N={N} K={K}")
+    rng = np.random.Generator(np.random.PCG64(N + K))
+    q, z, s = synth.draw_weights(rng, N, K)
+    W = w4.pack_weights(dev(q), dev(z), dev(s))
+    assert np.array_equal(W.buf.cpu().numpy(), oracle.layout_pack(q, z, s))
+    q2, z2, s2 = w4.unpack_weights(W)
+    assert np.array_equal(q2.cpu().numpy(), q)
+    assert np.array_equal(z2.cpu().numpy(), z)
+    assert np.array_equal(s2.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+def test_pack_index_pattern(w4):
+    """Index-pattern probe ("The 4-bit CPU path", section "The weight layout,
+    measured"): pack codes that encode their own position, unpack, and check
+    every code came back from where it went."""
+    N, K = 64, 512
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    q = ((7 * n + k + 3 * (k // 64)) % 16).astype(np.uint8)
+    z = ((np.arange(N)[:, None] + np.arange(K // 128)[None, :]) % 16).astype(np.uint8)
+    s = (np.arange(N * (K // 128), dtype=np.float32).reshape(N, -1) + 0.5)
+    W = w4.pack_weights(dev(q), dev(z), dev(s))
+    assert np.array_equal(W.buf.cpu().numpy(), oracle.layout_pack(q, z, s))
+    q2, z2, s2 = oracle.layout_unpack(W.buf.cpu().numpy(), N, K)
+    assert np.array_equal(q2, q) and np.array_equal(z2, z) and np.array_equal(s2, s)
+
+
+# ----------------------------------------------------------------- quantiser
+
+QUANT_SPECS = [synth.TINY, synth.DECODE_UP, synth.SKINNY_DOWN_16, synth.PREFILL_UP,
+               synth.LinearSpec("m5_f32", 5, 640, 16, seed=9, act="f32")]
+
+
+@pytest.mark.parametrize("spec", QUANT_SPECS, ids=[s.name for s in QUANT_SPECS])
+def test_quant_bit_exact(w4, spec):
+    say(f"quant {spec}")
+    lin = synth.make_linear(spec, with_weights=False)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    qa_ref, sa_ref = oracle.quant_act(lin["x"])
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+
+
+def test_quant_ties_and_zero_rows(w4):
+    say("quant ties")
+    rows = []
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "quant_ties.txt")
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append([float(v) for v in line.split("|")[0].split()])
+    x = np.zeros((len(rows) + 1, 128), np.float32)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = r
+    qa, sa = w4.quant_act(dev(x))
+    qa_ref, sa_ref = oracle.quant_act(x)
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    assert np.array_equal(sa.cpu().numpy(), sa_ref)
+    assert sa_ref[-1] == 0 and not qa_ref[-1].any()
+
+
+def test_quant_random_ties(w4):
+    """Many exact .5 ties: integer-plus-half values with absmax 127."""
+    say("quant random ties")
+    rng = np.random.Generator(np.random.PCG64(77))
+    x = (rng.integers(-127, 127, size=(64, 1024)) + 0.5).astype(np.float32)
+    x[:, 0] = 127.0
+    qa, sa = w4.quant_act(dev(x))
+    qa_ref, sa_ref = oracle.quant_act(x)
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    assert np.array_equal(sa.cpu().numpy(), sa_ref)
+
+
+# ----------------------------------------------------------------- partials + output
+
+def _paths_for(M):
+    paths = [3]
+    if M <= 16:
+        paths.append(2)
+    if M == 1:
+        paths.append(1)
+    return paths
+
+
+@pytest.mark.parametrize("spec", [synth.TINY, synth.DECODE_UP, synth.SKINNY_DOWN_4,
+                                  synth.SKINNY_DOWN_16],
+                         ids=lambda s: s.name)
+def test_partials_and_output_all_paths(w4, spec):
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"])
+    for path in _paths_for(spec.M):
+        say(f"partials {spec.name} path={path}")
+        P, y = w4.gemm_debug(qa, sa, W, path=path)
+        assert np.array_equal(P.cpu().numpy(), P_ref), f"path {path}"
+        _check_y(y, lin, qa_ref, sa_ref)
+    y = w4.gemm(qa, sa, W)
+    _check_y(y, lin, qa_ref, sa_ref)
+
+
+def test_prefill_full_size(w4):
+    """M=2048, K=3584, N=18944: partials bit-exact on two 64-row windows
+    (first tile rows and the last tile), bf16 output on sampled rows."""
+    spec = synth.PREFILL_UP
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    y = w4.gemm(qa, sa, W)
+    for rows in ((0, 64), (1984, 2048)):
+        say(f"prefill partials rows {rows}")
+        P, y_dbg = w4.gemm_debug(qa, sa, W, path=3, rows=rows)
+        P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=rows[0], m1=rows[1])
+        assert np.array_equal(P.cpu().numpy(), P_ref)
+        assert torch.equal(y_dbg, y)
+    say("prefill sampled rows")
+    rng = np.random.Generator(np.random.PCG64(5))
+    for m in sorted(rng.choice(spec.M, 24, replace=False)):
+        _check_y(y, lin, qa_ref, sa_ref, rows=(m, m + 1))
+    _check_y(y, lin, qa_ref, sa_ref, rows=(0, 40))
+
+
+SWEEP_M = list(range(1, 18)) + [31, 32, 33, 63, 64, 65, 127, 128, 129, 300]
+
+
+@pytest.mark.parametrize("M", SWEEP_M)
+def test_m_sweep(w4, M):
+    """Bucket and tile edges with a ragged N (not a multiple of the 128-wide
+    prefill tile) and an odd number of groups."""
+    spec = synth.LinearSpec(f"sweep{M}", M, 384, 208, seed=100 + M)
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"])
+    for path in _paths_for(M):
+        P, y = w4.gemm_debug(qa, sa, W, path=path)
+        assert np.array_equal(P.cpu().numpy(), P_ref), f"M={M} path={path}"
+        _check_y(y, lin, qa_ref, sa_ref)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (32, 128), (16, 1280), (144, 256)])
+def test_degenerate_shapes(w4, N, K):
+    for M in (1, 3, 16, 20):
+        spec = synth.LinearSpec(f"deg{N}x{K}m{M}", M, K, N, seed=N + K + M)
+        lin, W, qa_ref, sa_ref = _setup(w4, spec)
+        qa, sa = w4.quant_act(x_tensor(lin))
+        P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"])
+        for path in _paths_for(M):
+            P, y = w4.gemm_debug(qa, sa, W, path=path)
+            assert np.array_equal(P.cpu().numpy(), P_ref), (N, K, M, path)
+            _check_y(y, lin, qa_ref, sa_ref)
+
+
+def test_identity_scale_exact(w4):
+    """s == 1, integer activations with absmax 127 and |partial sums| < 2^24:
+    the output must equal bf16_rne(x @ (q - z)^T) bit for bit in any
+    accumulation order (numpy int64 matmul supplies the integer product)."""
+    say("identity scale")
+    rng = np.random.Generator(np.random.PCG64(31))
+    for M, K, N in ((1, 3584, 512), (7, 8704, 256), (40, 2048, 384)):
+        xi = rng.integers(-127, 128, size=(M, K))
+        xi[:, 0] = 127
+        q = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        z = rng.integers(0, 16, size=(N, K // 128), dtype=np.uint8)
+        s = np.ones((N, K // 128), np.float32)
+        W = w4.pack_weights(dev(q), dev(z), dev(s))
+        qa, sa = w4.quant_act(dev(xi.astype(np.float32)))
+        exact = xi @ (q.astype(np.int64) - np.repeat(z.astype(np.int64), 128, axis=1)).T
+        expect = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16)
+        for path in _paths_for(M):
+            _, y = w4.gemm_debug(qa, sa, W, path=path)
+            assert torch.equal(y.cpu(), expect), (M, K, N, path)
+
+
+def test_row_independence_and_determinism(w4):
+    say("row independence")
+    spec = synth.LinearSpec("rows", 48, 1024, 256, seed=41)
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    x = x_tensor(lin)
+    y1 = w4.linear(x, W)
+    y2 = w4.linear(x, W)
+    assert torch.equal(y1, y2)
+    x2 = x.clone()
+    x2[1::2] = x2[1::2] * 3 - 1
+    y3 = w4.linear(x2, W)
+    assert torch.equal(y3[0::2], y1[0::2])
+    for M in (1, 4, 16):                       # same row in different buckets
+        qa, sa = w4.quant_act(x[:M].contiguous())
+        for path in _paths_for(M):
+            _, y = w4.gemm_debug(qa, sa, W, path=path)
+            assert torch.equal(w4.gemm_debug(qa, sa, W, path=path)[1], y)
+
+
+def test_zero_weights_and_scales(w4):
+    spec = synth.LinearSpec("zeros", 20, 256, 64, seed=43)
+    lin = synth.make_linear(spec)
+    z = lin["z"]
+    q = np.repeat(z, 128, axis=1)
+    for M in (1, 5, 20):
+        qa, sa = w4.quant_act(x_tensor(lin)[:M].contiguous())
+        W = w4.pack_weights(dev(q), dev(z), dev(lin["s"]))
+        for path in _paths_for(M):
+            P, y = w4.gemm_debug(qa, sa, W, path=path)
+            assert not P.any() and not y.float().any()
+        W0 = w4.pack_weights(dev(lin["q"]), dev(z), dev(np.zeros_like(lin["s"])))
+        for path in _paths_for(M):
+            _, y = w4.gemm_debug(qa, sa, W0, path=path)
+            assert not y.float().any()
+
+
+def test_errors_leave_outputs_untouched(w4):
+    spec = synth.LinearSpec("err", 4, 256, 64, seed=44)
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    y = torch.full((4, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    bad = w4.PackedWeight(W.buf[:100], W.N, W.K, W.group, W.layout_version)
+    with pytest.raises(w4.W4A8Error) as ei:
+        w4.gemm(qa, sa, bad, out=y)
+    assert ei.value.status == -4
+    torch.cuda.synchronize()
+    assert torch.all(y.float() == 7.0)
+
+
+@pytest.mark.parametrize("name,K,N", [("k", 3584, 512), ("o", 3584, 3584), ("down", 18944, 3584)])
+@pytest.mark.parametrize("M", [1, 512])
+def test_layer_linears(w4, name, K, N, M):
+    spec = synth.LinearSpec(f"layer_{name}_m{M}", M, K, N, seed=4000 + K + N)
+    say(f"layer {spec}")
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    y = w4.gemm(qa, sa, W)
+    rows = (0, M) if M == 1 else (0, 64)
+    _check_y(y, lin, qa_ref, sa_ref, rows=rows)
+    P, _ = w4.gemm_debug(qa, sa, W, path=w4.select_path(M, N, K), rows=(M - 1, M), want_y=False)
+    P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=M - 1, m1=M)
+    assert np.array_equal(P.cpu().numpy(), P_ref)
