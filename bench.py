@@ -1,0 +1,345 @@
+#!/usr/bin/env python
+"""Benchmark of the W4A8 linear layer on one MI355X.
+
+Headline (one JSON line on stdout): decode throughput in GB/s of algorithmic
+bytes for one step of the decode workload — per-token int8 quantisation plus
+the W4A8 GEMV — at M=1, K=3584 -> N=18944, group 128 (a 7B-decoder MLP
+up-projection).  The same line carries:
+  roofline      the dominant kernel (the GEMV) against MI355X's 8 TB/s HBM
+  cpu_baseline  the CPU oracle timed on this host's cores on the same workload
+  prefill       the M=2048 prefill GEMM in int8 TOPS against 5.0 POP/s
+
+Timing: inputs are resident in HBM before the timed region; each timed step
+reads a different packed copy of the weights (16 copies, > 512 MB) so the
+256 MB Infinity Cache cannot serve them.  Steps run from a captured HIP graph
+(the launch-bound inner loop), timed with HIP events on the replay stream; the
+dominant kernel's average duration comes the same way from a graph of that
+kernel's launches alone (back to back, as rocprofv3 sees them).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 linear: decode GB/s (% HBM peak) at M=1; prefill int8 TOPS (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--copies", type=int, default=16, help="packed weight copies rotated per step")
+    p.add_argument("--prefill-steps", type=int, default=32)
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--only", choices=["all", "decode", "prefill", "copy"], default="all",
+                   help="run one part only (for hardware-counter passes)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(M, N, K, group=128, act_bytes=2):
+    """Bytes the method must move for one linear: packed int4 codes, 4-bit
+    zeros, fp32 scales, activations in and bf16 output out."""
+    G = K // group
+    return N * K // 2 + N * G // 2 + 4 * N * G + act_bytes * M * K + 2 * M * N
+
+
+def gemm_bytes(M, N, K, group=128):
+    """Bytes one GEMM launch must move: packed planes, int8 codes and fp32
+    scales of the activations in, bf16 output out."""
+    G = K // group
+    return N * K // 2 + N * G // 2 + 4 * N * G + M * K + 4 * M + 2 * M * N
+
+
+def graph_launches_ms(torch, launch, n):
+    """Average duration of launch(i) over n back-to-back launches replayed
+    from one captured HIP graph (no host gaps between kernels), timed with
+    events on the replay stream."""
+    return graph_steps_ms(torch, launch, min(n, 8), n) / n
+
+
+def graph_steps_ms(torch, step, warmup, steps):
+    """Capture `steps` calls of step(i) in one HIP graph, replay it, and time
+    the replay between a synchronize and events on the replay stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                 # eager warmup outside capture
+        for i in range(min(warmup, 4)):
+            step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw):
+        for i in range(warmup):
+            step(i)
+    with torch.cuda.graph(gt):
+        for i in range(steps):
+            step(i)
+    gw.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    gt.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def to_dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def x_dev(torch, lin):
+    x = lin["x"]
+    if x.dtype == np.uint16:
+        return to_dev(torch, x.view(np.int16)).view(torch.bfloat16)
+    return to_dev(torch, x)
+
+
+def setup_linear(torch, w4, spec, copies):
+    from bit_quantized_amd import synth
+    lin = synth.make_linear(spec)
+    q, z, s = (to_dev(torch, lin[k]) for k in ("q", "z", "s"))
+    Ws = [w4.pack_weights(q, z, s) for _ in range(copies)]
+    del q, z, s
+    x = x_dev(torch, lin)
+    return lin, x, Ws
+
+
+def parity_check(w4, lin, x, W, rows=None):
+    """The benchmarked path against the oracle before timing."""
+    import oracle
+    y = w4.linear(x, W).float().cpu().numpy()
+    qa_ref, sa_ref = oracle.quant_act(lin["x"])
+    m0, m1 = rows or (0, lin["spec"].M)
+    ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1))
+    ok, err, bound = oracle.tolerance_ok(y[m0:m1], ref)
+    if not ok:
+        raise SystemExit(f"parity check failed: max err {err:.3e} > {bound:.3e}")
+    return {"rows": [m0, m1], "max_err": err, "bound": bound}
+
+
+def bench_decode(torch, w4, args):
+    from bit_quantized_amd import synth
+    spec = synth.DECODE_UP
+    lin, x, Ws = setup_linear(torch, w4, spec, args.copies)
+    M, K, N = spec.M, spec.K, spec.N
+    parity = parity_check(w4, lin, x, Ws[0])
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    wsb = w4.workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    R = len(Ws)
+
+    def step(i):
+        w4.quant_act(x, qa, sa)
+        w4.gemm(qa, sa, Ws[i % R], out=y, workspace=ws)
+
+    total_ms = graph_steps_ms(torch, step, args.warmup, args.steps)
+    w4.quant_act(x, qa, sa)
+    kern_ms = graph_launches_ms(torch, lambda i: w4.gemm(qa, sa, Ws[i % R], out=y, workspace=ws),
+                                args.steps)
+    quant_ms = graph_launches_ms(torch, lambda i: w4.quant_act(x, qa, sa), args.steps)
+    step_bytes = algorithmic_bytes(M, N, K)
+    launch_bytes = gemm_bytes(M, N, K)
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = launch_bytes / (kern_ms * 1e-3) / 1e9
+    path = {1: "gemv", 2: "skinny", 3: "prefill"}[w4.select_path(M, N, K)]
+    return {
+        "spec": spec, "lin": lin, "value": value, "ms_per_step": ms_per_step,
+        "step_bytes": step_bytes, "parity": parity, "path": path,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"w4a8 {path} (M={M}, K={K}, N={N})",
+                     "bytes_per_launch": launch_bytes,
+                     "avg_launch_us": round(kern_ms * 1e3, 3),
+                     "timing": f"{args.steps} launches replayed from one HIP graph"},
+        "quant_us": round(quant_ms * 1e3, 3),
+    }
+
+
+def bench_prefill(torch, w4, args):
+    from bit_quantized_amd import synth
+    spec = synth.PREFILL_UP
+    copies = max(2, min(args.copies, 8))
+    lin, x, Ws = setup_linear(torch, w4, spec, copies)
+    M, K, N = spec.M, spec.K, spec.N
+    parity = parity_check(w4, lin, x, Ws[0], rows=(0, 48))
+    qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    R = len(Ws)
+
+    def step(i):
+        w4.quant_act(x, qa, sa)
+        w4.gemm(qa, sa, Ws[i % R], out=y)
+
+    n = args.prefill_steps
+    total_ms = graph_steps_ms(torch, step, max(2, n // 4), n)
+    w4.quant_act(x, qa, sa)
+    kern_ms = graph_launches_ms(torch, lambda i: w4.gemm(qa, sa, Ws[i % R], out=y), n)
+    ops = 2.0 * M * N * K
+    tops_kernel = ops / (kern_ms * 1e-3) / 1e12
+    tops_step = ops / (total_ms / n * 1e-3) / 1e12
+    return {
+        "spec": spec, "lin": lin, "parity": parity,
+        "workload": f"prefill_up M={M} K={K} N={N} group=128 (quant + GEMM)",
+        "value": round(tops_step, 1), "unit": "TOPS", "ms_per_step": total_ms / n,
+        "roofline": {"bound": "mfma", "achieved": round(tops_kernel, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
+                     "traffic": None, "kernel": f"w4a8 prefill (M={M}, K={K}, N={N})",
+                     "ops_per_launch": ops, "avg_launch_us": round(kern_ms * 1e3, 2),
+                     "timing": f"{n} launches replayed from one HIP graph"},
+    }
+
+
+def cpu_baseline_decode(res, seconds):
+    """The oracle as it stands on this host: one decode step = quantise the
+    token and compute all N outputs (exact per-group int products, float64
+    rescale), repeated for about `seconds`."""
+    import oracle
+    lin = res["lin"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        qa, sa = oracle.quant_act(lin["x"])
+        oracle.linear(qa, sa, lin["q"], lin["z"], lin["s"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(res["step_bytes"] * reps / el / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{reps} full decode steps (quant + all 18944 outputs) in {el:.1f} s"}
+
+
+def cpu_baseline_prefill(res, seconds):
+    import oracle
+    lin = res["lin"]
+    M, K, N = lin["spec"].M, lin["spec"].K, lin["spec"].N
+    t0 = time.perf_counter()
+    qa, sa = oracle.quant_act(lin["x"])
+    rows, m0 = 0, 0
+    while time.perf_counter() - t0 < seconds and m0 < M:
+        oracle.linear(qa, sa, lin["q"], lin["z"], lin["s"], rows=(m0, m0 + 8))
+        m0 += 8
+        rows += 8
+    el = time.perf_counter() - t0
+    return {"value": round(2.0 * rows * N * K / el / 1e12, 4), "unit": "TOPS",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"quant of all {M} rows + outputs of {rows} rows in {el:.1f} s"}
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, for scaling hardware byte counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(8):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 8}))
+
+
+def gpu_info(torch):
+    info = {"device": torch.cuda.get_device_name(0)}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        info["gcn_arch"] = getattr(props, "gcnArchName", "")
+        info["cus"] = props.multi_processor_count
+    except Exception:
+        pass
+    try:
+        info["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                                     capture_output=True, text=True).stdout.strip() or None
+    except Exception:
+        info["git"] = None
+    return info
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the W4A8 linear here has no multi-GPU path "
+              "(sharding is a design note only); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_amd as w4
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w4.load()
+    if args.only == "copy":
+        copy_calibration(torch)
+        return
+
+    dec = pre = None
+    if args.only in ("all", "decode"):
+        dec = bench_decode(torch, w4, args)
+    if args.only in ("all", "prefill") and not args.no_prefill:
+        pre = bench_prefill(torch, w4, args)
+    cpu_dec = cpu_pre = None
+    if not args.no_cpu_baseline and args.only == "all":
+        if dec:
+            cpu_dec = cpu_baseline_decode(dec, args.cpu_seconds)
+        if pre:
+            cpu_pre = cpu_baseline_prefill(pre, max(2.0, args.cpu_seconds / 3))
+
+    from bit_quantized_amd import synth
+    if dec is None:
+        out = {"metric": METRIC, "prefill": {k: v for k, v in pre.items() if k not in ("spec", "lin")}}
+        print(json.dumps(out))
+        return
+    spec = dec["spec"]
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"decode_up M={spec.M} K={spec.K} N={spec.N} group=128 "
+                               f"(per-token int8 quant + W4A8 {dec['path']})",
+                   "M": spec.M, "K": spec.K, "N": spec.N, "group": 128,
+                   "activations": "bf16 N(0,1), 0.5% channels x20", "seed": spec.seed,
+                   "input_sha256_16": synth.digest(dec["lin"]), "weight_copies": args.copies,
+                   "bytes_per_step": dec["step_bytes"], "timing": "hip graph of steps",
+                   "parallelism": "single GPU"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu_dec,
+        "quant_kernel_us": dec["quant_us"],
+        "parity": dec["parity"],
+    }
+    if pre:
+        p = {k: v for k, v in pre.items() if k not in ("spec", "lin")}
+        p["cpu_baseline"] = cpu_pre
+        line["prefill"] = p
+    line["system"] = gpu_info(torch)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

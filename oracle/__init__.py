@@ -56,6 +56,7 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.oracle_version.restype = ctypes.c_int
+    lib.oracle_threads.restype = ctypes.c_int
     for name, args in {
         "oracle_quant_act_f32": [vp, i64, i64, vp, vp],
         "oracle_quant_act_bf16": [vp, i64, i64, vp, vp],
@@ -134,6 +135,11 @@ def linear(qa, sa, q, z, s, group=128, rows=None, cols=None, mutant: int = 0):
     _check(lib.oracle_linear(_ptr(qa), _ptr(sa), _ptr(q), _ptr(z), _ptr(s), M, N, K, group,
                              m0, m1, n0, n1, _ptr(y)), "linear")
     return y
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(load().oracle_threads())
 
 
 def layout_bytes(N: int, K: int) -> int:

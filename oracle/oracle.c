@@ -57,6 +57,14 @@
 
 int oracle_version(void) { return 1 + 100 * ORACLE_MUTANT; }
 
+/* Threads the OpenMP loops below run on (reported beside CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif
+
 static float widen_bf16(uint16_t b) {
     uint32_t u = (uint32_t)b << 16;
     float f;
