@@ -6,6 +6,6 @@ Python binding (torch for device memory and streams only).
 """
 from ._lib import (  # noqa: F401
     BF16, F32, GROUP, PATH_AUTO, PATH_GEMV, PATH_PREFILL, PATH_SKINNY, PackedWeight, W4A8Error,
-    gemm, gemm_debug, linear, load, pack_weights, packed_weight_bytes, quant_act, select_path,
+    gemm, gemm_debug, linear, linear_workspace_bytes, load, pack_weights, packed_weight_bytes, quant_act, select_path,
     unpack_weights, workspace_bytes,
 )

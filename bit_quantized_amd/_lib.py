@@ -48,6 +48,9 @@ SIGNATURES = {
     "w4a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
     "w4a8_gemm_debug": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _i32, _i64,
                                        _i64, _vp, _vp, _vp, _sz, _vp]),
+    "w4a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "w4a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz,
+                                   _vp]),
 }
 
 _lib = None
@@ -211,7 +214,30 @@ def gemm_debug(qa, sa, w: PackedWeight, path: int = PATH_AUTO, rows=None, want_y
     return P, y
 
 
+def linear_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    return int(load().w4a8_linear_workspace_bytes(M, N, K, group))
+
+
 def linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None) -> torch.Tensor:
-    """Quantise activations per token, then the W4A8 GEMM (two launches)."""
-    qa, sa = quant_act(x)
-    return gemm(qa, sa, w, out=out, workspace=workspace)
+    """The layer from raw bf16/f32 activations: per-token quantisation and the
+    W4A8 GEMM (one launch at M == 1, where the GEMV quantises in-kernel)."""
+    lib = load()
+    w.check()
+    _need_cuda(x, out)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError(x.dtype)
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    need = linear_workspace_bytes(M, w.N, w.K, w.group)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w4a8_linear(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, _p(out),
+                           _p(workspace), wsb, _stream(x.device)))
+    return out

@@ -62,45 +62,80 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
   return a < b + m && b < a + n;
 }
 
-int pick_path(int64_t M) {
-  if (M == 1) return W4A8_PATH_GEMV;
+int pick_path(int64_t M, int64_t K) {
+  if (M == 1 && K <= kGemvMaxK) return W4A8_PATH_GEMV;
   if (M <= 16) return W4A8_PATH_SKINNY;
   return W4A8_PATH_PREFILL;
 }
 
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
-  if (path == W4A8_PATH_GEMV) return gemv_ksplit(M, N, K);
+  if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
   return 1;
 }
 
+// Split-K partial sums [ksplit][M][N] float, then (GEMV only) one 256-byte
+// slot for the scale the fused quantiser computes.
 size_t workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = ksplit_for(path, M, N, K);
-  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
+  if (ks <= 1) return 0;
+  size_t b = (size_t)ks * (size_t)M * (size_t)N * sizeof(float);
+  b = (b + 255) / 256 * 256;
+  return path == W4A8_PATH_GEMV ? b + 256 : b;
 }
 
-int run_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
-             int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int64_t m_begin,
-             int64_t m_end, int32_t* partials, uint16_t* y, void* workspace,
-             size_t workspace_bytes, void* stream, bool debug) {
+size_t gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
+  size_t need = 0;
+  for (int p = W4A8_PATH_GEMV; p <= W4A8_PATH_PREFILL; ++p) {
+    if (p == W4A8_PATH_GEMV && (M != 1 || K > kGemvMaxK)) continue;
+    if (p == W4A8_PATH_SKINNY && M > 16) continue;
+    const size_t w = workspace_for(p, M, N, K);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Activations for a GEMM: either quantised (qa, sa) or raw x that the M == 1
+// GEMV quantises in its prologue.
+struct ActIn {
+  const int8_t* qa;
+  const float* sa;
+  const void* x;
+  int x_dtype;
+};
+
+int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
+             int64_t K, int32_t group, int32_t path, int64_t m_begin, int64_t m_end,
+             int32_t* partials, uint16_t* y, void* workspace, size_t workspace_bytes,
+             void* stream, bool debug, bool validate_only = false) {
   int rc = check_weight_shape(N, K, group);
   if (rc) return rc;
   if (M <= 0 || M > ((int64_t)1 << 24))
     return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
-  if (!qa || !sa || !packed) return fail(W4A8_ERR_INVALID_ARG, "null input pointer");
-  if (!debug && !y) return fail(W4A8_ERR_INVALID_ARG, "null output pointer");
-  if (!aligned16(qa) || !aligned16(sa) || !aligned16(packed) || (y && !aligned16(y)))
+  const bool fused = act.x != nullptr;
+  if (!packed || (!fused && (!act.qa || !act.sa)))
+    return fail(W4A8_ERR_INVALID_ARG, "null input pointer");
+  if (!debug && !validate_only && !y) return fail(W4A8_ERR_INVALID_ARG, "null output pointer");
+  if (!aligned16(packed) || (y && !aligned16(y)) ||
+      (!fused && (!aligned16(act.qa) || !aligned16(act.sa))) || (fused && !aligned16(act.x)))
     return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
   const size_t need = (size_t)packed_bytes(N, K);
   if (packed_bytes_ < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
-  if (path == W4A8_PATH_AUTO) path = pick_path(M);
-  if (path == W4A8_PATH_GEMV && M != 1)
-    return fail(W4A8_ERR_INVALID_ARG, "GEMV path needs M == 1 (M=%lld)", (long long)M);
-  if (path == W4A8_PATH_SKINNY && M > 16)
-    return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
+  if (path == W4A8_PATH_AUTO) path = pick_path(M, K);
   if (path < W4A8_PATH_GEMV || path > W4A8_PATH_PREFILL)
     return fail(W4A8_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (path == W4A8_PATH_GEMV && M != 1)
+    return fail(W4A8_ERR_INVALID_ARG, "GEMV path needs M == 1 (M=%lld)", (long long)M);
+  if (path == W4A8_PATH_GEMV && K > kGemvMaxK)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "GEMV path needs K <= %lld (K=%lld)",
+                (long long)kGemvMaxK, (long long)K);
+  if (path == W4A8_PATH_SKINNY && M > 16)
+    return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
+  if (fused && path != W4A8_PATH_GEMV)
+    return fail(W4A8_ERR_INVALID_ARG, "in-kernel quantisation runs on the GEMV path only");
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
       return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
@@ -116,15 +151,20 @@ int run_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packe
   if (ws_need && !aligned16(workspace))
     return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   const size_t ybytes = (size_t)M * (size_t)N * 2;
-  if (y && (overlaps(y, ybytes, qa, (size_t)M * K) || overlaps(y, ybytes, sa, (size_t)M * 4) ||
-            overlaps(y, ybytes, packed, need) ||
+  const size_t xbytes = (size_t)M * K * (act.x_dtype == W4A8_F32 ? 4 : 2);
+  if (y && ((!fused && (overlaps(y, ybytes, act.qa, (size_t)M * K) ||
+                        overlaps(y, ybytes, act.sa, (size_t)M * 4))) ||
+            (fused && overlaps(y, ybytes, act.x, xbytes)) || overlaps(y, ybytes, packed, need) ||
             (ws_need && overlaps(y, ybytes, workspace, ws_need))))
     return fail(W4A8_ERR_INVALID_ARG, "output aliases an input or the workspace");
+  if (validate_only) return ok();
 
   const uint8_t* base = static_cast<const uint8_t*>(packed);
   GemmArgs a;
-  a.qa = qa;
-  a.sa = sa;
+  a.qa = act.qa;
+  a.sa = act.sa;
+  a.x = act.x;
+  a.x_dtype = act.x_dtype;
   a.w.codes = base;
   a.w.zeros = base + zeros_offset(N, K);
   a.w.scales = reinterpret_cast<const float*>(base + scales_offset(N, K));
@@ -136,7 +176,22 @@ int run_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packe
   a.m_begin = debug ? m_begin : 0;
   a.m_end = debug ? m_end : 0;
   a.workspace = static_cast<float*>(workspace);
+  a.sa_ws = nullptr;
   a.ksplit = ks;
+  a.cb = a.ks = 0;
+  const float* sa_for_reduce = act.sa;
+  if (path == W4A8_PATH_GEMV) {
+    const GemvShape gs = gemv_shape(N, K);
+    if (!gemv_shape_ok(N, K, gs))
+      return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "no GEMV grid for N=%lld K=%lld", (long long)N,
+                  (long long)K);
+    a.cb = gs.cb;
+    a.ks = gs.ks;
+    if (fused && ks > 1) {
+      a.sa_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_need - 256);
+      sa_for_reduce = a.sa_ws;
+    }
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
@@ -147,8 +202,16 @@ int run_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packe
     e = launch_skinny(a, st);
   else
     e = launch_prefill(a, st);
-  if (e == hipSuccess && ks > 1 && y) e = launch_splitk_reduce(a.workspace, ks, sa, M, N, y, st);
+  if (e == hipSuccess && ks > 1 && y)
+    e = launch_splitk_reduce(a.workspace, ks, sa_for_reduce, M, N, y, st);
   return device_status(e, "gemm launch");
+}
+
+// Workspace of w4a8_linear: the fused GEMV's own, or quantised activations
+// (qa, sa) followed by the GEMM's workspace.
+size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
+  if (pick_path(M, K) == W4A8_PATH_GEMV) return workspace_for(W4A8_PATH_GEMV, M, N, K);
+  return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
 }
 
 }  // namespace
@@ -235,31 +298,68 @@ int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t*
 
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (check_weight_shape(N, K, group) || M <= 0) return 0;
-  size_t need = 0;
-  for (int p = W4A8_PATH_GEMV; p <= W4A8_PATH_PREFILL; ++p) {
-    if (p == W4A8_PATH_GEMV && M != 1) continue;
-    if (p == W4A8_PATH_SKINNY && M > 16) continue;
-    const size_t w = workspace_for(p, M, N, K);
-    if (w > need) need = w;
-  }
-  return need;
+  return gemm_workspace_any(M, N, K);
 }
 
-int w4a8_select_path(int64_t M, int64_t, int64_t) { return M <= 0 ? 0 : pick_path(M); }
+int w4a8_select_path(int64_t M, int64_t, int64_t K) { return M <= 0 ? 0 : pick_path(M, K); }
 
 int w4a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
               int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y, void* workspace,
               size_t workspace_bytes, void* stream) {
-  return run_gemm(qa, sa, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO, 0, 0, nullptr, y,
-                  workspace, workspace_bytes, stream, false);
+  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group,
+                  W4A8_PATH_AUTO, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
 }
 
 int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int64_t m_begin,
                     int64_t m_end, int32_t* partials, uint16_t* y_or_null, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return run_gemm(qa, sa, packed, packed_bytes_, M, N, K, group, path, m_begin, m_end, partials,
-                  y_or_null, workspace, workspace_bytes, stream, true);
+  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, path, m_begin,
+                  m_end, partials, y_or_null, workspace, workspace_bytes, stream, true);
+}
+
+size_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (check_weight_shape(N, K, group) || M <= 0) return 0;
+  return linear_workspace(M, N, K);
+}
+
+int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes_,
+                int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (!x || !y) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
+    return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (pick_path(M, K) == W4A8_PATH_GEMV)
+    return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
+                    W4A8_PATH_GEMV, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
+  // Two launches: quantise into the workspace, then the GEMM.
+  const size_t need = linear_workspace(M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const size_t xbytes = (size_t)M * K * (x_dtype == W4A8_F32 ? 4 : 2);
+  if (overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, packed, packed_bytes_))
+    return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
+  if (overlaps(y, (size_t)M * N * 2, x, xbytes))
+    return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qa = reinterpret_cast<int8_t*>(ws);
+  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
+  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
+  // Validate the GEMM before launching the quantiser, so a rejected call
+  // launches nothing.
+  rc = run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
+                0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+                /*validate_only=*/true);
+  if (rc) return rc;
+  rc = w4a8_quant_act(x, x_dtype, M, K, qa, sa, stream);
+  if (rc) return rc;
+  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group,
+                  W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// Decode-side kernels: the M == 1 GEMV, the 2 <= M <= 16 skinny GEMM, and
-// the deterministic split-K reduction both use when N alone cannot fill the
+// Decode-side kernels: the 2 <= M <= 16 skinny GEMM and the deterministic
+// split-K reduction it (and the M == 1 GEMV) use when N alone cannot fill the
 // chip.
 //
 // "The 4-bit CPU path", section "W4A16": a kernel whose cost is dominated by
@@ -24,87 +24,6 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t 
     if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(a.sa[m] * v);
   } else {
     a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + n] = v;
-  }
-}
-
-// ------------------------------------------------------------------ M == 1
-//
-// Wavefront lane l = 16*j + c owns output channel c of the block and the 32
-// input channels {16j..16j+15} u {64+16j..64+16j+15} of every group it
-// visits: one 16-byte load per group, eight signed 4-way dot products against
-// the matching activation bytes, one int32 per lane per group.  The four
-// lanes of a channel hold disjoint quarters of the group; since the rescale
-// by s[n][g] is linear they are rescaled separately and summed once at the
-// end with cross-lane shuffles (the exact group sum is formed only for the
-// debug partials).
-template <bool DEBUG>
-__global__ void __launch_bounds__(kThreads)
-gemv_kernel(GemmArgs a) {
-  __shared__ float red[kWaves][16];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c = lane & 15, j = lane >> 4;
-  const int64_t nb = blockIdx.x;
-  const int64_t G = a.K / kGroup;
-  const int parts = a.ksplit * kWaves;
-  const int pidx = blockIdx.y * kWaves + wave;
-  const int64_t gb = slice_begin(G, parts, pidx), ge = slice_begin(G, parts, pidx + 1);
-  const uint8_t* codes = a.w.codes + nb * G * kBlockBytes + 16 * lane;
-  const uint8_t* zeros = a.w.zeros + nb * G * kZeroBlockBytes;
-  const float* scales = a.w.scales + nb * G * 16 + c;
-  const int8_t* act = a.qa + 16 * j;
-
-  float accf = 0.0f;
-  constexpr int U = 8;
-  for (int64_t g0 = gb; g0 < ge; g0 += U) {
-    uint4 wv[U], alo[U], ahi[U];
-    float sv[U];
-    uint32_t zv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (g0 + u < ge) {
-        const int64_t g = g0 + u;
-        wv[u] = *reinterpret_cast<const uint4*>(codes + g * kBlockBytes);
-        alo[u] = *reinterpret_cast<const uint4*>(act + g * kGroup);
-        ahi[u] = *reinterpret_cast<const uint4*>(act + g * kGroup + 64);
-        sv[u] = scales[g * 16];
-        zv[u] = zero_of(zeros + g * kZeroBlockBytes, c);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (g0 + u < ge) {
-        const uint32_t zz = zv[u] * 0x01010101u;
-        const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-        const uint32_t al[4] = {alo[u].x, alo[u].y, alo[u].z, alo[u].w};
-        const uint32_t ah[4] = {ahi[u].x, ahi[u].y, ahi[u].z, ahi[u].w};
-        int acc = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = sub_zero_bytes(d[w] & 0x0F0F0F0Fu, zz);
-          const uint32_t hi = sub_zero_bytes((d[w] >> 4) & 0x0F0F0F0Fu, zz);
-          acc = __builtin_amdgcn_sdot4((int)lo, (int)al[w], acc, false);
-          acc = __builtin_amdgcn_sdot4((int)hi, (int)ah[w], acc, false);
-        }
-        if (DEBUG) {
-          int p = acc + __shfl_xor(acc, 16);
-          p += __shfl_xor(p, 32);
-          if (j == 0 && a.partials && a.m_begin == 0 && a.m_end > 0)
-            a.partials[(16 * nb + c) * G + (g0 + u)] = p;
-        }
-        accf += sv[u] * (float)acc;
-      }
-    }
-  }
-  accf += __shfl_xor(accf, 16);
-  accf += __shfl_xor(accf, 32);
-  if (j == 0) red[wave][c] = accf;
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    float t = red[0][c];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) t += red[w][c];
-    store_out(a, 0, 16 * nb + c, t);
   }
 }
 
@@ -200,7 +119,9 @@ skinny_kernel(GemmArgs a) {
   }
 }
 
-// y[m][n] = bf16(sa[m] * sum_k ws[k][m][n]), summed in split order.
+// y[m][n] = bf16(sa[m] * sum_k ws[k][m][n]), summed in split order.  The
+// per-token scale comes from `sa` (a device array written before this kernel
+// runs: by the caller, or by the fused-quant GEMV).
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __restrict__ sa,
                      int64_t M, int64_t N, uint16_t* __restrict__ y) {
@@ -223,17 +144,7 @@ int pick_ksplit(int64_t N, int64_t K) {
 
 }  // namespace
 
-int gemv_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
-
-hipError_t launch_gemv(const GemmArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
-  if (a.partials)
-    hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);

@@ -66,18 +66,29 @@ hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t
                         hipStream_t st);
 
 struct GemmArgs {
-  const int8_t* qa;
-  const float* sa;
+  const int8_t* qa;       // quantised activations [M][K] (null when x is quantised in-kernel)
+  const float* sa;        // per-token scales [M]
+  const void* x;          // raw activations for the fused-quant GEMV, else null
+  int x_dtype;            // W4A8_BF16 / W4A8_F32 when x is set
   PackedView w;
   int64_t M, N, K;
   uint16_t* y;            // may be null in debug mode
   int32_t* partials;      // debug only, may be null
   int64_t m_begin, m_end; // debug row window
-  float* workspace;       // split-K partial sums
+  float* workspace;       // split-K partial sums [ksplit][M][N]
+  float* sa_ws;           // fused quant + split-K: the scale, for the reduction
   int ksplit;
+  int cb, ks;             // GEMV: workgroups along N, wavefronts per workgroup
 };
 
-int gemv_ksplit(int64_t M, int64_t N, int64_t K);
+// Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
+constexpr int64_t kGemvMaxK = 32768;
+
+struct GemvShape {
+  int cb, ks, ksplit;
+};
+GemvShape gemv_shape(int64_t N, int64_t K);
+bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s);
 int skinny_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st);

@@ -59,8 +59,9 @@ extern "C" {
 #define W4A8_BF16 0
 #define W4A8_F32 1
 
-/* GEMM paths (M buckets).  AUTO picks GEMV for M == 1, SKINNY for
- * 2 <= M <= 16, PREFILL for M > 16; the choice depends on (M, N, K) only. */
+/* GEMM paths (M buckets).  AUTO picks GEMV for M == 1 (K <= 32768, else
+ * SKINNY), SKINNY for 2 <= M <= 16, PREFILL for M > 16; the choice depends on
+ * (M, N, K) only. */
 #define W4A8_PATH_AUTO 0
 #define W4A8_PATH_GEMV 1
 #define W4A8_PATH_SKINNY 2
@@ -154,12 +155,31 @@ int w4a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t pack
  * per-group int32 partials written out for rows [m_begin, m_end):
  *   partials  device int32 [m_end - m_begin][N][K/group] (may be NULL)
  *   y_or_null device bfloat16 [M][N] or NULL (then y is not written)
- * path must be AUTO, GEMV (requires M == 1), SKINNY (M <= 16) or PREFILL.
+ * path must be AUTO, GEMV (requires M == 1 and K <= 32768), SKINNY
+ * (M <= 16) or PREFILL.
  */
 int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path,
                     int64_t m_begin, int64_t m_end, int32_t* partials, uint16_t* y_or_null,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * w4a8_linear — the whole layer from raw activations: per-token int8
+ * quantisation (the rule of w4a8_quant_act) followed by the GEMM of
+ * w4a8_gemm.  For M == 1 (and K <= 32768) both run in ONE launch: the decode
+ * GEMV quantises the token in its prologue, so a decode step has no separate
+ * quantisation kernel.  Otherwise the codes are written to the workspace and
+ * the GEMM of the selected path follows (two launches).  The result is
+ * bitwise identical to w4a8_quant_act followed by w4a8_gemm.
+ *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
+ *   y   device bfloat16 bits [M][N]
+ *   workspace  device scratch of w4a8_linear_workspace_bytes(M, N, K, group)
+ *     bytes (may be NULL when that is 0)
+ */
+size_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes,
+                int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -124,3 +124,16 @@ def test_select_path(lib):
     assert lib.w4a8_select_path(16, 3584, 18944) == 2
     assert lib.w4a8_select_path(17, 3584, 18944) == 3
     assert lib.w4a8_select_path(2048, 18944, 3584) == 3
+
+
+def test_linear_rejections(lib):
+    f = lib.w4a8_linear
+    pb = lib.w4a8_packed_weight_bytes(256, 256, 128)
+    y = ctypes.c_void_p(1 << 28)
+    assert f(None, 0, FAKE2, pb, 1, 256, 256, 128, y, None, 0, None) == -1
+    assert f(FAKE, 5, FAKE2, pb, 1, 256, 256, 128, y, None, 0, None) == -1
+    assert f(FAKE, 0, FAKE2, pb, 1, 250, 256, 128, y, None, 0, None) == -2
+    assert f(FAKE, 0, FAKE2, pb - 16, 1, 256, 256, 128, y, None, 0, None) == -4
+    assert f(FAKE, 0, FAKE2, pb, 4, 256, 256, 128, y, None, 0, None) == -4     # needs workspace
+    assert lib.w4a8_linear_workspace_bytes(1, 18944, 3584, 128) == 0          # one launch
+    assert lib.w4a8_linear_workspace_bytes(4, 256, 256, 128) >= 4 * 256 + 16

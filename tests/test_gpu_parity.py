@@ -307,3 +307,47 @@ def test_layer_linears(w4, name, K, N, M):
     P, _ = w4.gemm_debug(qa, sa, W, path=w4.select_path(M, N, K), rows=(M - 1, M), want_y=False)
     P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=M - 1, m1=M)
     assert np.array_equal(P.cpu().numpy(), P_ref)
+
+
+# ----------------------------------------------------------------- fused linear
+
+LINEAR_SPECS = [
+    synth.DECODE_UP,
+    synth.LinearSpec("lin_tiny_m1", 1, 256, 256, seed=60, act="f32"),
+    synth.LinearSpec("lin_k_m1", 1, 3584, 512, seed=61),
+    synth.LinearSpec("lin_o_m1", 1, 3584, 3584, seed=62),
+    synth.LinearSpec("lin_down_m1", 1, 18944, 3584, seed=63),
+    synth.LinearSpec("lin_wide_m1", 1, 384, 4608, seed=64),
+    synth.LinearSpec("lin_m4", 4, 1024, 512, seed=65),
+    synth.LinearSpec("lin_m40", 40, 512, 272, seed=66),
+]
+
+
+@pytest.mark.parametrize("spec", LINEAR_SPECS, ids=lambda s: s.name)
+def test_linear_matches_quant_then_gemm(w4, spec):
+    """w4a8_linear (one launch at M == 1: the GEMV quantises in-kernel) is
+    bitwise identical to w4a8_quant_act + w4a8_gemm, and within tolerance of
+    the oracle."""
+    say(f"linear {spec}")
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    x = x_tensor(lin)
+    y_fused = w4.linear(x, W)
+    qa, sa = w4.quant_act(x)
+    y_two = w4.gemm(qa, sa, W)
+    assert torch.equal(y_fused, y_two)
+    _check_y(y_fused, lin, qa_ref, sa_ref)
+    assert torch.equal(w4.linear(x, W), y_fused)
+
+
+def test_gemv_partials_wide(w4):
+    """GEMV partials where workgroup runs straddle channel blocks (N large
+    enough for the balanced split) and where K is split across workgroups."""
+    for spec in (synth.LinearSpec("gemv_wide", 1, 384, 4608, seed=70),
+                 synth.LinearSpec("gemv_ksplit", 1, 18944, 512, seed=71)):
+        say(f"gemv partials {spec}")
+        lin, W, qa_ref, sa_ref = _setup(w4, spec)
+        qa, sa = w4.quant_act(x_tensor(lin))
+        P, y = w4.gemm_debug(qa, sa, W, path=w4.PATH_GEMV)
+        P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"])
+        assert np.array_equal(P.cpu().numpy(), P_ref)
+        _check_y(y, lin, qa_ref, sa_ref)
