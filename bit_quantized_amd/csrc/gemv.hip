@@ -38,8 +38,9 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kQWaves = 4;                  // quantiser wavefronts
 constexpr int kSWaves = kWaves - kQWaves;   // streamer wavefronts
-constexpr int D = 4;                        // code blocks a streamer keeps in flight
 constexpr int kMaxRun = 16;                 // units per streamer wavefront
+constexpr int D = 4;                        // code blocks a streamer keeps in flight
+constexpr int kSmallK = 4096;               // rows a quantiser wavefront holds in registers
 constexpr int kMaxCb = 16;                  // channel blocks per workgroup
 
 enum { X_BF16 = 0, X_F32 = 1, X_QUANTISED = 2 };
@@ -209,7 +210,51 @@ __device__ __forceinline__ void load_next(const uint8_t* base, int64_t hot_off, 
   lcb += wrap;
 }
 
-template <int XT, bool DEBUG>
+// Quantiser wavefront qw, row held in registers (K <= kSmallK): lane chunk i
+// is chunk lane + 64 i of the row (8 activations or codes), i.e. group
+// 4i + lane/16.  The wavefront converts the chunks with i % 4 == qw, so each
+// group is handled by exactly one wavefront, and forms those groups'
+// per-quarter sums from what it has just written.
+template <int XT>
+__device__ __forceinline__ void quantise_held(const uint4* xr, int qw, int lane, int K, int G,
+                                              float scale, float amax, int8_t* qs, int* rs) {
+  const int nch = K / 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = lane + 64 * i;
+    if ((i & 3) == qw && ch < nch) {
+      uint2 pk;
+      if constexpr (XT == X_QUANTISED) {
+        pk = make_uint2(xr[i].x, xr[i].y);
+      } else {
+        const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
+          float r = 0.0f;
+          if (amax != 0.0f) r = fminf(fmaxf(rintf(v / scale), -127.0f), 127.0f);
+          w[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * (e & 3));
+        }
+        pk = make_uint2(w[0], w[1]);
+      }
+      *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int cq = lane & 15;
+  if (cq < 4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 4 * i + (lane >> 4);
+      if ((i & 3) == qw && g < G)
+        rs[4 * g + cq] = byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * cq)) +
+                         byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * cq));
+    }
+  }
+}
+
+template <int XT, bool SMALL, bool DEBUG>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -237,11 +282,44 @@ gemv_kernel(GemmArgs a) {
   const int u1 = sw >= 0 ? units * (sw + 1) / kSWaves : 0;
   const int nrun = u1 - u0;
 
-  // The quantisers' first activation loads go out before any code block, so
-  // they are not queued behind the weight stream in this compute unit's
-  // memory pipeline.
+  // The quantisers' activation loads go out before any code block: requests
+  // queued behind the weight stream wait microseconds.  With a short row
+  // (SMALL) the quantisers hold all of it, form the absmax, and only then let
+  // the streamers start (barrier 0); otherwise the first chunks are in
+  // flight before the stream begins.
   QPrefetch pf;
-  if (sw < 0) quantise_prefetch<XT>(a, wave, lane, K, pf);
+  float sscale = 0.0f, samax = 0.0f;
+  if (sw < 0) {
+    if constexpr (SMALL) {
+      const int nch = K / 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ch = min(lane + 64 * i, nch - 1);
+        if constexpr (XT == X_QUANTISED) {
+          const uint2 c2 = *reinterpret_cast<const uint2*>(a.qa + 8 * ch);
+          pf.v[i] = make_uint4(c2.x, c2.y, 0u, 0u);
+        } else {
+          pf.v[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + 8 * ch);
+        }
+      }
+      if constexpr (XT == X_QUANTISED) {
+        sscale = a.sa[0];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w4[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            samax = fmaxf(samax, fmaxf(fabsf(__uint_as_float(w4[k] << 16)),
+                                       fabsf(__uint_as_float(w4[k] & 0xFFFF0000u))));
+        }
+        samax = wave_max(samax);
+        sscale = samax / 127.0f;
+      }
+    } else {
+      quantise_prefetch<XT>(a, wave, lane, K, pf);
+    }
+  }
   for (int t = tid; t < kMaxCb * kSWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
   __syncthreads();
 
@@ -249,26 +327,31 @@ gemv_kernel(GemmArgs a) {
   int lcb = 0, lg = 0, lu = u0;  // next unit to load
   int64_t hot_off = 0;  // offset of this lane's 16 scale bytes (just fetched, cache-resident)
   if (sw >= 0) {
-    // run metadata first: scales (lane l: unit l/4, channels 4(l%4)..+3) and
-    // zero blocks (lane l < 16: unit l), clamped to the run's last unit
+    // run metadata: scales (lane l: unit l/4, channels 4(l%4)..+3) and zero
+    // blocks (lane l < 16: unit l), clamped to the run's last unit
     const int last = nrun > 0 ? nrun - 1 : 0;
     const int64_t bs = unit_block(u0 + min(lane >> 2, last), nb0, G, g0, gk);
     const int64_t bz = unit_block(u0 + min(lane & 15, last), nb0, G, g0, gk);
     const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
     hot_off = reinterpret_cast<const uint8_t*>(hot_s) - a.w.codes;  // same packed buffer
-    const uint4 s4 = *reinterpret_cast<const uint4*>(hot_s);
-    const uint2 z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
-    // then the first D code blocks of the run
+    // the first D code blocks of the run, then its metadata
     lcb = nrun > 0 ? u0 / gk : 0;
     lg = nrun > 0 ? u0 % gk : 0;
 #pragma unroll
     for (int i = 0; i < D; ++i)
       load_next(a.w.codes, hot_off, u1, nb0, G, g0, gk, lane, lu, lcb, lg, wv[i]);
-    *reinterpret_cast<uint4*>(&s_scale[sw][lane >> 2][4 * (lane & 3)]) = s4;
+    const uint4 s4 = *reinterpret_cast<const uint4*>(hot_s);
+    const uint2 z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait
+    if ((lane >> 2) < kMaxRun)
+      *reinterpret_cast<uint4*>(&s_scale[sw][lane >> 2][4 * (lane & 3)]) = s4;
     if (lane < kMaxRun) s_zero[sw][lane] = z2;
   } else {
-    float scale;
-    quantise_groups<XT>(a, wave, lane, K, G, pf, qs, rs, &scale);
+    float scale = sscale;
+    if constexpr (SMALL)
+      quantise_held<XT>(pf.v, wave, lane, K, G, sscale, samax, qs, rs);
+    else
+      quantise_groups<XT>(a, wave, lane, K, G, pf, qs, rs, &scale);
     if (wave == 0 && lane == 0) {
       s_sa = scale;
       if (a.sa_ws && blockIdx.x == 0 && blockIdx.y == 0) a.sa_ws[0] = scale;
@@ -321,8 +404,10 @@ gemv_kernel(GemmArgs a) {
           cg -= wrap * gk;
           ccb += wrap;
         }
-        // refill this slot with the unit D ahead
-        load_next(a.w.codes, hot_off, u1, nb0, G, g0, gk, lane, lu, lcb, lg, wv[i]);
+        // refill this slot with the unit D ahead (a ring only when runs can
+        // be longer than the ring)
+        if constexpr (D < kMaxRun)
+          load_next(a.w.codes, hot_off, u1, nb0, G, g0, gk, lane, lu, lcb, lg, wv[i]);
       }
     }
     accf += __shfl_xor(accf, 16);
@@ -348,16 +433,22 @@ gemv_kernel(GemmArgs a) {
   }
 }
 
-template <int XT>
-hipError_t launch_xt(const GemmArgs& a, hipStream_t st) {
+template <int XT, bool SMALL>
+hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (size_t)a.K + 16 * (size_t)G;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, true>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, SMALL, true>), grid, dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, false>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, SMALL, false>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int XT>
+hipError_t launch_xt(const GemmArgs& a, hipStream_t st) {
+  if (XT != X_F32 && a.K <= kSmallK) return launch_small<XT, XT != X_F32>(a, st);
+  return launch_small<XT, false>(a, st);
 }
 
 }  // namespace
