@@ -3,28 +3,33 @@
 //
 // "The 4-bit CPU path", section "W4A16": a kernel that touches every weight
 // once per call is "fine for decode" — its cost is the stream of packed
-// weights, and everything else must hide under that stream.  One 1024-thread
-// workgroup per compute unit (the grid is a whole number of rounds over the
-// compute units), with two roles:
-//   - 12 streamer wavefronts each own an equal contiguous run of the
-//     workgroup's (16-channel block, group) units, i.e. one contiguous run of
-//     the codes plane.  At entry each stages its run's scales and zero points
-//     in LDS with two wide loads and puts its first D code blocks in flight
-//     (1 KiB per wavefront per unit, nontemporal: every byte is read once);
-//   - 4 quantiser wavefronts meanwhile turn the token into int8 codes in LDS.
-//     Each reads the whole row to form the absmax itself (so they need no
-//     synchronisation among themselves), then quantises every fourth group
-//     (IEEE division, ties to even — the rule of w4a8_quant_act) and forms the
-//     per-quarter code sums of those groups.  Given pre-quantised codes they
-//     only copy them.
-// One workgroup barrier joins the two, then the streamers run a ring of D
-// register slots: consume a unit, refill its slot with the unit D ahead.
+// weights, and everything else must hide under that stream.  Each compute
+// unit draws a fixed share of HBM bandwidth through a short queue; a
+// wavefront that waits in that queue cannot take part in anything else, and a
+// workgroup barrier would make every wavefront wait for the slowest one.  So
+// one 1024-thread workgroup per compute unit (the grid is a whole number of
+// rounds over the compute units) splits into two roles that never meet at a
+// barrier before the last reduction:
+//   - kQ quantiser wavefronts load the token first (their requests lead the
+//     queue), take its absmax, quantise it into LDS (IEEE division, ties to
+//     even — the rule of w4a8_quant_act) with per-quarter code sums added by
+//     integer LDS atomics (exact, so order-free), and raise an LDS flag; they
+//     synchronise among themselves through LDS counters;
+//   - the other wavefronts put D code blocks of their runs in flight at once,
+//     wait for the flag (a bounded spin: the quantisers set it
+//     unconditionally), and stream.
+// The workgroup's (16-channel block, group) units are dealt out as contiguous
+// runs of the codes plane (1 KiB per wavefront per unit, nontemporal loads:
+// every byte is read once), the quantisers taking a smaller share since they
+// start late.  Each wavefront stages its run's scales and zero points in LDS
+// with two wide loads and streams the run through a ring of D register slots:
+// consume a unit, refill its slot with the unit D ahead.
 // Lane l = 16j + c owns channel c and input channels
 // {16j..16j+15} u {64+16j..64+16j+15} of each group: the raw codes q (0..15,
 // valid signed int8) go straight into eight v_dot4_i32_i8 and the zero point
 // is applied once per group as  sum qa*q - z * sum qa.  The float rescale
-// s[n][g] * P is linear, so each lane rescales its quarter; quarters are summed
-// with cross-lane shuffles and the pieces of a channel block (several
+// s[n][g] * P is linear, so each lane rescales its quarter; quarters are
+// summed with cross-lane shuffles and the pieces of a channel block (several
 // wavefronts may share one) in fixed wavefront order through LDS, so the
 // result never depends on timing.
 #include <atomic>
@@ -36,39 +41,27 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kQWaves = 4;                  // quantiser wavefronts
-constexpr int kSWaves = kWaves - kQWaves;   // streamer wavefronts
-constexpr int kMaxRun = 16;                 // units per streamer wavefront
-constexpr int D = 4;                        // code blocks a streamer keeps in flight
-constexpr int kSmallK = 4096;               // rows a quantiser wavefront holds in registers
-constexpr int kMaxCb = 16;                  // channel blocks per workgroup
+constexpr int kQ = 4;                       // quantiser wavefronts
+constexpr int kQWeight = 2;                 // run share of a quantiser (a streamer's is 4)
+constexpr int kShareTotal = kQ * kQWeight + (kWaves - kQ) * 4;
+constexpr int D = 4;                        // code blocks a wavefront keeps in flight
+constexpr int kMaxRun = 12;                 // units per wavefront
+constexpr int kMaxCb = 12;                  // channel blocks per workgroup
+constexpr int kQChunks = 4;                 // token chunks a quantiser thread holds at once
 
 enum { X_BF16 = 0, X_F32 = 1, X_QUANTISED = 2 };
 
+// Start of wavefront w's run in share units.
+__host__ __device__ constexpr int share_prefix(int w) {
+  return w <= kQ ? w * kQWeight : kQ * kQWeight + (w - kQ) * 4;
+}
+
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int kBufferWord3 = 0x00020000;    // raw byte buffer, gfx9 descriptor format
+constexpr int kNontemporal = 2;             // cache policy bit: nt
 __device__ __forceinline__ uint4 ntload16(const uint8_t* p) {
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-// Eight activations (chunk ch) widened to float.
-template <int XT>
-__device__ __forceinline__ void load8(const void* x, int ch, float* v) {
-  if constexpr (XT == X_BF16) {
-    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + 8 * ch);
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = __uint_as_float(w[k] << 16);
-      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-  } else {
-    const float* p = static_cast<const float*>(x) + 8 * ch;
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -77,191 +70,80 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Sum of the 16 signed bytes in a uint4.
-__device__ __forceinline__ int byte_sum16(uint4 v) {
-  int s = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false);
-  s = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, s, false);
-  s = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, s, false);
-  return __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
+// Sum of the 8 signed bytes in a uint2.
+__device__ __forceinline__ int byte_sum8(uint2 v) {
+  return __builtin_amdgcn_sdot4((int)v.y, 0x01010101,
+                                __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false), false);
 }
 
 // Codes-plane block index of unit u of a workgroup's run.
+// floor(total * i / parts) in 32-bit arithmetic (parts <= 65536, checked on
+// the host): total = q parts + r, so total i / parts = q i + r i / parts.
+__device__ __forceinline__ int split_point(unsigned total, unsigned parts, unsigned i) {
+  const unsigned q = total / parts, r = total % parts;
+  return (int)(q * i + (r * i) / parts);
+}
+
 __device__ __forceinline__ int64_t unit_block(int u, int nb0, int G, int g0, int gk) {
   return (int64_t)(nb0 + u / gk) * G + g0 + u % gk;
 }
 
-// Step the load position (unit lu at block lcb, group lg of the slice).
-__device__ __forceinline__ void advance(int& lu, int& lcb, int& lg, int gk) {
-  ++lu;
-  ++lg;
-  const int wrap = (lg == gk) ? 1 : 0;  // a select, not a branch
-  lg -= wrap * gk;
-  lcb += wrap;
-}
-
-// The first loads of a quantiser wavefront, issued before the streamers put
-// their code blocks in flight: the first 8 activation chunks of this lane
-// (bf16: chunk lane + 64 i) or, for pre-quantised codes, the codes of its
-// first group.
-struct QPrefetch {
-  uint4 v[8];
-};
-
-template <int XT>
-__device__ __forceinline__ void quantise_prefetch(const GemmArgs& a, int qw, int lane, int K,
-                                                  QPrefetch& pf) {
-  if constexpr (XT == X_BF16) {
-    const int nch = K / 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pf.v[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                8 * min(64 * i + lane, nch - 1));
-  } else if constexpr (XT == X_QUANTISED) {
-    const int g = min(qw + 4 * (lane >> 4), K / kGroup - 1);
-    const uint2 c2 = *reinterpret_cast<const uint2*>(a.qa + 8 * (g * 16 + (lane & 15)));
-    pf.v[0] = make_uint4(c2.x, c2.y, 0u, 0u);
-  }
-}
-
-// Quantiser wavefront qw: the token's codes for groups qw, qw+4, ... into qs,
-// with their per-quarter sums into rs.
-template <int XT>
-__device__ __forceinline__ void quantise_groups(const GemmArgs& a, int qw, int lane, int K, int G,
-                                                const QPrefetch& pf, int8_t* qs, int* rs,
-                                                float* scale_out) {
-  float scale;
-  float amax = 0.0f;
-  if constexpr (XT == X_QUANTISED) {
-    scale = a.sa[0];
-  } else {
-    // absmax over the whole row, eight chunks per lane in flight at a time
-    const int nch = K / 8;
-    for (int base = 0; base < nch; base += 64 * 8) {
-      float v[8][8];
-      if (XT == X_BF16 && base == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[i][2 * k] = __uint_as_float(w[k] << 16);
-            v[i][2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) load8<XT>(a.x, min(base + 64 * i + lane, nch - 1), v[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
-    }
-    amax = wave_max(amax);
-    scale = amax / 127.0f;
-  }
-  *scale_out = scale;
-  // 16 lanes per group, one 8-element chunk per lane; 4 groups per pass
-  const int t = lane >> 4, cq = lane & 15;
-  for (int g = qw + 4 * t; g < G; g += 16) {
-    const int ch = g * 16 + cq;
-    uint2 pk;
-    if constexpr (XT == X_QUANTISED) {
-      pk = (g == qw + 4 * t) ? make_uint2(pf.v[0].x, pf.v[0].y)
-                             : *reinterpret_cast<const uint2*>(a.qa + 8 * ch);
-    } else {
-      float v[8];
-      load8<XT>(a.x, ch, v);
-      uint32_t w[2] = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float r = 0.0f;
-        if (amax != 0.0f) r = fminf(fmaxf(rintf(v[e] / scale), -127.0f), 127.0f);
-        w[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * (e & 3));
-      }
-      pk = make_uint2(w[0], w[1]);
-    }
-    *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
-  }
-  // the same wavefront reads back what it wrote: order it at wavefront scope
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (cq < 4) {
-    for (int g = qw + 4 * t; g < G; g += 16) {
-      rs[4 * g + cq] = byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * cq)) +
-                       byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * cq));
-    }
-  }
-}
-
-// Load the next unit of the run into a ring slot.  Past the end of the run the
-// load still issues (so every wavefront has the same, compile-time count of
-// loads in flight and waits stay exact) but reads the lane's own scale bytes,
-// fetched moments ago; its value is never used.  Branch-free on purpose.
-__device__ __forceinline__ void load_next(const uint8_t* base, int64_t hot_off, int u1, int nb0,
-                                          int G, int g0, int gk, int lane, int& lu, int& lcb,
-                                          int& lg, uint4& w) {
+// Load the next unit of the run into a ring slot.  The wavefront reads its
+// run through a buffer descriptor that spans exactly the run's blocks; past
+// the end of the run the load still issues (so every wavefront has the same,
+// compile-time count of loads in flight and waits stay exact) but with an
+// offset beyond the descriptor's range, which the hardware answers with zeros
+// and no memory request.  Branch-free on purpose.
+__device__ __forceinline__ void load_next(__amdgpu_buffer_rsrc_t rsrc, int oob, int u1, int G,
+                                          int gk, int lane, int& lu, int& lg, int& rel,
+                                          uint4& w) {
   const int live = lu < u1 ? 1 : 0;  // wave-uniform
-  const int64_t code_off = unit_block(0, nb0 + lcb, G, g0 + lg, gk) * kBlockBytes + 16 * lane;
-  w = ntload16(base + (live ? code_off : hot_off));
+  const int off = live ? rel * kBlockBytes + 16 * lane : oob;
+  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNontemporal);
+  w = make_uint4(t.x, t.y, t.z, t.w);
   lu += live;
   lg += live;
   const int wrap = (lg == gk) ? 1 : 0;
   lg -= wrap * gk;
-  lcb += wrap;
+  rel += live + wrap * (G - gk);  // next group, or the next block's first group
 }
 
-// Quantiser wavefront qw, row held in registers (K <= kSmallK): lane chunk i
-// is chunk lane + 64 i of the row (8 activations or codes), i.e. group
-// 4i + lane/16.  The wavefront converts the chunks with i % 4 == qw, so each
-// group is handled by exactly one wavefront, and forms those groups'
-// per-quarter sums from what it has just written.
+// One 8-element chunk of the token (chunk ch), raw: bf16 -> one uint4, f32 ->
+// two, pre-quantised codes -> one uint2 (in .x, .y).
 template <int XT>
-__device__ __forceinline__ void quantise_held(const uint4* xr, int qw, int lane, int K, int G,
-                                              float scale, float amax, int8_t* qs, int* rs) {
-  const int nch = K / 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ch = lane + 64 * i;
-    if ((i & 3) == qw && ch < nch) {
-      uint2 pk;
-      if constexpr (XT == X_QUANTISED) {
-        pk = make_uint2(xr[i].x, xr[i].y);
-      } else {
-        const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = __uint_as_float((e & 1) ? (w4[e >> 1] & 0xFFFF0000u) : (w4[e >> 1] << 16));
-          float r = 0.0f;
-          if (amax != 0.0f) r = fminf(fmaxf(rintf(v / scale), -127.0f), 127.0f);
-          w[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * (e & 3));
-        }
-        pk = make_uint2(w[0], w[1]);
-      }
-      *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  const int cq = lane & 15;
-  if (cq < 4) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int g = 4 * i + (lane >> 4);
-      if ((i & 3) == qw && g < G)
-        rs[4 * g + cq] = byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * cq)) +
-                         byte_sum16(*reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * cq));
-    }
+__device__ __forceinline__ void load_chunk(const GemmArgs& a, int ch, uint4* r) {
+  if constexpr (XT == X_BF16) {
+    r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + 8 * ch);
+  } else if constexpr (XT == X_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + 8 * ch);
+    r[0] = p[0];
+    r[1] = p[1];
+  } else {
+    const uint2 c2 = *reinterpret_cast<const uint2*>(a.qa + 8 * ch);
+    r[0] = make_uint4(c2.x, c2.y, 0u, 0u);
   }
 }
 
-template <int XT, bool SMALL, bool DEBUG>
+template <int XT>
+__device__ __forceinline__ float chunk_value(const uint4* r, int e) {
+  if constexpr (XT == X_BF16) {
+    const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+  } else {
+    const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+    return __uint_as_float(w[e]);
+  }
+}
+
+template <int XT, bool DEBUG>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ __attribute__((aligned(16))) float s_scale[kSWaves][kMaxRun][16];
-  __shared__ __attribute__((aligned(16))) uint2 s_zero[kSWaves][kMaxRun];
-  __shared__ float part[kMaxCb][kSWaves][16];
-  __shared__ float s_sa;
+  __shared__ __attribute__((aligned(16))) float s_scale[kWaves][kMaxRun][16];
+  __shared__ __attribute__((aligned(16))) uint2 s_zero[kWaves][kMaxRun];
+  __shared__ float part[kMaxCb][kWaves][16];
+  // [0] token absmax bits, [1] quantisers past the absmax, [2] quantisers done
+  __shared__ unsigned s_sync[4];
   const int K = (int)a.K, G = K / kGroup, NB = (int)(a.N / kBlockCols);
   int8_t* qs = reinterpret_cast<int8_t*>(smem);               // [K] activation codes
   int* rs = reinterpret_cast<int*>(smem + K);                  // [4G] per-quarter code sums
@@ -269,97 +151,147 @@ gemv_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int c = lane & 15, j = lane >> 4;
-  // This workgroup: channel blocks [nb0, nb1) x groups [g0, g1), dealt to
-  // the streamers as equal contiguous runs of (block, group) units in
-  // block-major order (the order of the codes plane).
-  const int nb0 = (int)((int64_t)NB * blockIdx.x / gridDim.x);
-  const int nb1 = (int)((int64_t)NB * (blockIdx.x + 1) / gridDim.x);
-  const int g0 = (int)((int64_t)G * blockIdx.y / gridDim.y);
-  const int g1 = (int)((int64_t)G * (blockIdx.y + 1) / gridDim.y);
+  // This workgroup: channel blocks [nb0, nb1) x groups [g0, g1).
+  const int nb0 = split_point(NB, gridDim.x, blockIdx.x);
+  const int nb1 = split_point(NB, gridDim.x, blockIdx.x + 1);
+  const int g0 = split_point(G, gridDim.y, blockIdx.y);
+  const int g1 = split_point(G, gridDim.y, blockIdx.y + 1);
   const int gk = g1 - g0, units = (nb1 - nb0) * gk;
-  const int sw = wave - kQWaves;                                // streamer index
-  const int u0 = sw >= 0 ? units * sw / kSWaves : 0;
-  const int u1 = sw >= 0 ? units * (sw + 1) / kSWaves : 0;
+  const int u0 = units * share_prefix(wave) / kShareTotal;
+  const int u1 = units * share_prefix(wave + 1) / kShareTotal;
   const int nrun = u1 - u0;
 
-  // The quantisers' activation loads go out before any code block: requests
-  // queued behind the weight stream wait microseconds.  With a short row
-  // (SMALL) the quantisers hold all of it, form the absmax, and only then let
-  // the streamers start (barrier 0); otherwise the first chunks are in
-  // flight before the stream begins.
-  QPrefetch pf;
-  float sscale = 0.0f, samax = 0.0f;
-  if (sw < 0) {
-    if constexpr (SMALL) {
-      const int nch = K / 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = min(lane + 64 * i, nch - 1);
-        if constexpr (XT == X_QUANTISED) {
-          const uint2 c2 = *reinterpret_cast<const uint2*>(a.qa + 8 * ch);
-          pf.v[i] = make_uint4(c2.x, c2.y, 0u, 0u);
-        } else {
-          pf.v[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + 8 * ch);
-        }
-      }
-      if constexpr (XT == X_QUANTISED) {
-        sscale = a.sa[0];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w4[4] = {pf.v[i].x, pf.v[i].y, pf.v[i].z, pf.v[i].w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            samax = fmaxf(samax, fmaxf(fabsf(__uint_as_float(w4[k] << 16)),
-                                       fabsf(__uint_as_float(w4[k] & 0xFFFF0000u))));
-        }
-        samax = wave_max(samax);
-        sscale = samax / 127.0f;
-      }
-    } else {
-      quantise_prefetch<XT>(a, wave, lane, K, pf);
-    }
-  }
-  for (int t = tid; t < kMaxCb * kSWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
+  for (int t = tid; t < kMaxCb * kWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
+  for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
+  if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
 
+  // the run's metadata: scales (lane l: unit l/4, channels 4(l%4)..+3) and
+  // zero blocks (lane l: unit l), clamped to the run's last unit
+  const int last = nrun > 0 ? nrun - 1 : 0;
+  const int64_t bs = unit_block(u0 + min(lane >> 2, last), nb0, G, g0, gk);
+  const int64_t bz = unit_block(u0 + min(lane & 15, last), nb0, G, g0, gk);
+  const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
+  // the run's blocks: [first, first + span) of the codes plane
+  const int64_t first = unit_block(u0, nb0, G, g0, gk);
+  const int span = nrun > 0 ? (int)(unit_block(u1 - 1, nb0, G, g0, gk) - first + 1) : 0;
+  const int oob = span * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w.codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
+      kBufferWord3);
   uint4 wv[D];
-  int lcb = 0, lg = 0, lu = u0;  // next unit to load
-  int64_t hot_off = 0;  // offset of this lane's 16 scale bytes (just fetched, cache-resident)
-  if (sw >= 0) {
-    // run metadata: scales (lane l: unit l/4, channels 4(l%4)..+3) and zero
-    // blocks (lane l < 16: unit l), clamped to the run's last unit
-    const int last = nrun > 0 ? nrun - 1 : 0;
-    const int64_t bs = unit_block(u0 + min(lane >> 2, last), nb0, G, g0, gk);
-    const int64_t bz = unit_block(u0 + min(lane & 15, last), nb0, G, g0, gk);
-    const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
-    hot_off = reinterpret_cast<const uint8_t*>(hot_s) - a.w.codes;  // same packed buffer
-    // the first D code blocks of the run, then its metadata
-    lcb = nrun > 0 ? u0 / gk : 0;
-    lg = nrun > 0 ? u0 % gk : 0;
+  int lu = u0, lg = nrun > 0 ? u0 % gk : 0, rel = 0;  // next unit to load
+  uint4 s4;
+  uint2 z2;
+  float scale;
+
+  if (wave < kQ) {
+    // ---- quantiser: token chunks (8 elements) qt, qt + 256, ... in batches
+    // of kQChunks; the last batch stays in registers for the second pass
+    const int qt = tid;                                         // 0 .. 64 kQ - 1
+    constexpr int kQThreads = 64 * kQ;
+    const int nch = K / 8;
+    const int nbatch = (nch + kQChunks * kQThreads - 1) / (kQChunks * kQThreads);
+    constexpr int RW = XT == X_F32 ? 2 : 1;
+    uint4 xr[kQChunks][RW];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(a, min(i * kQThreads + qt, nch - 1), xr[i]);
+    s4 = *reinterpret_cast<const uint4*>(hot_s);
+    z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
+    for (int b = 0; b < nbatch; ++b) {
+      if (b > 0) {
+#pragma unroll
+        for (int i = 0; i < kQChunks; ++i)
+          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
+      }
+      if constexpr (XT != X_QUANTISED) {
+#pragma unroll
+        for (int i = 0; i < kQChunks; ++i)
+          if ((b * kQChunks + i) * kQThreads + qt < nch)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(chunk_value<XT>(xr[i], e)));
+      }
+    }
+    if constexpr (XT == X_QUANTISED) {
+      scale = a.sa[0];
+    } else {
+      // row absmax: every quantiser publishes its wavefront max (non-negative
+      // floats order as their bit patterns), then waits for the others
+      amax = wave_max(amax);
+      if (lane == 0) {
+        __hip_atomic_fetch_max(&s_sync[0], __float_as_uint(amax), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&s_sync[1], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      while (__hip_atomic_load(&s_sync[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+             (unsigned)kQ)
+        __builtin_amdgcn_s_sleep(1);
+      scale = __uint_as_float(
+          __hip_atomic_load(&s_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) / 127.0f;
+    }
+    for (int b = nbatch - 1; b >= 0; --b) {
+      if (b != nbatch - 1) {
+#pragma unroll
+        for (int i = 0; i < kQChunks; ++i)
+          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kQChunks; ++i) {
+        const int ch = (b * kQChunks + i) * kQThreads + qt;
+        if (ch < nch) {
+          uint2 pk;
+          if constexpr (XT == X_QUANTISED) {
+            pk = make_uint2(xr[i][0].x, xr[i][0].y);
+          } else {
+            // an all-zero token has scale 0 and all-zero codes (no division)
+            const bool live = scale != 0.0f;
+            const float den = live ? scale : 1.0f;
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float r = fminf(fmaxf(rintf(chunk_value<XT>(xr[i], e) / den), -127.0f), 127.0f);
+              r = live ? r : 0.0f;
+              w[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * (e & 3));
+            }
+            pk = make_uint2(w[0], w[1]);
+          }
+          *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
+          // chunk ch covers elements 8(ch%16)..+7 of group ch/16: quarter
+          // ((ch % 16) % 8) / 2 of the lane layout (0..63 and 64..127 fold)
+          atomicAdd(&rs[4 * (ch >> 4) + ((ch & 7) >> 1)], byte_sum8(pk));
+        }
+      }
+    }
+    if (a.sa_ws && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.sa_ws[0] = scale;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
+    if (lane == 0)
+      __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // then the quantiser streams its own (shorter) run
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      load_next(a.w.codes, hot_off, u1, nb0, G, g0, gk, lane, lu, lcb, lg, wv[i]);
-    const uint4 s4 = *reinterpret_cast<const uint4*>(hot_s);
-    const uint2 z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
-    __builtin_amdgcn_sched_barrier(0);  // every load above issues before any wait
-    if ((lane >> 2) < kMaxRun)
-      *reinterpret_cast<uint4*>(&s_scale[sw][lane >> 2][4 * (lane & 3)]) = s4;
-    if (lane < kMaxRun) s_zero[sw][lane] = z2;
+      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   } else {
-    float scale = sscale;
-    if constexpr (SMALL)
-      quantise_held<XT>(pf.v, wave, lane, K, G, sscale, samax, qs, rs);
-    else
-      quantise_groups<XT>(a, wave, lane, K, G, pf, qs, rs, &scale);
-    if (wave == 0 && lane == 0) {
-      s_sa = scale;
-      if (a.sa_ws && blockIdx.x == 0 && blockIdx.y == 0) a.sa_ws[0] = scale;
-    }
+    // ---- streamer: metadata and D code blocks in flight, then the flag
+    s4 = *reinterpret_cast<const uint4*>(hot_s);
+    z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    __builtin_amdgcn_sched_barrier(0);  // every load above issues before the wait
+    if constexpr (XT == X_QUANTISED) scale = a.sa[0];
+    while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+           (unsigned)kQ)
+      __builtin_amdgcn_s_sleep(1);
+    if constexpr (XT != X_QUANTISED)
+      scale = __uint_as_float(
+          __hip_atomic_load(&s_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) / 127.0f;
   }
-  __syncthreads();
+  if ((lane >> 2) < kMaxRun) *reinterpret_cast<uint4*>(&s_scale[wave][lane >> 2][4 * (lane & 3)]) = s4;
+  if (lane < kMaxRun) s_zero[wave][lane] = z2;
 
-  if (sw >= 0) {
+  // the run, through the ring
+  {
     float accf = 0.0f;
     int ccb = nrun > 0 ? u0 / gk : 0, cg = nrun > 0 ? u0 % gk : 0;  // compute position
     int cur = ccb;
@@ -372,7 +304,7 @@ gemv_kernel(GemmArgs a) {
           if (ccb != cur) {
             accf += __shfl_xor(accf, 16);
             accf += __shfl_xor(accf, 32);
-            if (j == 0) part[cur][sw][c] = accf;
+            if (j == 0) part[cur][wave][c] = accf;
             accf = 0.0f;
             cur = ccb;
           }
@@ -389,7 +321,7 @@ gemv_kernel(GemmArgs a) {
             acc = __builtin_amdgcn_sdot4((int)((d[w] >> 4) & 0x0F0F0F0Fu), (int)h4[w], acc,
                                          false);
           }
-          const uint32_t zbyte = reinterpret_cast<const uint8_t*>(&s_zero[sw][r])[c >> 1];
+          const uint32_t zbyte = reinterpret_cast<const uint8_t*>(&s_zero[wave][r])[c >> 1];
           const int z = (int)((zbyte >> zshift) & 0xFu);
           const int p = acc - z * rs[4 * g + j];
           if (DEBUG) {
@@ -398,32 +330,29 @@ gemv_kernel(GemmArgs a) {
             if (j == 0 && a.partials && a.m_begin == 0 && a.m_end > 0)
               a.partials[((int64_t)16 * (nb0 + ccb) + c) * G + g] = pg;
           }
-          accf += s_scale[sw][r][c] * (float)p;
+          accf += s_scale[wave][r][c] * (float)p;
           ++cg;
           const int wrap = (cg == gk) ? 1 : 0;
           cg -= wrap * gk;
           ccb += wrap;
         }
-        // refill this slot with the unit D ahead (a ring only when runs can
-        // be longer than the ring)
-        if constexpr (D < kMaxRun)
-          load_next(a.w.codes, hot_off, u1, nb0, G, g0, gk, lane, lu, lcb, lg, wv[i]);
+        // refill this slot with the unit D ahead
+        load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
       }
     }
     accf += __shfl_xor(accf, 16);
     accf += __shfl_xor(accf, 32);
-    if (nrun > 0 && j == 0) part[cur][sw][c] = accf;
+    if (nrun > 0 && j == 0) part[cur][wave][c] = accf;
   }
   __syncthreads();
 
-  // each channel block: its streamer pieces in streamer order
+  // each channel block: its wavefront pieces in wavefront order
   const int ncb = nb1 - nb0;
-  const float scale = s_sa;
   for (int t = tid; t < ncb * 16; t += kThreads) {
     const int cbl = t >> 4, cc = t & 15;
     float total = part[cbl][0][cc];
 #pragma unroll
-    for (int w = 1; w < kSWaves; ++w) total += part[cbl][w][cc];
+    for (int w = 1; w < kWaves; ++w) total += part[cbl][w][cc];
     const int64_t n = (int64_t)16 * (nb0 + cbl) + cc;
     if (gridDim.y == 1) {
       if (a.y) a.y[n] = f32_to_bf16_rne(scale * total);
@@ -433,22 +362,16 @@ gemv_kernel(GemmArgs a) {
   }
 }
 
-template <int XT, bool SMALL>
-hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
+template <int XT>
+hipError_t launch_xt(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (size_t)a.K + 16 * (size_t)G;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, SMALL, true>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, true>), grid, dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, SMALL, false>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, false>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
-}
-
-template <int XT>
-hipError_t launch_xt(const GemmArgs& a, hipStream_t st) {
-  if (XT != X_F32 && a.K <= kSmallK) return launch_small<XT, XT != X_F32>(a, st);
-  return launch_small<XT, false>(a, st);
 }
 
 }  // namespace
@@ -482,7 +405,8 @@ int device_cus() {
 GemvShape gemv_shape(int64_t N, int64_t K) {
   const int64_t NB = N / kBlockCols, G = K / kGroup;
   const int64_t cus = device_cus();
-  const int64_t max_units = (int64_t)kSWaves * kMaxRun;
+  // a streamer's run is at most ceil(units * 4 / kShareTotal) units
+  const int64_t max_units = (int64_t)kMaxRun * kShareTotal / 4;
   GemvShape s{1, kWaves, 1};
   while ((G + s.ksplit - 1) / s.ksplit > max_units) s.ksplit *= 2;
   const int64_t gk = (G + s.ksplit - 1) / s.ksplit;
@@ -505,10 +429,10 @@ GemvShape gemv_shape(int64_t N, int64_t K) {
 // workgroup and <= kMaxRun units per streamer wavefront.
 bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s) {
   const int64_t NB = N / kBlockCols, G = K / kGroup;
-  if (s.cb < 1 || s.ksplit < 1 || s.ksplit > G) return false;
+  if (s.cb < 1 || s.cb > 65536 || s.ksplit < 1 || s.ksplit > G || s.ksplit > 65536) return false;
   const int64_t ncb = (NB + s.cb - 1) / s.cb;
   const int64_t gk_max = (G + s.ksplit - 1) / s.ksplit;
-  const int64_t run = (ncb * gk_max + kSWaves - 1) / kSWaves;
+  const int64_t run = (ncb * gk_max * 4 + kShareTotal - 1) / kShareTotal;
   return ncb <= kMaxCb && run <= kMaxRun;
 }
 
