@@ -51,6 +51,22 @@ def parse():
     return p.parse_args()
 
 
+def measured_traffic(profile):
+    """HBM bytes per launch from a committed counter summary under profiles/,
+    or None once the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line and not line.startswith("#"))
+        src = open(os.path.join(ROOT, kv["kernel_source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != kv.get("kernel_source_sha256"):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def algorithmic_bytes(M, N, K, group=128, act_bytes=2):
     """Bytes the method must move for one linear: packed int4 codes, 4-bit
     zeros, fp32 scales, activations in and bf16 output out."""
@@ -172,7 +188,8 @@ def bench_decode(torch, w4, args):
         "spec": spec, "lin": lin, "value": value, "ms_per_step": ms_per_step,
         "step_bytes": step_bytes, "parity": parity, "path": path,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("w4a8_gemv_decode_up_M1_K3584_N18944_traffic.txt"),
                      "kernel": f"w4a8 fused quant + {path} (M={M}, K={K}, N={N})",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(kern_ms * 1e3, 3),
@@ -213,7 +230,8 @@ def bench_prefill(torch, w4, args):
         "value": round(tops_step, 1), "unit": "TOPS", "ms_per_step": total_ms / n,
         "roofline": {"bound": "mfma", "achieved": round(tops_kernel, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": f"w4a8 prefill (M={M}, K={K}, N={N})",
+                     "traffic": measured_traffic("w4a8_prefill_up_M2048_K3584_N18944_traffic.txt"),
+                     "kernel": f"w4a8 prefill (M={M}, K={K}, N={N})",
                      "ops_per_launch": ops, "avg_launch_us": round(kern_ms * 1e3, 2),
                      "timing": f"{n} launches replayed from one HIP graph"},
     }

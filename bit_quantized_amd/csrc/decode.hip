@@ -2,8 +2,8 @@
 // split-K reduction it (and the M == 1 GEMV) use when N alone cannot fill the
 // chip.
 //
-// "The 4-bit CPU path", section "W4A16": a kernel whose cost is dominated by
-// touching each weight once per call is "fine for decode"; these kernels
+// "The 4-bit CPU path", section "W4A16": at decode a kernel whose cost is
+// reading each weight once per call is good enough; these kernels
 // stream every packed weight byte exactly once with 1 KiB-per-wavefront
 // coalesced loads and unpack the nibbles in registers.
 #include "w4a8_internal.h"

@@ -1,9 +1,9 @@
 // M == 1 decode GEMV, optionally with the per-token activation quantisation
 // fused into it.
 //
-// "The 4-bit CPU path", section "W4A16": a kernel that touches every weight
-// once per call is "fine for decode" — its cost is the stream of packed
-// weights, and everything else must hide under that stream.  Each compute
+// "The 4-bit CPU path", section "W4A16": at decode a kernel that reads each
+// weight once per call is good enough, because the call costs what streaming
+// the packed weights costs; everything else must hide under that stream.  Each compute
 // unit draws a fixed share of HBM bandwidth through a short queue; a
 // wavefront that waits in that queue cannot take part in anything else, and a
 // workgroup barrier would make every wavefront wait for the slowest one.  So

@@ -1,10 +1,10 @@
 // Prefill GEMM (M > 16) on the int8 matrix cores.
 //
-// "The 4-bit CPU path", section "W4A16": a per-row dequantising kernel is
-// "ruinous for prefill", so large batches take a separate GEMM path; here
-// that path keeps the weights as 4-bit codes in LDS, unpacks them in
-// registers to q - z bytes and runs v_mfma_i32_16x16x64_i8 per group, so the
-// weights are never expanded in HBM.
+// "The 4-bit CPU path", section "W4A16": dequantising per row is far too
+// slow once many tokens share the weights, so large batches take a separate
+// GEMM path.  Here that path keeps the weights as 4-bit codes in LDS, unpacks
+// them in registers to q - z bytes and runs v_mfma_i32_16x16x64_i8 per group,
+// so the weights are never expanded in HBM.
 //
 // Tile: 128 tokens x 128 output channels per 256-thread workgroup, four
 // wavefronts of 64 x 64.  Per group of 128 input channels the workgroup
