@@ -6,39 +6,42 @@
 // them in registers to q - z bytes and runs v_mfma_i32_16x16x64_i8 per group,
 // so the weights are never expanded in HBM.
 //
-// Tile: 128 tokens x 128 output channels per 256-thread workgroup, four
+// Tile: 256 tokens x 128 output channels per 512-thread workgroup, eight
 // wavefronts of 64 x 64.  Per group of 128 input channels the workgroup
-// stages the activation tile (128 x 128 int8) and eight packed code blocks
-// (8 KiB) in LDS, double-buffered, with the next group's global loads in
-// flight while the current group computes.
+// stages the activation tile (256 x 128 int8), the eight code blocks of the
+// tile unpacked once to q - z bytes, and their scales in LDS, double-buffered,
+// with the next group's global loads in flight while the current group
+// computes.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;                 // tokens per tile
+constexpr int kThreads = 512;           // 8 wavefronts, 2 per SIMD
+constexpr int BM = 256;                 // tokens per tile
 constexpr int BN = 128;                 // output channels per tile
-constexpr int NCB = BN / kBlockCols;    // packed blocks per tile
+constexpr int NCB = BN / kBlockCols;    // packed blocks per tile (8)
 constexpr int kAStride = kGroup + 16;   // LDS row pitch of the activation tile (bank spread)
 constexpr int kAOff = 0;
-constexpr int kBOff = kAOff + BM * kAStride;
-constexpr int kSOff = kBOff + NCB * kBlockBytes;
-constexpr int kZOff = kSOff + NCB * 16 * 4;
-constexpr int kBufBytes = kZOff + NCB * kZeroBlockBytes;
+constexpr int kBOff = kAOff + BM * kAStride;          // unpacked q - z, [NCB][2][64 lanes][16 B]
+constexpr int kSOff = kBOff + NCB * 2 * kBlockBytes;  // scales [NCB][16]
+constexpr int kBufBytes = kSOff + NCB * 16 * 4;
+constexpr int kAChunks = BM * kGroup / 16 / kThreads;  // 16-B activation chunks per thread (4)
 
+// One group's operands as they come from HBM, held in registers while the
+// previous group computes.
 struct Stage {
-  uint4 a[4];
-  uint4 b[2];
-  float s;
-  uint2 z;
+  uint4 a[kAChunks];
+  uint4 b;      // this thread's 16 packed bytes: block t/64, lane t%64
+  uint32_t z;   // that lane's zero point
+  float s;      // threads < 128: scale of channel t%16 of block t/16
 };
 
 __device__ __forceinline__ void load_stage(const GemmArgs& a, int64_t m0, int64_t cb0, int64_t NB,
                                            int64_t G, int64_t g, Stage& st) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
     const int64_t m = m0 + (ch >> 3);
     if (m < a.M)
@@ -46,48 +49,52 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, int64_t m0, int64_
     else
       st.a[i] = make_uint4(0, 0, 0, 0);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = tid + kThreads * i;
-    const int64_t nb = cb0 + (ch >> 6);
-    if (nb < NB)
-      st.b[i] = *reinterpret_cast<const uint4*>(a.w.codes + (nb * G + g) * kBlockBytes +
-                                                (ch & 63) * 16);
-    else
-      st.b[i] = make_uint4(0, 0, 0, 0);
+  const int64_t nb = cb0 + (tid >> 6);
+  if (nb < NB) {
+    st.b = *reinterpret_cast<const uint4*>(a.w.codes + (nb * G + g) * kBlockBytes + (tid & 63) * 16);
+    st.z = zero_of(a.w.zeros + (nb * G + g) * kZeroBlockBytes, tid & 15);
+  } else {
+    st.b = make_uint4(0, 0, 0, 0);
+    st.z = 0;
   }
   if (tid < NCB * 16) {
-    const int64_t nb = cb0 + (tid >> 4);
-    st.s = nb < NB ? a.w.scales[(nb * G + g) * 16 + (tid & 15)] : 0.0f;
-  } else if (tid < NCB * 16 + NCB) {
-    const int64_t nb = cb0 + (tid - NCB * 16);
-    st.z = nb < NB ? *reinterpret_cast<const uint2*>(a.w.zeros + (nb * G + g) * kZeroBlockBytes)
-                   : make_uint2(0, 0);
+    const int64_t nbs = cb0 + (tid >> 4);
+    st.s = nbs < NB ? a.w.scales[(nbs * G + g) * 16 + (tid & 15)] : 0.0f;
   }
 }
 
+// Stage -> LDS.  The packed codes are unpacked here, once per workgroup, to
+// signed q - z bytes in exactly the order the MFMA B operand is read: block
+// u, half h (low nibbles = input channels 16j..16j+15 of the group, high =
+// 64+16j..), lane L.
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
     *reinterpret_cast<uint4*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = tid + kThreads * i;
-    *reinterpret_cast<uint4*>(buf + kBOff + ch * 16) = st.b[i];
-  }
-  if (tid < NCB * 16) {
-    reinterpret_cast<float*>(buf + kSOff)[tid] = st.s;
-  } else if (tid < NCB * 16 + NCB) {
-    *reinterpret_cast<uint2*>(buf + kZOff + (tid - NCB * 16) * kZeroBlockBytes) = st.z;
-  }
+  const uint32_t zz = st.z * 0x01010101u;
+  const uint32_t d[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
+  uint4 lo, hi;
+  lo.x = sub_zero_bytes(d[0] & 0x0F0F0F0Fu, zz);
+  lo.y = sub_zero_bytes(d[1] & 0x0F0F0F0Fu, zz);
+  lo.z = sub_zero_bytes(d[2] & 0x0F0F0F0Fu, zz);
+  lo.w = sub_zero_bytes(d[3] & 0x0F0F0F0Fu, zz);
+  hi.x = sub_zero_bytes((d[0] >> 4) & 0x0F0F0F0Fu, zz);
+  hi.y = sub_zero_bytes((d[1] >> 4) & 0x0F0F0F0Fu, zz);
+  hi.z = sub_zero_bytes((d[2] >> 4) & 0x0F0F0F0Fu, zz);
+  hi.w = sub_zero_bytes((d[3] >> 4) & 0x0F0F0F0Fu, zz);
+  const int u = tid >> 6, L = tid & 63;
+  *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = lo;
+  *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = hi;
+  if (tid < NCB * 16) reinterpret_cast<float*>(buf + kSOff)[tid] = st.s;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-// run of tiles (output-channel major) so the packed weights a tile column
-// needs are fetched into one XCD's L2 only.
+// run of tiles (tokens fastest) so the packed weights of a tile column are
+// fetched into one XCD's L2 and the tiles running together on an XCD share
+// their operands there.
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
   const int64_t xcd = b % 8, local = b / 8;
   const int64_t per = T / 8, rem = T % 8;
@@ -100,7 +107,7 @@ prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 wavefronts of 64 x 64
   const int r16 = lane & 15, j = lane >> 4;
   const int64_t G = a.K / kGroup;
   const int64_t NB = a.N / kBlockCols;
@@ -133,14 +140,8 @@ prefill_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int cb = wn * 4 + u;
-      const uint4 wv = *reinterpret_cast<const uint4*>(buf + kBOff + cb * kBlockBytes + lane * 16);
-      const uint32_t zz = zero_of(buf + kZOff + cb * kZeroBlockBytes, r16) * 0x01010101u;
-      const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        b0[u][w] = (int)sub_zero_bytes(d[w] & 0x0F0F0F0Fu, zz);
-        b1[u][w] = (int)sub_zero_bytes((d[w] >> 4) & 0x0F0F0F0Fu, zz);
-      }
+      b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
+      b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
       sv[u] = reinterpret_cast<const float*>(buf + kSOff)[cb * 16 + r16];
     }
 #pragma unroll
@@ -166,6 +167,8 @@ prefill_kernel(GemmArgs a) {
         for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[r];
       }
     }
+    // the other buffer was last read in group g - 1, before the barrier that
+    // ended it
     if (more) store_stage(smem[(g + 1) & 1], st);
     __syncthreads();
   }
