@@ -34,33 +34,35 @@ struct Stage {
   uint4 a[kAChunks];
   uint4 b;      // this thread's 16 packed bytes: block t/64, lane t%64
   uint32_t z;   // that lane's zero point
-  float s;      // threads < 128: scale of channel t%16 of block t/16
+  float s;      // scale of channel t%16 of block (t/16)%8
 };
 
 __device__ __forceinline__ void load_stage(const GemmArgs& a, int64_t m0, int64_t cb0, int64_t NB,
                                            int64_t G, int64_t g, Stage& st) {
+  // Branch-free: rows and blocks past the matrix read the last valid one and
+  // are zeroed after the load, so every thread issues the same loads and the
+  // waits for them stay exact.
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
     const int64_t m = m0 + (ch >> 3);
-    if (m < a.M)
-      st.a[i] = *reinterpret_cast<const uint4*>(a.qa + m * a.K + g * kGroup + (ch & 7) * 16);
-    else
-      st.a[i] = make_uint4(0, 0, 0, 0);
+    const uint4 v = *reinterpret_cast<const uint4*>(a.qa + min(m, a.M - 1) * a.K + g * kGroup +
+                                                    (ch & 7) * 16);
+    const uint32_t keep = m < a.M ? 0xFFFFFFFFu : 0u;
+    st.a[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
   }
   const int64_t nb = cb0 + (tid >> 6);
-  if (nb < NB) {
-    st.b = *reinterpret_cast<const uint4*>(a.w.codes + (nb * G + g) * kBlockBytes + (tid & 63) * 16);
-    st.z = zero_of(a.w.zeros + (nb * G + g) * kZeroBlockBytes, tid & 15);
-  } else {
-    st.b = make_uint4(0, 0, 0, 0);
-    st.z = 0;
-  }
-  if (tid < NCB * 16) {
-    const int64_t nbs = cb0 + (tid >> 4);
-    st.s = nbs < NB ? a.w.scales[(nbs * G + g) * 16 + (tid & 15)] : 0.0f;
-  }
+  const int64_t nbc = min(nb, NB - 1);
+  const uint4 bv =
+      *reinterpret_cast<const uint4*>(a.w.codes + (nbc * G + g) * kBlockBytes + (tid & 63) * 16);
+  const uint32_t zv = zero_of(a.w.zeros + (nbc * G + g) * kZeroBlockBytes, tid & 15);
+  const uint32_t keep = nb < NB ? 0xFFFFFFFFu : 0u;
+  st.b = make_uint4(bv.x & keep, bv.y & keep, bv.z & keep, bv.w & keep);
+  st.z = zv & keep;
+  const int64_t nbs = cb0 + ((tid >> 4) & (NCB - 1));
+  const float sv = a.w.scales[(min(nbs, NB - 1) * G + g) * 16 + (tid & 15)];
+  st.s = __uint_as_float(__float_as_uint(sv) & (nbs < NB ? 0xFFFFFFFFu : 0u));
 }
 
 // Stage -> LDS.  The packed codes are unpacked here, once per workgroup, to
@@ -88,7 +90,9 @@ __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st) {
   const int u = tid >> 6, L = tid & 63;
   *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = lo;
   *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = hi;
-  if (tid < NCB * 16) reinterpret_cast<float*>(buf + kSOff)[tid] = st.s;
+  // every thread holds the scale of entry tid % 128 (four identical writers
+  // per entry), so the store needs no branch
+  reinterpret_cast<float*>(buf + kSOff)[tid & (NCB * 16 - 1)] = st.s;
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -131,8 +135,9 @@ prefill_kernel(GemmArgs a) {
   __syncthreads();
 
   for (int64_t g = 0; g < G; ++g) {
-    const bool more = g + 1 < G;
-    if (more) load_stage(a, m0, cb0, NB, G, g + 1, st);
+    // the next group's operands (the last iteration re-reads group G - 1 into
+    // the idle buffer, which keeps the loop body free of branches)
+    load_stage(a, m0, cb0, NB, G, min(g + 1, G - 1), st);
     const uint8_t* buf = smem[g & 1];
 
     v4i b0[4], b1[4];
@@ -144,47 +149,67 @@ prefill_kernel(GemmArgs a) {
       b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
       sv[u] = reinterpret_cast<const float*>(buf + kSOff)[cb * 16 + r16];
     }
+    // A fragments, then the 16 tiles' MFMA pairs; each tile's rescale is
+    // interleaved with the MFMAs of the tiles after it (scheduling groups
+    // below), so the vector ALU and the matrix cores work side by side.
+    v4i a0[4], a1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
-      const v4i a0 = *reinterpret_cast<const v4i*>(arow);
-      const v4i a1 = *reinterpret_cast<const v4i*>(arow + 64);
+      a0[i] = *reinterpret_cast<const v4i*>(arow);
+      a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
+    }
+    // MFMA pair of tile t, then the rescale of tile t - 2 (whose result is
+    // ready by then): the vector ALU and the matrix cores work side by side.
+    // The fences keep the compiler from regrouping them.
+    v4i acc[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v4i acc = {0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[u], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[u], acc, 0, 0, 0);
+    for (int t = 0; t < 18; ++t) {
+      if (t < 16) {
+        const int i = t >> 2, u = t & 3;
+        const v4i zero = {0, 0, 0, 0};
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
+      }
+      if (t >= 2) {
+        const int e = t - 2, i = e >> 2, u = e & 3;
         if (DEBUG && a.partials) {
           const int64_t nb = cb0 + wn * 4 + u;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
             if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
-              a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[r];
+              a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
           }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[r];
+        for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // the other buffer was last read in group g - 1, before the barrier that
     // ended it
-    if (more) store_stage(smem[(g + 1) & 1], st);
+    store_stage(smem[(g + 1) & 1], st);
     __syncthreads();
   }
 
   if (!a.y) return;
+  // all row scales first (one wait), then the stores
+  float sam[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sam[i][r] = a.sa[min(m0 + wm * 64 + i * 16 + 4 * j + r, a.M - 1)];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
       if (m >= a.M) continue;
-      const float sam = a.sa[m];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int64_t nb = cb0 + wn * 4 + u;
-        if (nb < NB) a.y[m * a.N + nb * 16 + r16] = f32_to_bf16_rne(sam * accf[i][u][r]);
+        if (nb < NB) a.y[m * a.N + nb * 16 + r16] = f32_to_bf16_rne(sam[i][r] * accf[i][u][r]);
       }
     }
   }
