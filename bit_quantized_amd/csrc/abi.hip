@@ -134,6 +134,11 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
                 (long long)kGemvMaxK, (long long)K);
   if (path == W4A8_PATH_SKINNY && M > 16)
     return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
+  if (path == W4A8_PATH_PREFILL && (M * K > kPrefillMaxBytes || N * K / 2 > kPrefillMaxBytes))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
+                "PREFILL path addresses activations and codes with 32-bit offsets "
+                "(M*K=%lld, N*K/2=%lld, limit %lld)",
+                (long long)(M * K), (long long)(N * K / 2), (long long)kPrefillMaxBytes);
   if (fused && path != W4A8_PATH_GEMV)
     return fail(W4A8_ERR_INVALID_ARG, "in-kernel quantisation runs on the GEMV path only");
   if (debug) {

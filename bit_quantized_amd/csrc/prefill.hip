@@ -28,68 +28,79 @@ constexpr int kSOff = kBOff + NCB * 2 * kBlockBytes;  // scales [NCB][16]
 constexpr int kBufBytes = kSOff + NCB * 16 * 4;
 constexpr int kAChunks = BM * kGroup / 16 / kThreads;  // 16-B activation chunks per thread (4)
 
-// One group's operands as they come from HBM, held in registers while the
-// previous group computes.
+// One group's operands as they come from HBM, held in registers while
+// earlier groups compute.
 struct Stage {
-  uint4 a[kAChunks];
-  uint4 b;      // this thread's 16 packed bytes: block t/64, lane t%64
-  uint32_t z;   // that lane's zero point
-  float s;      // scale of channel t%16 of block (t/16)%8
+  v4i a[kAChunks];
+  v4i b;          // this thread's 16 packed bytes: block t/64, lane t%64
+  uint32_t zb;    // the byte holding that lane's zero point
+  float s;        // scale of channel t%16 of block (t/16)%8
 };
 
-__device__ __forceinline__ void load_stage(const GemmArgs& a, int64_t m0, int64_t cb0, int64_t NB,
-                                           int64_t G, int64_t g, Stage& st) {
-  // Branch-free: rows and blocks past the matrix read the last valid one and
-  // are zeroed after the load, so every thread issues the same loads and the
-  // waits for them stay exact.
+// Per-thread byte offsets of its operands within group 0; group g adds a
+// uniform g * (bytes per group) to the plane base.  Rows and blocks past the
+// matrix read the last valid one: they only reach outputs that are never
+// stored, so nothing needs masking and every thread issues the same loads.
+// (The host keeps M*K and N*K/2 below 2^31 on this path.)
+struct Offsets {
+  uint32_t a[kAChunks];
+  uint32_t b, z, s;
+  int zshift;
+};
+
+__device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
+                                                int64_t NB, int64_t G) {
   const int tid = threadIdx.x;
+  Offsets o;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
-    const int64_t m = m0 + (ch >> 3);
-    const uint4 v = *reinterpret_cast<const uint4*>(a.qa + min(m, a.M - 1) * a.K + g * kGroup +
-                                                    (ch & 7) * 16);
-    const uint32_t keep = m < a.M ? 0xFFFFFFFFu : 0u;
-    st.a[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    o.a[i] = (uint32_t)(min(m0 + (ch >> 3), a.M - 1) * a.K + (ch & 7) * 16);
   }
-  const int64_t nb = cb0 + (tid >> 6);
-  const int64_t nbc = min(nb, NB - 1);
-  const uint4 bv =
-      *reinterpret_cast<const uint4*>(a.w.codes + (nbc * G + g) * kBlockBytes + (tid & 63) * 16);
-  const uint32_t zv = zero_of(a.w.zeros + (nbc * G + g) * kZeroBlockBytes, tid & 15);
-  const uint32_t keep = nb < NB ? 0xFFFFFFFFu : 0u;
-  st.b = make_uint4(bv.x & keep, bv.y & keep, bv.z & keep, bv.w & keep);
-  st.z = zv & keep;
-  const int64_t nbs = cb0 + ((tid >> 4) & (NCB - 1));
-  const float sv = a.w.scales[(min(nbs, NB - 1) * G + g) * 16 + (tid & 15)];
-  st.s = __uint_as_float(__float_as_uint(sv) & (nbs < NB ? 0xFFFFFFFFu : 0u));
+  const int64_t nb = min(cb0 + (tid >> 6), NB - 1);
+  o.b = (uint32_t)(nb * G * kBlockBytes + (tid & 63) * 16);
+  o.z = (uint32_t)(nb * G * kZeroBlockBytes + ((tid & 15) >> 1));
+  o.zshift = (tid & 1) * 4;
+  const int64_t nbs = min(cb0 + ((tid >> 4) & (NCB - 1)), NB - 1);
+  o.s = (uint32_t)(nbs * G * 16 + (tid & 15));
+  return o;
+}
+
+__device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
+                                           Stage& st) {
+  const int8_t* qa = a.qa + g * kGroup;
+  const uint8_t* codes = a.w.codes + g * kBlockBytes;
+  const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
+  const float* scales = a.w.scales + g * 16;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) st.a[i] = *reinterpret_cast<const v4i*>(qa + o.a[i]);
+  st.b = *reinterpret_cast<const v4i*>(codes + o.b);
+  st.zb = zeros[o.z];
+  st.s = scales[o.s];
 }
 
 // Stage -> LDS.  The packed codes are unpacked here, once per workgroup, to
 // signed q - z bytes in exactly the order the MFMA B operand is read: block
 // u, half h (low nibbles = input channels 16j..16j+15 of the group, high =
 // 64+16j..), lane L.
-__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st) {
+__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
-    *reinterpret_cast<uint4*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
+    *reinterpret_cast<v4i*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
   }
-  const uint32_t zz = st.z * 0x01010101u;
-  const uint32_t d[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
-  uint4 lo, hi;
-  lo.x = sub_zero_bytes(d[0] & 0x0F0F0F0Fu, zz);
-  lo.y = sub_zero_bytes(d[1] & 0x0F0F0F0Fu, zz);
-  lo.z = sub_zero_bytes(d[2] & 0x0F0F0F0Fu, zz);
-  lo.w = sub_zero_bytes(d[3] & 0x0F0F0F0Fu, zz);
-  hi.x = sub_zero_bytes((d[0] >> 4) & 0x0F0F0F0Fu, zz);
-  hi.y = sub_zero_bytes((d[1] >> 4) & 0x0F0F0F0Fu, zz);
-  hi.z = sub_zero_bytes((d[2] >> 4) & 0x0F0F0F0Fu, zz);
-  hi.w = sub_zero_bytes((d[3] >> 4) & 0x0F0F0F0Fu, zz);
+  const uint32_t zz = ((st.zb >> zshift) & 0xFu) * 0x01010101u;
+  v4i lo, hi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t d = (uint32_t)st.b[w];
+    lo[w] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
+    hi[w] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
+  }
   const int u = tid >> 6, L = tid & 63;
-  *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = lo;
-  *reinterpret_cast<uint4*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = hi;
+  *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = lo;
+  *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = hi;
   // every thread holds the scale of entry tid % 128 (four identical writers
   // per entry), so the store needs no branch
   reinterpret_cast<float*>(buf + kSOff)[tid & (NCB * 16 - 1)] = st.s;
@@ -103,6 +114,61 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
   const int64_t xcd = b % 8, local = b / 8;
   const int64_t per = T / 8, rem = T % 8;
   return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+// One group on the matrix cores: fragments from LDS, the 16 tiles' MFMA
+// pairs, and the per-group rescale into the fp32 accumulators.
+template <bool DEBUG>
+__device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* buf, int64_t g,
+                                              int64_t m0, int64_t cb0, int64_t NB, int64_t G,
+                                              float (&accf)[4][4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  v4i b0[4], b1[4];
+  float sv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cb = wn * 4 + u;
+    b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
+    b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
+    sv[u] = reinterpret_cast<const float*>(buf + kSOff)[cb * 16 + r16];
+  }
+  v4i a0[4], a1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
+    a0[i] = *reinterpret_cast<const v4i*>(arow);
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
+  }
+  // MFMA pair of tile t, then the rescale of tile t - 2 (whose result is
+  // ready by then): the vector ALU and the matrix cores work side by side.
+  // The fences keep the compiler from regrouping them.
+  v4i acc[16];
+#pragma unroll
+  for (int t = 0; t < 18; ++t) {
+    if (t < 16) {
+      const int i = t >> 2, u = t & 3;
+      const v4i zero = {0, 0, 0, 0};
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
+    }
+    if (t >= 2) {
+      const int e = t - 2, i = e >> 2, u = e & 3;
+      if (DEBUG && a.partials) {
+        const int64_t nb = cb0 + wn * 4 + u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+          if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
+            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <bool DEBUG>
@@ -129,67 +195,28 @@ prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
 
-  Stage st;
-  load_stage(a, m0, cb0, NB, G, 0, st);
-  store_stage(smem[0], st);
+  // One group of 128 input channels per step: the operands of group g + 2
+  // are loaded while group g computes and group g + 1 (loaded one step
+  // earlier) is unpacked into the idle LDS buffer.  The two register stages
+  // alternate, so the loop is unrolled by two.
+
+  const Offsets off = make_offsets(a, m0, cb0, NB, G);
+  Stage s0, s1;
+  load_stage(a, off, 0, s0);
+  load_stage(a, off, min((int64_t)1, G - 1), s1);
+  store_stage(smem[0], s0, off.zshift);
   __syncthreads();
-
-  for (int64_t g = 0; g < G; ++g) {
-    // the next group's operands (the last iteration re-reads group G - 1 into
-    // the idle buffer, which keeps the loop body free of branches)
-    load_stage(a, m0, cb0, NB, G, min(g + 1, G - 1), st);
-    const uint8_t* buf = smem[g & 1];
-
-    v4i b0[4], b1[4];
-    float sv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cb = wn * 4 + u;
-      b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
-      b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
-      sv[u] = reinterpret_cast<const float*>(buf + kSOff)[cb * 16 + r16];
-    }
-    // A fragments, then the 16 tiles' MFMA pairs; each tile's rescale is
-    // interleaved with the MFMAs of the tiles after it (scheduling groups
-    // below), so the vector ALU and the matrix cores work side by side.
-    v4i a0[4], a1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
-      a0[i] = *reinterpret_cast<const v4i*>(arow);
-      a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
-    }
-    // MFMA pair of tile t, then the rescale of tile t - 2 (whose result is
-    // ready by then): the vector ALU and the matrix cores work side by side.
-    // The fences keep the compiler from regrouping them.
-    v4i acc[16];
-#pragma unroll
-    for (int t = 0; t < 18; ++t) {
-      if (t < 16) {
-        const int i = t >> 2, u = t & 3;
-        const v4i zero = {0, 0, 0, 0};
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
-      }
-      if (t >= 2) {
-        const int e = t - 2, i = e >> 2, u = e & 3;
-        if (DEBUG && a.partials) {
-          const int64_t nb = cb0 + wn * 4 + u;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
-            if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
-              a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the other buffer was last read in group g - 1, before the barrier that
-    // ended it
-    store_stage(smem[(g + 1) & 1], st);
+  for (int64_t g = 0; g < G; g += 2) {
+    // (the last steps re-read group G - 1 into stages nobody consumes, which
+    // keeps each half free of branches)
+    load_stage(a, off, min(g + 2, G - 1), s0);
+    compute_group<DEBUG>(a, smem[0], g, m0, cb0, NB, G, accf);
+    store_stage(smem[1], s1, off.zshift);  // buffer 1 was last read before the previous barrier
+    __syncthreads();
+    if (g + 1 >= G) break;
+    load_stage(a, off, min(g + 3, G - 1), s1);
+    compute_group<DEBUG>(a, smem[1], g + 1, m0, cb0, NB, G, accf);
+    store_stage(smem[0], s0, off.zshift);
     __syncthreads();
   }
 

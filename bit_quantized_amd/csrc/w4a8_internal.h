@@ -83,6 +83,9 @@ struct GemmArgs {
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
 constexpr int64_t kGemvMaxK = 32768;
+// The prefill kernel addresses the activation and code planes with 32-bit
+// per-thread offsets.
+constexpr int64_t kPrefillMaxBytes = ((int64_t)1 << 31) - 1;
 
 struct GemvShape {
   int cb, ks, ksplit;

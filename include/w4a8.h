@@ -61,7 +61,8 @@ extern "C" {
 
 /* GEMM paths (M buckets).  AUTO picks GEMV for M == 1 (K <= 32768, else
  * SKINNY), SKINNY for 2 <= M <= 16, PREFILL for M > 16; the choice depends on
- * (M, N, K) only. */
+ * (M, N, K) only.  PREFILL needs M*K < 2^31 and N*K/2 < 2^31 (32-bit operand
+ * offsets); larger shapes return W4A8_ERR_UNSUPPORTED_SHAPE. */
 #define W4A8_PATH_AUTO 0
 #define W4A8_PATH_GEMV 1
 #define W4A8_PATH_SKINNY 2
