@@ -8,6 +8,9 @@ up-projection).  The same line carries:
   roofline      the dominant kernel (the GEMV) against MI355X's 8 TB/s HBM
   cpu_baseline  the CPU oracle timed on this host's cores on the same workload
   prefill       the M=2048 prefill GEMM in int8 TOPS against 5.0 POP/s
+  skinny        M=4 and M=16 decode, K=18944 -> N=3584, quant + GEMM
+  layer         a 7B-shaped decoder layer's seven linears plus the output
+                head, each alone and all from one graph, at M=1 and M=512
 
 Timing: inputs are resident in HBM before the timed region; each timed step
 reads a different packed copy of the weights (16 copies, > 512 MB) so the
@@ -46,8 +49,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--only", choices=["all", "decode", "prefill", "copy"], default="all",
-                   help="run one part only (for hardware-counter passes)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the skinny and layer legs")
+    p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "copy"],
+                   default="all", help="run one part only (for hardware-counter passes)")
     return p.parse_args()
 
 
@@ -137,17 +142,24 @@ def setup_linear(torch, w4, spec, copies):
     return lin, x, Ws
 
 
-def parity_check(w4, lin, x, W, rows=None):
-    """The benchmarked path against the oracle before timing."""
+def parity_check(w4, lin, x, W, rows=None, cols=None):
+    """The benchmarked path against the oracle before timing (on a window of
+    rows and columns for the large shapes)."""
     import oracle
     y = w4.linear(x, W).float().cpu().numpy()
     qa_ref, sa_ref = oracle.quant_act(lin["x"])
     m0, m1 = rows or (0, lin["spec"].M)
-    ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1))
-    ok, err, bound = oracle.tolerance_ok(y[m0:m1], ref)
+    c0, c1 = cols or (0, lin["spec"].N)
+    ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1),
+                        cols=(c0, c1))
+    ok, err, bound = oracle.tolerance_ok(y[m0:m1, c0:c1], ref)
     if not ok:
-        raise SystemExit(f"parity check failed: max err {err:.3e} > {bound:.3e}")
-    return {"rows": [m0, m1], "max_err": err, "bound": bound}
+        raise SystemExit(f"parity check failed ({lin['spec'].name}): max err {err:.3e} > "
+                         f"{bound:.3e}")
+    out = {"rows": [m0, m1], "max_err": err, "bound": bound}
+    if cols:
+        out["cols"] = [c0, c1]
+    return out
 
 
 def bench_decode(torch, w4, args):
@@ -237,6 +249,96 @@ def bench_prefill(torch, w4, args):
     }
 
 
+def bench_skinny(torch, w4, args):
+    """Skinny decode (2 <= M <= 16): K=18944 -> N=3584, as quant + GEMM
+    through w4a8_linear, against the HBM roofline."""
+    from bit_quantized_amd import synth
+    out = []
+    for spec in (synth.SKINNY_DOWN_4, synth.SKINNY_DOWN_16):
+        lin, x, Ws = setup_linear(torch, w4, spec, args.copies)
+        M, K, N = spec.M, spec.K, spec.N
+        parity = parity_check(w4, lin, x, Ws[0])
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(max(w4.linear_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
+                         device="cuda")
+        R = len(Ws)
+        n = 64
+        step_ms = graph_steps_ms(torch, lambda i: w4.linear(x, Ws[i % R], out=y, workspace=ws),
+                                 8, n) / n
+        qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+        w4.quant_act(x, qa, sa)
+        gws = torch.zeros(max(w4.workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+        gemm_ms = graph_steps_ms(torch, lambda i: w4.gemm(qa, sa, Ws[i % R], out=y, workspace=gws),
+                                 8, n) / n
+        b = algorithmic_bytes(M, N, K)
+        out.append({"workload": f"{spec.name} M={M} K={K} N={N} (quant + GEMM)",
+                    "path": {1: "gemv", 2: "skinny", 3: "prefill"}[w4.select_path(M, N, K)],
+                    "us_per_step": round(step_ms * 1e3, 3),
+                    "GBps": round(b / (step_ms * 1e-3) / 1e9, 1),
+                    "frac": round(b / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "gemm_us": round(gemm_ms * 1e3, 3), "bytes_per_step": b, "parity": parity})
+        del Ws
+    return out
+
+
+def bench_layer(torch, w4, args):
+    """One 7B-shaped decoder layer's linears (q, k, v, o, gate, up, down) and
+    the output head, at M=1 (decode) and M=512 (prefill): each linear alone
+    (kernel time from a graph of launches), and the eight in sequence from one
+    HIP graph (the wall time a layer step would see).  Two packed copies of
+    every weight rotate, so the 256 MB Infinity Cache cannot serve them."""
+    from bit_quantized_amd import synth
+    res = {}
+    for M in (1, 512):
+        specs = synth.layer_specs(M)
+        legs = []
+        for spec in specs:
+            lin, x, Ws = setup_linear(torch, w4, spec, 2)
+            K, N = spec.K, spec.N
+            parity = parity_check(w4, lin, x, Ws[0], rows=(0, 1), cols=(0, 64))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.zeros(max(w4.linear_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
+                             device="cuda")
+            legs.append({"spec": spec, "x": x, "Ws": Ws, "y": y, "ws": ws, "parity": parity})
+        rows = []
+        for L in legs:
+            spec = L["spec"]
+            n = 32 if M == 1 else 8
+            ms = graph_steps_ms(torch, lambda i, L=L: w4.linear(L["x"], L["Ws"][i % 2], out=L["y"],
+                                                               workspace=L["ws"]), 4, n) / n
+            r = {"linear": spec.name.split("_")[1], "K": spec.K, "N": spec.N,
+                 "us": round(ms * 1e3, 3), "parity_ok": L["parity"]["max_err"] <= L["parity"]["bound"]}
+            if M == 1:
+                b = algorithmic_bytes(M, spec.N, spec.K)
+                r["GBps"] = round(b / (ms * 1e-3) / 1e9, 1)
+                r["frac"] = round(r["GBps"] / HBM_PEAK_GBS, 4)
+            else:
+                ops = 2.0 * M * spec.N * spec.K
+                r["TOPS"] = round(ops / (ms * 1e-3) / 1e12, 1)
+                r["frac"] = round(r["TOPS"] / INT8_PEAK_TOPS, 4)
+            rows.append(r)
+
+        def layer_step(i):
+            for L in legs:
+                w4.linear(L["x"], L["Ws"][i % 2], out=L["y"], workspace=L["ws"])
+
+        n = 16 if M == 1 else 4
+        wall_ms = graph_steps_ms(torch, layer_step, 2, n) / n
+        entry = {"linears": rows, "sum_us": round(sum(r["us"] for r in rows), 2),
+                 "graph_wall_us": round(wall_ms * 1e3, 2)}
+        if M == 1:
+            b = sum(algorithmic_bytes(1, L["spec"].N, L["spec"].K) for L in legs)
+            entry["graph_GBps"] = round(b / (wall_ms * 1e-3) / 1e9, 1)
+        else:
+            ops = sum(2.0 * M * L["spec"].N * L["spec"].K for L in legs)
+            entry["graph_TOPS"] = round(ops / (wall_ms * 1e-3) / 1e12, 1)
+        res[f"M{M}"] = entry
+        del legs
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_decode(res, seconds):
     """The oracle as it stands on this host: one decode step = quantise the
     token and compute all N outputs (exact per-group int products, float64
@@ -317,11 +419,15 @@ def main():
         copy_calibration(torch)
         return
 
-    dec = pre = None
+    dec = pre = skinny = layer = None
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
         pre = bench_prefill(torch, w4, args)
+    if args.only == "skinny" or (args.only == "all" and not args.no_extra):
+        skinny = bench_skinny(torch, w4, args)
+    if args.only == "layer" or (args.only == "all" and not args.no_extra):
+        layer = bench_layer(torch, w4, args)
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline and args.only == "all":
         if dec:
@@ -331,7 +437,13 @@ def main():
 
     from bit_quantized_amd import synth
     if dec is None:
-        out = {"metric": METRIC, "prefill": {k: v for k, v in pre.items() if k not in ("spec", "lin")}}
+        out = {"metric": METRIC}
+        if pre:
+            out["prefill"] = {k: v for k, v in pre.items() if k not in ("spec", "lin")}
+        if skinny:
+            out["skinny"] = skinny
+        if layer:
+            out["layer"] = layer
         print(json.dumps(out))
         return
     spec = dec["spec"]
@@ -364,6 +476,10 @@ def main():
         p = {k: v for k, v in pre.items() if k not in ("spec", "lin")}
         p["cpu_baseline"] = cpu_pre
         line["prefill"] = p
+    if skinny:
+        line["skinny"] = skinny
+    if layer:
+        line["layer"] = layer
     line["system"] = gpu_info(torch)
     print(json.dumps(line))
 
