@@ -90,6 +90,7 @@ constexpr int64_t kPrefillMaxBytes = ((int64_t)1 << 31) - 1;
 struct GemvShape {
   int cb, ks, ksplit;
 };
+int device_cus();  // compute units of the current device (cached)
 GemvShape gemv_shape(int64_t N, int64_t K);
 bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s);
 int skinny_ksplit(int64_t M, int64_t N, int64_t K);
