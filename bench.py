@@ -293,6 +293,7 @@ def bench_layer(torch, w4, args):
     for M in (1, 512):
         specs = synth.layer_specs(M)
         legs = []
+        sib = {}
         for spec in specs:
             lin, x, Ws = setup_linear(torch, w4, spec, 2)
             K, N = spec.K, spec.N
@@ -301,6 +302,9 @@ def bench_layer(torch, w4, args):
             ws = torch.zeros(max(w4.linear_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
                              device="cuda")
             legs.append({"spec": spec, "x": x, "Ws": Ws, "y": y, "ws": ws, "parity": parity})
+            name = spec.name.split("_")[1]
+            if name in ("q", "k", "v", "gate", "up"):
+                sib[name] = (lin, x)
         rows = []
         for L in legs:
             spec = L["spec"]
@@ -327,12 +331,64 @@ def bench_layer(torch, w4, args):
         wall_ms = graph_steps_ms(torch, layer_step, 2, n) / n
         entry = {"linears": rows, "sum_us": round(sum(r["us"] for r in rows), 2),
                  "graph_wall_us": round(wall_ms * 1e3, 2)}
+
+        # sibling projections fused: q/k/v as one weight, gate/up as one (one
+        # activation quantisation and one GEMM each); five launches a layer
+        fused = []
+        for group_names in (("q", "k", "v"), ("gate", "up")):
+            parts = [tuple(to_dev(torch, sib[nm][0][k]) for k in ("q", "z", "s"))
+                     for nm in group_names]
+            Ws = [w4.pack_siblings(parts) for _ in range(2)]
+            del parts
+            x0 = sib[group_names[0]][1]
+            Nf = Ws[0].packed.N
+            # parity: every sibling's first 64 columns of row 0 against the
+            # oracle, on the shared input
+            import oracle
+            lin0 = sib[group_names[0]][0]
+            qa_ref, sa_ref = oracle.quant_act(lin0["x"])
+            for nm, yv in zip(group_names, w4.linear_siblings(x0, Ws[0])):
+                ln = sib[nm][0]
+                ref = oracle.linear(qa_ref, sa_ref, ln["q"], ln["z"], ln["s"], rows=(0, 1),
+                                    cols=(0, 64))
+                ok, err, bound = oracle.tolerance_ok(yv.float().cpu().numpy()[0:1, 0:64], ref)
+                if not ok:
+                    raise SystemExit(f"fused sibling parity failed ({nm}, M={M})")
+            yf = torch.empty((M, Nf), dtype=torch.bfloat16, device="cuda")
+            wsf = torch.zeros(max(w4.linear_workspace_bytes(M, Nf, x0.shape[1]), 16),
+                              dtype=torch.uint8, device="cuda")
+            fused.append({"name": "".join(group_names) if len(group_names) == 3 else "gate_up",
+                          "x": x0, "Ws": Ws, "y": yf, "ws": wsf, "N": Nf, "K": x0.shape[1]})
+        rest = [L for L in legs if L["spec"].name.split("_")[1] in ("o", "down", "head")]
+        frows = []
+        for F in fused:
+            nn = 32 if M == 1 else 8
+            ms = graph_steps_ms(torch, lambda i, F=F: w4.linear(F["x"], F["Ws"][i % 2].packed,
+                                                               out=F["y"], workspace=F["ws"]),
+                                4, nn) / nn
+            frows.append({"linear": F["name"], "K": F["K"], "N": F["N"], "us": round(ms * 1e3, 3)})
+
+        def fused_step(i):
+            w4.linear(fused[0]["x"], fused[0]["Ws"][i % 2].packed, out=fused[0]["y"],
+                      workspace=fused[0]["ws"])
+            L = rest[0]  # o
+            w4.linear(L["x"], L["Ws"][i % 2], out=L["y"], workspace=L["ws"])
+            w4.linear(fused[1]["x"], fused[1]["Ws"][i % 2].packed, out=fused[1]["y"],
+                      workspace=fused[1]["ws"])
+            for L in rest[1:]:  # down, head
+                w4.linear(L["x"], L["Ws"][i % 2], out=L["y"], workspace=L["ws"])
+
+        fwall_ms = graph_steps_ms(torch, fused_step, 2, n) / n
+        entry["fused_siblings"] = {"linears": frows, "graph_wall_us": round(fwall_ms * 1e3, 2)}
+        del fused, sib
         if M == 1:
             b = sum(algorithmic_bytes(1, L["spec"].N, L["spec"].K) for L in legs)
             entry["graph_GBps"] = round(b / (wall_ms * 1e-3) / 1e9, 1)
+            entry["fused_siblings"]["graph_GBps"] = round(b / (fwall_ms * 1e-3) / 1e9, 1)
         else:
             ops = sum(2.0 * M * L["spec"].N * L["spec"].K for L in legs)
             entry["graph_TOPS"] = round(ops / (wall_ms * 1e-3) / 1e12, 1)
+            entry["fused_siblings"]["graph_TOPS"] = round(ops / (fwall_ms * 1e-3) / 1e12, 1)
         res[f"M{M}"] = entry
         del legs
         torch.cuda.empty_cache()

@@ -41,6 +41,8 @@ SIGNATURES = {
     "w4a8_last_error": (ctypes.c_char_p, []),
     "w4a8_packed_weight_bytes": (_sz, [_i64, _i64, _i32]),
     "w4a8_pack_weights": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "w4a8_pack_weights_into": (ctypes.c_int,
+                               [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _i64, _i64, _vp]),
     "w4a8_unpack_weights": (ctypes.c_int, [_vp, _sz, _i64, _i64, _i32, _vp, _vp, _vp, _vp]),
     "w4a8_quant_act": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
     "w4a8_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
@@ -132,6 +134,51 @@ def pack_weights(q: torch.Tensor, z: torch.Tensor, s: torch.Tensor, group: int =
     _check(lib.w4a8_pack_weights(_p(q), _p(z), _p(s), N, K, group, _p(out), out.numel(),
                                  _stream(q.device)))
     return PackedWeight(out, N, K, group, lib.w4a8_layout_version())
+
+
+@dataclass
+class SiblingWeight:
+    """Sibling projections of one input (query/key/value, gate/up) packed
+    side by side as one weight: one activation quantisation and one GEMM
+    produce all of them, each a column range of the output."""
+    packed: PackedWeight
+    widths: tuple
+
+    def split(self, y: torch.Tensor):
+        """Per-sibling views of an output [M][sum(widths)] (no copy)."""
+        return list(torch.split(y, list(self.widths), dim=1))
+
+
+def pack_siblings(parts, group: int = GROUP) -> SiblingWeight:
+    """parts: [(q, z, s), ...] sharing K; each packed straight into its
+    output-channel range of one buffer (w4a8_pack_weights_into)."""
+    lib = load()
+    if not parts:
+        raise ValueError("no parts")
+    K = parts[0][0].shape[1]
+    widths = tuple(int(q.shape[0]) for q, _, _ in parts)
+    N = sum(widths)
+    dev = parts[0][0].device
+    nbytes = lib.w4a8_packed_weight_bytes(N, K, group)
+    if nbytes == 0:
+        _check(lib.w4a8_pack_weights(None, None, None, N, K, group, None, 0, None))
+    out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    off = 0
+    for (q, z, s), n in zip(parts, widths):
+        _need_cuda(q, z, s)
+        if q.dtype != torch.uint8 or z.dtype != torch.uint8 or s.dtype != torch.float32:
+            raise TypeError("q, z must be uint8 and s float32")
+        if q.shape[1] != K:
+            raise ValueError("sibling projections must share K")
+        _check(lib.w4a8_pack_weights_into(_p(q), _p(z), _p(s), n, K, group, _p(out), out.numel(),
+                                          N, off, _stream(dev)))
+        off += n
+    return SiblingWeight(PackedWeight(out, N, K, group, lib.w4a8_layout_version()), widths)
+
+
+def linear_siblings(x: torch.Tensor, w: SiblingWeight, out=None, workspace=None):
+    """All siblings from one quantisation and one GEMM; returns their views."""
+    return w.split(linear(x, w.packed, out=out, workspace=workspace))
 
 
 def unpack_weights(w: PackedWeight):

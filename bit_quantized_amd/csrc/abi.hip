@@ -245,24 +245,37 @@ size_t w4a8_packed_weight_bytes(int64_t N, int64_t K, int32_t group) {
   return (size_t)packed_bytes(N, K);
 }
 
-int w4a8_pack_weights(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
-                      int32_t group, void* packed, size_t packed_bytes_, void* stream) {
-  int rc = check_weight_shape(N, K, group);
+int w4a8_pack_weights_into(const uint8_t* q, const uint8_t* z, const float* s, int64_t N_part,
+                           int64_t K, int32_t group, void* packed, size_t packed_bytes_,
+                           int64_t N_total, int64_t n_offset, void* stream) {
+  int rc = check_weight_shape(N_part, K, group);
   if (rc) return rc;
+  rc = check_weight_shape(N_total, K, group);
+  if (rc) return rc;
+  if (n_offset < 0 || n_offset % kBlockCols || n_offset + N_part > N_total)
+    return fail(W4A8_ERR_INVALID_ARG,
+                "channels [%lld, %lld) are not a 16-aligned range of the %lld packed ones",
+                (long long)n_offset, (long long)(n_offset + N_part), (long long)N_total);
   if (!q || !z || !s || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(q) || !aligned16(packed) || !aligned16(s))
     return fail(W4A8_ERR_MISALIGNED, "q, s and packed must be 16-byte aligned");
-  const size_t need = (size_t)packed_bytes(N, K);
+  const size_t need = (size_t)packed_bytes(N_total, K);
   if (packed_bytes_ < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
   const size_t G = (size_t)(K / kGroup);
-  if (overlaps(packed, need, q, (size_t)(N * K)) || overlaps(packed, need, z, (size_t)N * G) ||
-      overlaps(packed, need, s, (size_t)N * G * 4))
+  if (overlaps(packed, need, q, (size_t)(N_part * K)) ||
+      overlaps(packed, need, z, (size_t)N_part * G) ||
+      overlaps(packed, need, s, (size_t)N_part * G * 4))
     return fail(W4A8_ERR_INVALID_ARG, "packed buffer aliases an input");
   (void)hipGetLastError();
-  return device_status(launch_pack(q, z, s, N, K, static_cast<uint8_t*>(packed),
-                                   static_cast<hipStream_t>(stream)),
+  return device_status(launch_pack_into(q, z, s, N_part, K, static_cast<uint8_t*>(packed), N_total,
+                                        n_offset, static_cast<hipStream_t>(stream)),
                        "pack launch");
+}
+
+int w4a8_pack_weights(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
+                      int32_t group, void* packed, size_t packed_bytes_, void* stream) {
+  return w4a8_pack_weights_into(q, z, s, N, K, group, packed, packed_bytes_, N, 0, stream);
 }
 
 int w4a8_unpack_weights(const void* packed, size_t packed_bytes_, int64_t N, int64_t K,

@@ -398,9 +398,9 @@ int device_cus() {
 // Grid for an N x K weight.  One 1024-thread workgroup fills a compute unit,
 // so the grid is a whole number of rounds of the compute units (no tail of
 // late workgroups) with about 128 (block, group) units per workgroup.  K is
-// split across workgroups (into >= 16-group slices) when there are too few
-// channel blocks to give every compute unit one, or when one block's groups
-// exceed what the streamers of a workgroup hold.  `cb` carries the number of
+// split across workgroups (into >= 16-group slices) when one block's groups
+// exceed what the streamers of a workgroup hold, or when the channel blocks
+// fill less than half the compute units.  `cb` carries the number of
 // workgroups along N.
 GemvShape gemv_shape(int64_t N, int64_t K) {
   const int64_t NB = N / kBlockCols, G = K / kGroup;
@@ -419,8 +419,10 @@ GemvShape gemv_shape(int64_t N, int64_t K) {
     if (w > NB) w = NB;
     s.cb = (int)w;
   } else {
+    // fewer channel blocks than compute units: split K while the doubled grid
+    // still fits in one round (a second round would cost more than it saves)
     s.cb = (int)NB;
-    while ((int64_t)s.cb * s.ksplit < cus && G / (s.ksplit * 2) >= 16) s.ksplit *= 2;
+    while ((int64_t)s.cb * s.ksplit * 2 <= cus && G / (s.ksplit * 2) >= 16) s.ksplit *= 2;
   }
   return s;
 }

@@ -99,29 +99,40 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
-hipError_t launch_pack(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
-                       uint8_t* packed, hipStream_t st) {
+// Packs a [N_part][K] weight into channels [n_offset, n_offset + N_part) of a
+// buffer packed for N_total channels: every plane holds its channel blocks in
+// order, so the part is one contiguous range of each plane.
+hipError_t launch_pack_into(const uint8_t* q, const uint8_t* z, const float* s, int64_t N_part,
+                            int64_t K, uint8_t* packed, int64_t N_total, int64_t n_offset,
+                            hipStream_t st) {
   const int64_t G = K / kGroup;
-  const int64_t runs = N * K / 32;  // 16-byte runs
-  const int64_t cells = N * G;
+  const int64_t b0 = n_offset / kBlockCols;  // first channel block of the part
+  const int64_t runs = N_part * K / 32;      // 16-byte runs
+  const int64_t cells = N_part * G;
   hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks_for(runs)), dim3(256), 0, st, q, K, G, runs,
-                     packed);
+                     packed + b0 * G * kBlockBytes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pack_meta_kernel, dim3(blocks_for(cells)), dim3(256), 0, st, z, s, G, cells,
-                     packed + zeros_offset(N, K),
-                     reinterpret_cast<float*>(packed + scales_offset(N, K)));
+                     packed + zeros_offset(N_total, K) + b0 * G * kZeroBlockBytes,
+                     reinterpret_cast<float*>(packed + scales_offset(N_total, K)) + b0 * G * 16);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t a0 = N * K / 2, a1 = zeros_offset(N, K);
-  const int64_t b0 = zeros_offset(N, K) + N * G / 2, b1 = scales_offset(N, K);
-  const int64_t gaps = (a1 - a0) + (b1 - b0);
+  // the alignment gaps of the whole buffer (idempotent, so every part may)
+  const int64_t a0 = N_total * K / 2, a1 = zeros_offset(N_total, K);
+  const int64_t c0 = zeros_offset(N_total, K) + N_total * G / 2, c1 = scales_offset(N_total, K);
+  const int64_t gaps = (a1 - a0) + (c1 - c0);
   if (gaps > 0) {
     hipLaunchKernelGGL(zero_gaps_kernel, dim3(blocks_for(gaps)), dim3(256), 0, st, packed, a0, a1,
-                       b0, b1);
+                       c0, c1);
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_pack(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
+                       uint8_t* packed, hipStream_t st) {
+  return launch_pack_into(q, z, s, N, K, packed, N, 0, st);
 }
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q, uint8_t* z,

@@ -60,6 +60,9 @@ __device__ __forceinline__ uint32_t zero_of(const uint8_t* zblk, int c) {
 
 hipError_t launch_pack(const uint8_t* q, const uint8_t* z, const float* s, int64_t N, int64_t K,
                        uint8_t* packed, hipStream_t st);
+hipError_t launch_pack_into(const uint8_t* q, const uint8_t* z, const float* s, int64_t N_part,
+                            int64_t K, uint8_t* packed, int64_t N_total, int64_t n_offset,
+                            hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q, uint8_t* z,
                          float* s, hipStream_t st);
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,

@@ -111,6 +111,29 @@ int w4a8_pack_weights(const uint8_t* q, const uint8_t* z, const float* s,
                       int64_t N, int64_t K, int32_t group,
                       void* packed, size_t packed_bytes, void* stream);
 
+/*
+ * w4a8_pack_weights_into — sibling projections of one input (query/key/value,
+ * gate/up) packed side by side as ONE weight of N_total output channels, so a
+ * single activation quantisation and a single GEMM serve all of them.  Packs
+ * the [N_part][K] weight (q, z, s as for w4a8_pack_weights) into output
+ * channels [n_offset, n_offset + N_part) of a buffer of
+ * w4a8_packed_weight_bytes(N_total, K, group) bytes; packing every part of a
+ * partition of [0, N_total) gives the bytes w4a8_pack_weights makes from the
+ * parts stacked along N.  Parts may be packed in any order; the alignment
+ * gaps between the planes are zeroed by each call.
+ * ("Serve a pre-quantized int8 weight-only DiT ...", comments "Verdict in
+ * brief" and "Round two": query/key/value weights load as one fused
+ * projection; "The 4-bit CPU path", section "The weight layout, measured": a
+ * fused gate/up projection.)
+ * Requirements: as w4a8_pack_weights for both N_part and N_total;
+ * n_offset % 16 == 0 and n_offset + N_part <= N_total (else
+ * W4A8_ERR_INVALID_ARG).
+ */
+int w4a8_pack_weights_into(const uint8_t* q, const uint8_t* z, const float* s,
+                           int64_t N_part, int64_t K, int32_t group,
+                           void* packed, size_t packed_bytes,
+                           int64_t N_total, int64_t n_offset, void* stream);
+
 /* Inverse of w4a8_pack_weights (for tests and inspection): writes q, z, s in
  * the logical layouts described above. */
 int w4a8_unpack_weights(const void* packed, size_t packed_bytes,

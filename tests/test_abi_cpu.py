@@ -137,3 +137,15 @@ def test_linear_rejections(lib):
     assert f(FAKE, 0, FAKE2, pb, 4, 256, 256, 128, y, None, 0, None) == -4     # needs workspace
     assert lib.w4a8_linear_workspace_bytes(1, 18944, 3584, 128) == 0          # one launch
     assert lib.w4a8_linear_workspace_bytes(4, 256, 256, 128) >= 4 * 256 + 16
+
+
+def test_pack_into_rejections(lib):
+    f = lib.w4a8_pack_weights_into
+    big = 1 << 30
+    assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, big, 64, 8, None) == -1     # offset % 16
+    assert f(FAKE, FAKE, FAKE, 32, 128, 128, FAKE2, big, 64, 48, None) == -1    # past N_total
+    assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, big, 64, -16, None) == -1   # negative
+    assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, big, 70, 0, None) == -2     # N_total tail
+    assert f(FAKE, FAKE, FAKE, 20, 128, 128, FAKE2, big, 64, 0, None) == -2     # part tail
+    pb = lib.w4a8_packed_weight_bytes(64, 128, 128)
+    assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, pb - 1, 64, 0, None) == -4  # sized for N_total

@@ -351,3 +351,55 @@ def test_gemv_partials_wide(w4):
         P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"])
         assert np.array_equal(P.cpu().numpy(), P_ref)
         _check_y(y, lin, qa_ref, sa_ref)
+
+
+# ----------------------------------------------------- sibling projections
+
+def _sibling_parts(seed, K, widths):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [synth.draw_weights(rng, n, K) for n in widths]
+
+
+def test_pack_into_equals_stacked_pack(w4):
+    """Parts packed into their channel ranges (in any order) give the bytes of
+    the stacked weight packed whole."""
+    say("pack_into K=384 widths 48,16,32")
+    K, widths = 384, (48, 16, 32)
+    parts = _sibling_parts(5, K, widths)
+    q = np.concatenate([p[0] for p in parts])
+    z = np.concatenate([p[1] for p in parts])
+    s = np.concatenate([p[2] for p in parts])
+    whole = w4.pack_weights(dev(q), dev(z), dev(s)).buf.cpu().numpy()
+    fused = w4.pack_siblings([tuple(dev(a) for a in p) for p in parts])
+    assert fused.widths == widths
+    assert np.array_equal(fused.packed.buf.cpu().numpy(), whole)
+    # reverse order of packing, into a buffer first filled with garbage
+    lib = w4.load()
+    N = sum(widths)
+    buf = torch.full((len(whole),), 0xA5, dtype=torch.uint8, device="cuda")
+    offs = np.cumsum((0,) + widths)[:-1]
+    for p, n, off in reversed(list(zip(parts, widths, offs))):
+        qd, zd, sd = (dev(a) for a in p)
+        rc = lib.w4a8_pack_weights_into(qd.data_ptr(), zd.data_ptr(), sd.data_ptr(), n, K, 128,
+                                        buf.data_ptr(), buf.numel(), N, int(off), None)
+        assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), whole)
+
+
+@pytest.mark.parametrize("M", [1, 4, 300])
+def test_sibling_linear(w4, M):
+    """Query/key/value-shaped siblings as one weight: one quantisation and one
+    GEMM; every sibling's columns against the oracle on that sibling alone."""
+    say(f"siblings M={M}")
+    K, widths = 1024, (512, 128, 128)
+    parts = _sibling_parts(7, K, widths)
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    W = w4.pack_siblings([tuple(dev(a) for a in p) for p in parts])
+    ys = w4.linear_siblings(dev(x), W)
+    qa_ref, sa_ref = oracle.quant_act(x)
+    for (q, z, s), y in zip(parts, ys):
+        ref = oracle.linear(qa_ref, sa_ref, q, z, s)
+        ok, err, bound = oracle.tolerance_ok(to_f32(y), ref, REL)
+        assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
