@@ -71,6 +71,7 @@ int pick_path(int64_t M, int64_t K) {
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
+  if (path == W4A8_PATH_PREFILL) return prefill_ksplit(M, N, K);
   return 1;
 }
 

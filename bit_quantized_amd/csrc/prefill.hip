@@ -186,6 +186,8 @@ prefill_kernel(GemmArgs a) {
   const int64_t t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
   const int64_t tm = t % tiles_m, tn = t / tiles_m;
   const int64_t m0 = tm * BM, cb0 = tn * NCB;
+  // K slice of this workgroup: groups [gb, ge) (all of K unless split)
+  const int64_t gb = G * blockIdx.y / gridDim.y, ge = G * (blockIdx.y + 1) / gridDim.y;
 
   float accf[4][4][4];
 #pragma unroll
@@ -202,24 +204,41 @@ prefill_kernel(GemmArgs a) {
 
   const Offsets off = make_offsets(a, m0, cb0, NB, G);
   Stage s0, s1;
-  load_stage(a, off, 0, s0);
-  load_stage(a, off, min((int64_t)1, G - 1), s1);
+  load_stage(a, off, gb, s0);
+  load_stage(a, off, min(gb + 1, ge - 1), s1);
   store_stage(smem[0], s0, off.zshift);
   __syncthreads();
-  for (int64_t g = 0; g < G; g += 2) {
-    // (the last steps re-read group G - 1 into stages nobody consumes, which
+  for (int64_t g = gb; g < ge; g += 2) {
+    // (the last steps re-read group ge - 1 into stages nobody consumes, which
     // keeps each half free of branches)
-    load_stage(a, off, min(g + 2, G - 1), s0);
+    load_stage(a, off, min(g + 2, ge - 1), s0);
     compute_group<DEBUG>(a, smem[0], g, m0, cb0, NB, G, accf);
     store_stage(smem[1], s1, off.zshift);  // buffer 1 was last read before the previous barrier
     __syncthreads();
-    if (g + 1 >= G) break;
-    load_stage(a, off, min(g + 3, G - 1), s1);
+    if (g + 1 >= ge) break;
+    load_stage(a, off, min(g + 3, ge - 1), s1);
     compute_group<DEBUG>(a, smem[1], g + 1, m0, cb0, NB, G, accf);
     store_stage(smem[0], s0, off.zshift);
     __syncthreads();
   }
 
+  if (gridDim.y > 1) {
+    // split K: this slice's float sums, reduced (and scaled) by a second kernel
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t nb = cb0 + wn * 4 + u;
+          if (nb < NB)
+            a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + nb * 16 + r16] = accf[i][u][r];
+        }
+      }
+    return;
+  }
   if (!a.y) return;
   // all row scales first (one wait), then the stores
   float sam[4][4];
@@ -244,13 +263,24 @@ prefill_kernel(GemmArgs a) {
 
 }  // namespace
 
+// Split K only while the output tiles leave compute units idle, keeping at
+// least two groups per slice.
+int prefill_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N / kBlockCols + NCB - 1) / NCB);
+  const int64_t G = K / kGroup, cus = device_cus();
+  int ks = 1;
+  while (tiles * ks * 2 <= cus && G >= (int64_t)ks * 2 * 2) ks *= 2;
+  return ks;
+}
+
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
   const int64_t NB = a.N / kBlockCols;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((NB + NCB - 1) / NCB);
+  const dim3 grid((unsigned)tiles, (unsigned)a.ksplit);
   if (a.partials)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -97,6 +97,7 @@ int device_cus();  // compute units of the current device (cached)
 GemvShape gemv_shape(int64_t N, int64_t K);
 bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s);
 int skinny_ksplit(int64_t M, int64_t N, int64_t K);
+int prefill_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st);
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
