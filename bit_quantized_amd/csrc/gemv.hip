@@ -84,7 +84,9 @@ __device__ __forceinline__ int split_point(unsigned total, unsigned parts, unsig
   return (int)(q * i + (r * i) / parts);
 }
 
+template <bool KSPLIT>
 __device__ __forceinline__ int64_t unit_block(int u, int nb0, int G, int g0, int gk) {
+  if constexpr (!KSPLIT) return (int64_t)nb0 * G + u;  // whole blocks: the run is contiguous
   return (int64_t)(nb0 + u / gk) * G + g0 + u % gk;
 }
 
@@ -135,7 +137,7 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
   }
 }
 
-template <int XT, bool DEBUG>
+template <int XT, bool DEBUG, bool KSPLIT>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -151,54 +153,72 @@ gemv_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int c = lane & 15, j = lane >> 4;
-  // This workgroup: channel blocks [nb0, nb1) x groups [g0, g1).
-  const int nb0 = split_point(NB, gridDim.x, blockIdx.x);
-  const int nb1 = split_point(NB, gridDim.x, blockIdx.x + 1);
-  const int g0 = split_point(G, gridDim.y, blockIdx.y);
-  const int g1 = split_point(G, gridDim.y, blockIdx.y + 1);
-  const int gk = g1 - g0, units = (nb1 - nb0) * gk;
+  // This workgroup: channel blocks [nb0, nb1) x groups [g0, g0 + gk).  The
+  // host passes NB = cb_q * gridDim.x + cb_r, so no division is needed here;
+  // everything up to the first loads is kept short, because those loads
+  // start the memory pipe.
+  const int bx = blockIdx.x;
+  const int nb0 = bx * a.cb_q + min(bx, a.cb_r);
+  const int nb1 = nb0 + a.cb_q + (bx < a.cb_r ? 1 : 0);
+  int g0 = 0, gk = G;
+  if constexpr (KSPLIT) {
+    g0 = split_point(G, gridDim.y, blockIdx.y);
+    gk = split_point(G, gridDim.y, blockIdx.y + 1) - g0;
+  }
+  const int units = (nb1 - nb0) * gk;
   const int u0 = units * share_prefix(wave) / kShareTotal;
   const int u1 = units * share_prefix(wave + 1) / kShareTotal;
   const int nrun = u1 - u0;
+
+  // the run's metadata: scales (lane l: unit l/4, channels 4(l%4)..+3) and
+  // zero blocks (lane l: unit l), clamped to the run's last unit
+  const int last = nrun > 0 ? nrun - 1 : 0;
+  const int64_t bs = unit_block<KSPLIT>(u0 + min(lane >> 2, last), nb0, G, g0, gk);
+  const int64_t bz = unit_block<KSPLIT>(u0 + min(lane & 15, last), nb0, G, g0, gk);
+  const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
+  // the run's blocks: [first, first + span) of the codes plane
+  const int64_t first = unit_block<KSPLIT>(u0, nb0, G, g0, gk);
+  const int span = nrun > 0 ? (int)(unit_block<KSPLIT>(u1 - 1, nb0, G, g0, gk) - first + 1) : 0;
+  const int oob = span * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w.codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
+      kBufferWord3);
+  uint4 wv[D];
+  int lu = u0, lg = 0, rel = 0;  // next unit to load (lg: its group within the slice)
+  if constexpr (KSPLIT) lg = nrun > 0 ? u0 % gk : 0;
+  uint4 s4;
+  uint2 z2;
+  float scale;
+  const int nch = K / 8;
+  constexpr int RW = XT == X_F32 ? 2 : 1;
+  constexpr int kQThreads = 64 * kQ;
+  uint4 xr[kQChunks][RW];
+
+  // first loads: every wavefront's run metadata (two small loads), then the
+  // quantisers' token chunks and the streamers' first D code blocks
+  s4 = *reinterpret_cast<const uint4*>(hot_s);
+  z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
+  if (wave < kQ) {
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(a, min(i * kQThreads + tid, nch - 1), xr[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
 
   for (int t = tid; t < kMaxCb * kWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
   for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
   if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
 
-  // the run's metadata: scales (lane l: unit l/4, channels 4(l%4)..+3) and
-  // zero blocks (lane l: unit l), clamped to the run's last unit
-  const int last = nrun > 0 ? nrun - 1 : 0;
-  const int64_t bs = unit_block(u0 + min(lane >> 2, last), nb0, G, g0, gk);
-  const int64_t bz = unit_block(u0 + min(lane & 15, last), nb0, G, g0, gk);
-  const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
-  // the run's blocks: [first, first + span) of the codes plane
-  const int64_t first = unit_block(u0, nb0, G, g0, gk);
-  const int span = nrun > 0 ? (int)(unit_block(u1 - 1, nb0, G, g0, gk) - first + 1) : 0;
-  const int oob = span * kBlockBytes;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.w.codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
-      kBufferWord3);
-  uint4 wv[D];
-  int lu = u0, lg = nrun > 0 ? u0 % gk : 0, rel = 0;  // next unit to load
-  uint4 s4;
-  uint2 z2;
-  float scale;
-
   if (wave < kQ) {
     // ---- quantiser: token chunks (8 elements) qt, qt + 256, ... in batches
-    // of kQChunks; the last batch stays in registers for the second pass
+    // of kQChunks (the first batch is in flight already); the last batch
+    // stays in registers for the second pass
     const int qt = tid;                                         // 0 .. 64 kQ - 1
-    constexpr int kQThreads = 64 * kQ;
-    const int nch = K / 8;
     const int nbatch = (nch + kQChunks * kQThreads - 1) / (kQChunks * kQThreads);
-    constexpr int RW = XT == X_F32 ? 2 : 1;
-    uint4 xr[kQChunks][RW];
     float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(a, min(i * kQThreads + qt, nch - 1), xr[i]);
-    s4 = *reinterpret_cast<const uint4*>(hot_s);
-    z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
     for (int b = 0; b < nbatch; ++b) {
       if (b > 0) {
 #pragma unroll
@@ -272,13 +292,7 @@ gemv_kernel(GemmArgs a) {
     for (int i = 0; i < D; ++i)
       load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   } else {
-    // ---- streamer: metadata and D code blocks in flight, then the flag
-    s4 = *reinterpret_cast<const uint4*>(hot_s);
-    z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
-#pragma unroll
-    for (int i = 0; i < D; ++i)
-      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
-    __builtin_amdgcn_sched_barrier(0);  // every load above issues before the wait
+    // ---- streamer: metadata and D code blocks are in flight; the flag
     if constexpr (XT == X_QUANTISED) scale = a.sa[0];
     while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
            (unsigned)kQ)
@@ -362,16 +376,24 @@ gemv_kernel(GemmArgs a) {
   }
 }
 
-template <int XT>
-hipError_t launch_xt(const GemmArgs& a, hipStream_t st) {
+template <int XT, bool KSPLIT>
+hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (size_t)a.K + 16 * (size_t)G;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, true>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT>), grid, dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, false>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int XT>
+hipError_t launch_xt(GemmArgs a, hipStream_t st) {
+  const int NB = (int)(a.N / kBlockCols);
+  a.cb_q = NB / a.cb;  // workgroup b holds cb_q blocks, plus one if b < cb_r
+  a.cb_r = NB % a.cb;
+  return a.ksplit > 1 ? launch_ks<XT, true>(a, st) : launch_ks<XT, false>(a, st);
 }
 
 }  // namespace

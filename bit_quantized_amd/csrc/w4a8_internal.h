@@ -82,6 +82,7 @@ struct GemmArgs {
   float* sa_ws;           // fused quant + split-K: the scale, for the reduction
   int ksplit;
   int cb, ks;             // GEMV: workgroups along N, wavefronts per workgroup
+  int cb_q, cb_r;         // GEMV: N/16 = cb_q * cb + cb_r (set by the launcher)
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
