@@ -403,3 +403,33 @@ def test_sibling_linear(w4, M):
         ref = oracle.linear(qa_ref, sa_ref, q, z, s)
         ok, err, bound = oracle.tolerance_ok(to_f32(y), ref, REL)
         assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+
+
+@pytest.mark.parametrize("amax", [127.0, 63.5])
+def test_fused_gemv_ties(w4, amax):
+    """A token whose x / sa are exact half-integers (sa = amax / 127 = 1 or
+    0.5): the fused GEMV's in-kernel codes must round ties to even exactly as
+    w4a8_quant_act does, so both paths give the same output bit for bit, and
+    that output matches the oracle."""
+    say(f"fused ties amax={amax}")
+    K, N = 3584, 512
+    sa = amax / 127.0
+    rng = np.random.Generator(np.random.PCG64(21))
+    k = rng.integers(-127, 127, size=K)                  # k + 0.5 in [-126.5, 126.5]
+    x = ((k + 0.5) * sa).astype(np.float32)
+    x[17] = amax                                          # the row's absmax
+    x = x[None, :]
+    xb = synth.bf16_round_bits(x)
+    assert np.array_equal(synth.bf16_bits_to_f32(xb), x)  # exact in bf16
+    q, z, s = synth.draw_weights(rng, N, K)
+    W = w4.pack_weights(dev(q), dev(z), dev(s))
+    xt = dev(xb.view(np.int16)).view(torch.bfloat16)
+    y_fused = w4.linear(xt, W)
+    qa, sa_t = w4.quant_act(xt)
+    y_two = w4.gemm(qa, sa_t, W)
+    assert torch.equal(y_fused, y_two)
+    qa_ref, sa_ref = oracle.quant_act(x)
+    assert np.array_equal(qa.cpu().numpy(), qa_ref) and float(sa_ref[0]) == sa
+    ref = oracle.linear(qa_ref, sa_ref, q, z, s)
+    ok, err, bound = oracle.tolerance_ok(to_f32(y_fused), ref, REL)
+    assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
