@@ -18,11 +18,6 @@ constexpr int kNontemporal = 2;           // cache policy bit: nt
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// Balanced split of [0, n) into `parts` contiguous slices.
-__device__ __forceinline__ int64_t slice_begin(int64_t n, int parts, int idx) {
-  return n * idx / parts;
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kBufferWord3);
@@ -72,10 +67,12 @@ skinny_kernel(GemmArgs a) {
   const int r16 = lane & 15, j = lane >> 4;
   const int64_t nb = blockIdx.x;
   const int64_t G = a.K / kGroup;
-  const int parts = a.ksplit * kWaves;
+  // this wavefront's slice of the groups: G = gq * (ksplit * 16) + gr, the
+  // first gr slices one group longer (quotient and remainder from the host,
+  // so no division delays the first loads)
   const int pidx = blockIdx.y * kWaves + wave;
-  const int gb = (int)slice_begin(G, parts, pidx);
-  const int nrun = (int)slice_begin(G, parts, pidx + 1) - gb;
+  const int gb = pidx * a.gq + min(pidx, a.gr);
+  const int nrun = a.gq + (pidx < a.gr ? 1 : 0);
   const int64_t blk0 = nb * G + gb;  // first unit of the run in the packed planes
 
   const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.w.codes + blk0 * kBlockBytes, (int64_t)nrun * kBlockBytes);
@@ -186,7 +183,10 @@ int pick_ksplit(int64_t N, int64_t K) {
 
 int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
+  const int64_t G = a.K / kGroup, parts = (int64_t)a.ksplit * kWaves;
+  a.gq = (int)(G / parts);
+  a.gr = (int)(G % parts);
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
   if (a.partials)
     hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(kThreads), 0, st, a);

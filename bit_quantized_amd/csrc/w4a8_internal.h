@@ -83,6 +83,7 @@ struct GemmArgs {
   int ksplit;
   int cb, ks;             // GEMV: workgroups along N, wavefronts per workgroup
   int cb_q, cb_r;         // GEMV: N/16 = cb_q * cb + cb_r (set by the launcher)
+  int gq, gr;             // skinny: G = gq * (ksplit * 16) + gr (set by the launcher)
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
@@ -100,7 +101,7 @@ bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s);
 int skinny_ksplit(int64_t M, int64_t N, int64_t K);
 int prefill_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t st);
+hipError_t launch_skinny(GemmArgs a, hipStream_t st);
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st);
