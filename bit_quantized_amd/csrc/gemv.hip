@@ -47,7 +47,6 @@ constexpr int kShareTotal = kQ * kQWeight + (kWaves - kQ) * 4;
 constexpr int D = 4;                        // code blocks a wavefront keeps in flight
 constexpr int kMaxRun = 12;                 // units per wavefront
 constexpr int kMaxCb = 12;                  // channel blocks per workgroup
-constexpr int kQChunks = 4;                 // token chunks a quantiser thread holds at once
 
 enum { X_BF16 = 0, X_F32 = 1, X_QUANTISED = 2 };
 
@@ -137,7 +136,9 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
   }
 }
 
-template <int XT, bool DEBUG, bool KSPLIT>
+// kQChunks: token chunks (8 elements) a quantiser thread holds at once; the
+// whole token fits in one batch when K / 8 <= 256 * kQChunks.
+template <int XT, bool DEBUG, bool KSPLIT, int kQChunks>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -376,16 +377,28 @@ gemv_kernel(GemmArgs a) {
   }
 }
 
-template <int XT, bool KSPLIT>
+template <int XT, bool KSPLIT, int QC>
 hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (size_t)a.K + 16 * (size_t)G;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+// Token chunks per quantiser thread: as few as hold the token in one batch
+// (fewer, shorter loads on the critical path); past 20480 inputs (float
+// tokens: past 8192) the token is quantised in batches of 4 chunks.
+template <int XT, bool KSPLIT>
+hipError_t launch_qc(const GemmArgs& a, hipStream_t st) {
+  const int64_t nch = a.K / 8, per = 64 * kQ;
+  if (nch <= 2 * per) return launch_ks<XT, KSPLIT, 2>(a, st);
+  if (nch <= 4 * per || XT == X_F32) return launch_ks<XT, KSPLIT, 4>(a, st);
+  if (nch <= 10 * per) return launch_ks<XT, KSPLIT, 10>(a, st);
+  return launch_ks<XT, KSPLIT, 4>(a, st);
 }
 
 template <int XT>
@@ -393,7 +406,7 @@ hipError_t launch_xt(GemmArgs a, hipStream_t st) {
   const int NB = (int)(a.N / kBlockCols);
   a.cb_q = NB / a.cb;  // workgroup b holds cb_q blocks, plus one if b < cb_r
   a.cb_r = NB % a.cb;
-  return a.ksplit > 1 ? launch_ks<XT, true>(a, st) : launch_ks<XT, false>(a, st);
+  return a.ksplit > 1 ? launch_qc<XT, true>(a, st) : launch_qc<XT, false>(a, st);
 }
 
 }  // namespace
