@@ -31,24 +31,15 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t 
   }
 }
 
-// One unit (16-channel block x one group) of a wavefront's run, as loaded.
-struct Slot {
-  v4u w;        // packed codes of this lane
-  v4i a0, a1;   // activation row r16, input channels 16j.. and 64+16j.. of the group
-  float s;      // scale of channel r16
-  uint32_t zw;  // the zero block's dword holding channel r16's zero point
-};
-
 // ------------------------------------------------------------- 2 <= M <= 16
 //
 // One workgroup per 16-channel block (and K slice when the blocks alone
 // cannot fill the machine); its 16 wavefronts split the slice's groups into
-// contiguous runs and stream them through a ring of D register slots, as the
-// GEMV does.  Every operand is read through a buffer descriptor bounded to
-// what exists (the run's codes, scales and zeros; the M activation rows), so
-// rows >= M and units past a run read as zeros with no memory request and
-// every wavefront issues the same, compile-time count of loads (exact waits,
-// no branches around loads).
+// contiguous runs and walk them four units (16 channels x one group) at a
+// time.  Every operand is read through a buffer descriptor bounded to what
+// exists (the run's codes, scales and zeros; the M activation rows), so
+// units past a run read as zeros with no memory request and the compute
+// needs no branch.
 //
 // Per unit: one v_mfma_i32_16x16x64_i8 pair.  A is the activation tile, B
 // the unpacked q - z bytes.  Lane l supplies A row l%16 and B column l%16
@@ -58,9 +49,35 @@ struct Slot {
 // cross-lane work.  Result layout: lane l holds column l%16, rows
 // 4*(l/16) .. 4*(l/16)+3.  The wavefronts' pieces are summed in LDS in fixed
 // wavefront order.
-template <bool DEBUG>
+//
+// The cost of this kernel is its count of memory instructions more than its
+// bytes, so each kind of operand is fetched with as few as its size allows
+// and moved to the lanes that need it with ds_bpermute:
+//   codes        one 1 KiB load per unit;
+//   activations  coalesced row segments of the row-major int8 matrix: for
+//                MP = 2, 4, 8 (M rounded up to a power of two) one load
+//                holds MP rows x 1024/MP bytes, i.e. 8/MP units; for MP = 16
+//                one load holds the 16 rows x 64 bytes of one unit-half;
+//   scales       one load per four units (lane 16i+c: unit i, channel c);
+//   zeros        one load per four units (lanes 0..7: the four 8-byte blocks).
+// Loads are issued four units ahead (the next quad's per-quad operands
+// first, then each unit's own as its slot frees), and the last quad issues
+// nothing, so no load is made for a unit that a wavefront never computes
+// beyond the at most three that pad its last quad.
+template <int MP>
+struct ActShape {
+  static constexpr int kUnitsPerLoad = MP >= 8 ? 1 : 8 / MP;     // units one load covers
+  static constexpr int kSlotLoads = MP == 16 ? 2 : (MP == 8 ? 1 : 0);  // loads per unit slot
+  static constexpr int kQuadLoads = MP >= 8 ? 0 : 4 / kUnitsPerLoad;   // loads per quad
+  static constexpr int kLanesPerRow = MP == 16 ? 4 : 64 / MP;
+};
+
+template <bool DEBUG, int MP>
 __global__ void __launch_bounds__(kThreads)
 skinny_kernel(GemmArgs a) {
+  using S = ActShape<MP>;
+  constexpr int QL = S::kQuadLoads > 0 ? S::kQuadLoads : 1;
+  constexpr int SL = S::kSlotLoads > 0 ? S::kSlotLoads : 1;
   __shared__ float red[kWaves][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -73,84 +90,139 @@ skinny_kernel(GemmArgs a) {
   const int pidx = blockIdx.y * kWaves + wave;
   const int gb = pidx * a.gq + min(pidx, a.gr);
   const int nrun = a.gq + (pidx < a.gr ? 1 : 0);
+  const int nq = (nrun + 3) >> 2;
   const int64_t blk0 = nb * G + gb;  // first unit of the run in the packed planes
 
   const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.w.codes + blk0 * kBlockBytes, (int64_t)nrun * kBlockBytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.w.scales + blk0 * 16, (int64_t)nrun * 64);
   const __amdgpu_buffer_rsrc_t rz = rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.qa, a.M * a.K);
-  const int oob = 0x7FFFFFF0;                       // beyond every descriptor
-  const int act_lane = r16 < a.M ? r16 * (int)a.K + 16 * j : oob;
+  const int oob = 0x7FFFFFF0;  // beyond every descriptor
 
-  auto load = [&](int r, Slot& sl) __attribute__((always_inline)) {
-    const bool live = r < nrun;  // wave-uniform
-    const int g = gb + r;
-    const v4u w = __builtin_amdgcn_raw_buffer_load_b128(rc, live ? r * kBlockBytes + 16 * lane : oob, 0,
-                                                        kNontemporal);
-    const int ao = live && act_lane != oob ? act_lane + g * kGroup : oob;
-    sl.w = w;
-    sl.a0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, ao, 0, 0));
-    sl.a1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                        ra, ao == oob ? oob : ao + 64, 0, 0));
-    sl.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         rs, live ? r * 64 + 4 * r16 : oob, 0, 0));
-    sl.zw = __builtin_amdgcn_raw_buffer_load_b32(rz, live ? r * kZeroBlockBytes + (r16 >> 3) * 4 : oob,
-                                                 0, 0);
+  // activation row segment this lane fetches (row >= M: none)
+  const int arow = lane / S::kLanesPerRow, aseg = lane % S::kLanesPerRow;
+  const int act_base = arow < a.M ? arow * (int)a.K + gb * kGroup + 16 * aseg : oob;
+  const int z_base = lane < 8 ? 4 * lane : oob;
+
+  auto act_off = [&](int u) __attribute__((always_inline)) {  // unit u of the run, first byte
+    return act_base == oob ? oob : act_base + u * kGroup;
+  };
+  // per-quad operands of quad q: scales, zeros, and (MP <= 4) the activations
+  auto load_quad = [&](int q, uint32_t& s, uint32_t& z, v4i* act) __attribute__((always_inline)) {
+    s = __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * q + j) * 64 + 4 * r16, 0, 0);
+    z = __builtin_amdgcn_raw_buffer_load_b32(rz, z_base == oob ? oob : 4 * q * kZeroBlockBytes + z_base, 0, 0);
+    if constexpr (S::kQuadLoads > 0) {
+#pragma unroll
+      for (int n = 0; n < S::kQuadLoads; ++n)
+        act[n] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ra, act_off(4 * q + n * S::kUnitsPerLoad), 0, 0));
+    }
+  };
+  // per-unit operands of unit u: codes and (MP >= 8) the activations
+  auto load_unit = [&](int u, v4u& w, v4i* act) __attribute__((always_inline)) {
+    if constexpr (S::kSlotLoads > 0) {
+#pragma unroll
+      for (int h = 0; h < S::kSlotLoads; ++h)
+        act[h] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ra, act_off(u) == oob ? oob : act_off(u) + 64 * h, 0, 0));
+    }
+    w = __builtin_amdgcn_raw_buffer_load_b128(rc, u * kBlockBytes + 16 * lane, 0, kNontemporal);
   };
 
+  // ds_bpermute byte addresses: source lane of this lane's A operand for
+  // (unit-in-load du, half h) is base + 8 du + 4 h (MP <= 8) or 4 r + j
+  // (MP == 16, one load per half)
+  const int perm_a = MP == 16 ? 4 * (4 * r16 + j) : 4 * (S::kLanesPerRow * (r16 % MP) + j);
+  const int perm_s = 4 * r16;              // + 64 i: scale of unit i, channel r16
+  const int perm_z = 4 * (r16 >> 3);       // + 8 i: zero dword of unit i holding channel r16
+  const int zshift = (r16 & 7) * 4;        // nibble of channel r16 in that dword
+
   float accf[4] = {0.f, 0.f, 0.f, 0.f};
-  Slot ring[D];
+  v4u wr[4];                 // codes ring, one slot per unit of the quad
+  v4i ar[4][SL];             // per-unit activations (MP >= 8)
+  v4i aq[2][QL];             // per-quad activations (MP <= 4), current and next quad
+  uint32_t sq[2], zq[2];     // per-quad scales and zeros, current and next quad
+
+  auto compute = [&](int q, int i, const v4u& w, const v4i* au, const v4i* aqc, uint32_t sc,
+                     uint32_t zc) __attribute__((always_inline)) {
+    v4i a0, a1;
+    if constexpr (MP == 16) {
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    load(i, ring[i]);
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = __builtin_amdgcn_ds_bpermute(perm_a, au[0][t]);
+        a1[t] = __builtin_amdgcn_ds_bpermute(perm_a, au[1][t]);
+      }
+    } else {
+      const int n = i / S::kUnitsPerLoad, du = i % S::kUnitsPerLoad;
+      const v4i& src = MP == 8 ? au[0] : aqc[n];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a0[t] = __builtin_amdgcn_ds_bpermute(perm_a + 32 * du, src[t]);
+        a1[t] = __builtin_amdgcn_ds_bpermute(perm_a + 32 * du + 16, src[t]);
+      }
+    }
+    const float s = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_s + 64 * i, (int)sc));
+    const uint32_t zw = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_z + 8 * i, (int)zc);
+    const uint32_t zz = ((zw >> zshift) & 0xFu) * 0x01010101u;
+    v4i b0, b1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t d = w[t];
+      b0[t] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
+      b1[t] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
+    }
+    v4i acc = {0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
+    const int r = 4 * q + i;
+    if (DEBUG && a.partials && r < nrun) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t m = 4 * j + t;
+        if (m < a.M && m >= a.m_begin && m < a.m_end)
+          a.partials[((m - a.m_begin) * a.N + 16 * nb + r16) * G + (gb + r)] = acc[t];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) accf[t] += s * (float)acc[t];
+  };
+
+  load_quad(0, sq[0], zq[0], aq[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    load_unit(i, wr[i], ar[i]);
     __builtin_amdgcn_sched_barrier(0);  // slot order = issue order, so waits stay exact
   }
-  const int zshift = (r16 & 7) * 4;  // nibble of channel r16 in its dword
-  for (int ub = 0; ub < nrun; ub += D) {
+  int q = 0;
+  for (; q < nq - 1; ++q) {
+    load_quad(q + 1, sq[1], zq[1], aq[1]);  // next quad's shared operands first
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      // a slot past the run holds zeros (codes, zero point, activations and
-      // scale all read as 0), so computing it adds exactly nothing: no branch
-      const int r = ub + i;
-      {
-        const Slot& sl = ring[i];
-        const uint32_t zz = ((sl.zw >> zshift) & 0xFu) * 0x01010101u;
-        v4i b0, b1;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t d = sl.w[w];
-          b0[w] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
-          b1[w] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
-        }
-        v4i acc = {0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(sl.a0, b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(sl.a1, b1, acc, 0, 0, 0);
-        if (DEBUG && a.partials && r < nrun) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t m = 4 * j + q;
-            if (m < a.M && m >= a.m_begin && m < a.m_end)
-              a.partials[((m - a.m_begin) * a.N + 16 * nb + r16) * G + (gb + r)] = acc[q];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) accf[q] += sl.s * (float)acc[q];
-      }
-      load(r + D, ring[i]);  // refill with the unit D ahead (zeros past the run)
-      __builtin_amdgcn_sched_barrier(0);  // keep the ring order: refill before the next slot
+    for (int i = 0; i < 4; ++i) {
+      compute(q, i, wr[i], ar[i], aq[0], sq[0], zq[0]);
+      load_unit(4 * (q + 1) + i, wr[i], ar[i]);  // refill the slot with the next quad's unit
+      __builtin_amdgcn_sched_barrier(0);
     }
+    sq[0] = sq[1];
+    zq[0] = zq[1];
+#pragma unroll
+    for (int n = 0; n < QL; ++n) aq[0][n] = aq[1][n];
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) red[wave][q][lane] = accf[q];
+  for (int i = 0; i < 4; ++i) compute(q, i, wr[i], ar[i], aq[0], sq[0], zq[0]);
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t) red[wave][t][lane] = accf[t];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float t = red[0][q][lane];
+    for (int t = 0; t < 4; ++t) {
+      float v = red[0][t][lane];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) t += red[w][q][lane];
-      const int64_t m = 4 * j + q;
-      if (m < a.M) store_out(a, m, 16 * nb + r16, t);
+      for (int w = 1; w < kWaves; ++w) v += red[w][t][lane];
+      const int64_t m = 4 * j + t;
+      if (m < a.M) store_out(a, m, 16 * nb + r16, v);
     }
   }
 }
@@ -183,15 +255,27 @@ int pick_ksplit(int64_t N, int64_t K) {
 
 int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 
+template <int MP>
+void launch_mp(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  if (a.partials)
+    hipLaunchKernelGGL((skinny_kernel<true, MP>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((skinny_kernel<false, MP>), grid, dim3(kThreads), 0, st, a);
+}
+
 hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
   const int64_t G = a.K / kGroup, parts = (int64_t)a.ksplit * kWaves;
   a.gq = (int)(G / parts);
   a.gr = (int)(G % parts);
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
-  if (a.partials)
-    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  if (a.M <= 2)
+    launch_mp<2>(a, grid, st);
+  else if (a.M <= 4)
+    launch_mp<4>(a, grid, st);
+  else if (a.M <= 8)
+    launch_mp<8>(a, grid, st);
   else
-    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(kThreads), 0, st, a);
+    launch_mp<16>(a, grid, st);
   return hipGetLastError();
 }
 

@@ -46,6 +46,35 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Codes of eight activations under one row scale (the same rule everywhere).
+__device__ __forceinline__ uint2 quant8(const float* v, float amax, float scale) {
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float r = 0.0f;
+    if (amax != 0.0f) {
+      r = rintf(v[i] / scale);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+    }
+    const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+    packed[i >> 2] |= b << (8 * (i & 3));
+  }
+  return make_uint2(packed[0], packed[1]);
+}
+
+// Row maximum over the block's wavefronts (all threads get it).
+template <int THREADS>
+__device__ __forceinline__ float block_max(float amax, float* red) {
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int w = 1; w < THREADS / 64; ++w) amax = fmaxf(amax, red[w]);
+  return amax;
+}
+
+// Long rows: the row is read twice (maximum, then codes) in a strided loop.
 template <typename T>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
@@ -62,13 +91,7 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
-  amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
-  amax = red[0];
-#pragma unroll
-  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
-
+  amax = block_max<kQuantThreads>(amax, red);
   const float scale = amax / 127.0f;
   if (threadIdx.x == 0) sa[m] = scale;
 
@@ -76,32 +99,76 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   for (int64_t ch = threadIdx.x; ch < chunks; ch += kQuantThreads) {
     float v[8];
     Chunk8<T>::load(row + ch * 8, v);
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float r = 0.0f;
-      if (amax != 0.0f) {
-        r = rintf(v[i] / scale);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-      }
-      const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
-      packed[i >> 2] |= b << (8 * (i & 3));
-    }
-    *reinterpret_cast<uint2*>(out + ch * 8) = make_uint2(packed[0], packed[1]);
+    *reinterpret_cast<uint2*>(out + ch * 8) = quant8(v, amax, scale);
   }
+}
+
+// Rows of up to 8 * kRowThreads * NPT activations: every thread loads its NPT
+// chunks of eight at once and keeps them in registers, so the row is read
+// once and the block waits for memory once (the small-M case, where only M
+// blocks run and each one's latency is the whole cost).
+constexpr int kRowThreads = 1024;
+
+template <typename T, int NPT>
+__global__ void __launch_bounds__(kRowThreads)
+quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
+                 float* __restrict__ sa) {
+  __shared__ float red[kRowThreads / 64];
+  const int64_t m = blockIdx.x;
+  const T* row = x + m * K;
+  const int chunks = (int)(K / 8);
+  float v[NPT][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int ch = threadIdx.x + c * kRowThreads;
+    if (ch < chunks) {
+      Chunk8<T>::load(row + (int64_t)ch * 8, v[c]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NPT; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+  amax = block_max<kRowThreads>(amax, red);
+  const float scale = amax / 127.0f;
+  if (threadIdx.x == 0) sa[m] = scale;
+  int8_t* out = qa + m * K;
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) {
+    const int ch = threadIdx.x + c * kRowThreads;
+    if (ch < chunks) *reinterpret_cast<uint2*>(out + (int64_t)ch * 8) = quant8(v[c], amax, scale);
+  }
+}
+
+template <typename T>
+void launch_typed(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipStream_t st) {
+  const int64_t chunks = K / 8;
+  const dim3 grid((unsigned)M);
+  // many rows fill the machine by themselves; few rows want one round trip each
+  if (M > 64 || chunks > 8 * kRowThreads)
+    hipLaunchKernelGGL(quant_act_kernel<T>, grid, dim3(kQuantThreads), 0, st, x, K, qa, sa);
+  else if (chunks <= kRowThreads)
+    hipLaunchKernelGGL((quant_row_kernel<T, 1>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+  else if (chunks <= 2 * kRowThreads)
+    hipLaunchKernelGGL((quant_row_kernel<T, 2>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+  else if (chunks <= 4 * kRowThreads)
+    hipLaunchKernelGGL((quant_row_kernel<T, 4>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+  else
+    hipLaunchKernelGGL((quant_row_kernel<T, 8>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
 }
 
 }  // namespace
 
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
                         hipStream_t st) {
-  if (x_dtype == 0) {
-    hipLaunchKernelGGL(quant_act_kernel<uint16_t>, dim3((unsigned)M), dim3(kQuantThreads), 0, st,
-                       static_cast<const uint16_t*>(x), K, qa, sa);
-  } else {
-    hipLaunchKernelGGL(quant_act_kernel<float>, dim3((unsigned)M), dim3(kQuantThreads), 0, st,
-                       static_cast<const float*>(x), K, qa, sa);
-  }
+  if (x_dtype == 0)
+    launch_typed(static_cast<const uint16_t*>(x), M, K, qa, sa, st);
+  else
+    launch_typed(static_cast<const float*>(x), M, K, qa, sa, st);
   return hipGetLastError();
 }
 

@@ -113,6 +113,25 @@ def test_quant_bit_exact(w4, spec):
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
 
 
+# Row lengths on both sides of each register-resident variant's limit (1, 2,
+# 4 and 8 chunks of eight per thread of a 1024-thread block), the strided
+# two-pass kernel past them, and M on both sides of the few-rows limit.
+QUANT_EDGES = [(3, 8192, "bf16_outliers"), (2, 8320, "bf16_outliers"), (5, 16384, "f32"),
+               (5, 16512, "f32"), (4, 32896, "bf16_outliers"), (1, 65536, "bf16_outliers"),
+               (2, 65664, "f32"), (64, 1152, "bf16_outliers"), (65, 256, "bf16_outliers")]
+
+
+@pytest.mark.parametrize("M,K,act", QUANT_EDGES, ids=[f"M{m}_K{k}_{a[:4]}" for m, k, a in QUANT_EDGES])
+def test_quant_row_length_edges(w4, M, K, act):
+    say(f"quant edges M={M} K={K} {act}")
+    lin = synth.make_linear(synth.LinearSpec("qedge", M, K, 16, seed=M + K, act=act),
+                            with_weights=False)
+    qa, sa = w4.quant_act(x_tensor(lin))
+    qa_ref, sa_ref = oracle.quant_act(lin["x"])
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+
+
 def test_quant_ties_and_zero_rows(w4):
     say("quant ties")
     rows = []
