@@ -140,8 +140,9 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
                 "PREFILL path addresses activations and codes with 32-bit offsets "
                 "(M*K=%lld, N*K/2=%lld, limit %lld)",
                 (long long)(M * K), (long long)(N * K / 2), (long long)kPrefillMaxBytes);
-  if (fused && path != W4A8_PATH_GEMV)
-    return fail(W4A8_ERR_INVALID_ARG, "in-kernel quantisation runs on the GEMV path only");
+  if (fused && path != W4A8_PATH_GEMV &&
+      !(path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype) && !debug))
+    return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
       return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
@@ -355,10 +356,16 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (pick_path(M, K) == W4A8_PATH_GEMV)
     return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
                     W4A8_PATH_GEMV, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
-  // Two launches: quantise into the workspace, then the GEMM.
+  // The workspace is required at its documented size on every path, so a
+  // caller's sizing does not depend on which kernels run.
   const size_t need = linear_workspace(M, N, K);
   if (!workspace || workspace_bytes < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  // One launch when the skinny kernel can quantise these rows itself.
+  if (pick_path(M, K) == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, x_dtype))
+    return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
+                    W4A8_PATH_SKINNY, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
+  // Two launches: quantise into the workspace, then the GEMM.
   if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   const size_t xbytes = (size_t)M * K * (x_dtype == W4A8_F32 ? 4 : 2);
   if (overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, packed, packed_bytes_))

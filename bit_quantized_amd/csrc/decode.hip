@@ -72,18 +72,102 @@ struct ActShape {
   static constexpr int kLanesPerRow = MP == 16 ? 4 : 64 / MP;
 };
 
-template <bool DEBUG, int MP>
+// Raw activations of the fused-quantisation variant: NPT chunks of eight per
+// thread, kept in registers between the row maximum and the codes.
+template <typename T> struct XChunk {  // unused (int8 input): no raw activations
+  static constexpr int kLoads = 1;
+  static __device__ __forceinline__ float absmax(const v4u (*)[1], int) { return 0.0f; }
+};
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <> struct XChunk<uint16_t> {  // bfloat16 bits: one 16-byte load
+  static constexpr int kLoads = 1;
+  // max |x| of n chunks: the magnitudes of finite bfloat16 values order as
+  // their sign-cleared bit patterns, two per packed 16-bit maximum
+  static __device__ __forceinline__ float absmax(const v4u (*r)[1], int n) {
+    u16x2 m = {0, 0};
+    for (int c = 0; c < n; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, r[c][0][i] & 0x7FFF7FFFu));
+    return __uint_as_float((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
+  }
+  static __device__ __forceinline__ void widen(const v4u* r, float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(r[0][i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[0][i] & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct XChunk<float> {  // two 16-byte loads
+  static constexpr int kLoads = 2;
+  static __device__ __forceinline__ float absmax(const v4u (*r)[2], int n) {
+    float m = 0.0f;
+    for (int c = 0; c < n; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(__uint_as_float(r[c][i >> 2][i & 3])));
+    return m;
+  }
+  static __device__ __forceinline__ void widen(const v4u* r, float* v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(r[i >> 2][i & 3]);
+  }
+};
+
+// NPT == 0: activations are the caller's int8 codes (row-major [M][K]).
+// NPT > 0: the kernel quantises x (bf16 or f32, [M][K]) itself, with the
+// rule of the stand-alone quantiser (sa = absmax / 127 by IEEE division,
+// codes rint(x / sa) ties to even, clamped to +-127; a zero row gives sa 0
+// and codes 0), into LDS: every workgroup covers all of K, so each one sees
+// whole rows.  The row is split over 1024 / MP threads, each loading its NPT
+// chunks of eight before the first weight loads (so waiting for them leaves
+// the weight loads in flight); the wavefronts then read their A operands
+// from LDS (row stride K + 16 bytes, which keeps a 16-lane read on distinct
+// banks) instead of from memory.
+template <bool DEBUG, int MP, int NPT, typename T>
 __global__ void __launch_bounds__(kThreads)
 skinny_kernel(GemmArgs a) {
+  constexpr bool FUSED = NPT > 0;
   using S = ActShape<MP>;
-  constexpr int QL = S::kQuadLoads > 0 ? S::kQuadLoads : 1;
-  constexpr int SL = S::kSlotLoads > 0 ? S::kSlotLoads : 1;
+  constexpr int kQuadLoads = FUSED ? 0 : S::kQuadLoads;
+  constexpr int kSlotLoads = FUSED ? 0 : S::kSlotLoads;
+  constexpr int QL = kQuadLoads > 0 ? kQuadLoads : 1;
+  constexpr int SL = kSlotLoads > 0 ? kSlotLoads : 1;
   __shared__ float red[kWaves][4][64];
+  __shared__ float s_wmax[kWaves];
+  __shared__ float s_sa[16];
+  extern __shared__ __attribute__((aligned(16))) int8_t qs[];  // fused: [M][K + 16] codes
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, j = lane >> 4;
   const int64_t nb = blockIdx.x;
   const int64_t G = a.K / kGroup;
+  const int rstride = (int)a.K + 16;  // fused: LDS row stride of the codes
+
+  // fused: this thread's row and chunks of eight, loaded before anything else
+  constexpr int XL = FUSED ? XChunk<T>::kLoads : 1;
+  constexpr int NX = FUSED ? NPT : 1;
+  constexpr int kRowThreads = kThreads / MP;
+  const int xrow = threadIdx.x / kRowThreads, xt = threadIdx.x % kRowThreads;
+  const int cpr = (int)(a.K / 8);  // chunks per row
+  // chunks xt, xt + 1024/MP, ... of row xrow: the first nx of them exist
+  const int nx = xrow < a.M && xt < cpr ? (cpr - xt + kRowThreads - 1) / kRowThreads : 0;
+  v4u xr[NX][XL];
+  if constexpr (FUSED) {
+    const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, a.M * a.K * (int64_t)sizeof(T));
+    const int oob = 0x7FFFFFF0;
+    const int off0 = (xrow * (int)a.K + 8 * xt) * (int)sizeof(T);
+#pragma unroll
+    for (int c = 0; c < NPT; ++c) {
+      const int off = c < nx ? off0 + c * 8 * kRowThreads * (int)sizeof(T) : oob;
+#pragma unroll
+      for (int l = 0; l < XL; ++l)
+        xr[c][l] = __builtin_amdgcn_raw_buffer_load_b128(rx, off == oob ? oob : off + 16 * l, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // this wavefront's slice of the groups: G = gq * (ksplit * 16) + gr, the
   // first gr slices one group longer (quotient and remainder from the host,
   // so no division delays the first loads)
@@ -96,13 +180,16 @@ skinny_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.w.codes + blk0 * kBlockBytes, (int64_t)nrun * kBlockBytes);
   const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.w.scales + blk0 * 16, (int64_t)nrun * 64);
   const __amdgpu_buffer_rsrc_t rz = rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
-  const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.qa, a.M * a.K);
+  const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.qa, FUSED ? 0 : a.M * a.K);
   const int oob = 0x7FFFFFF0;  // beyond every descriptor
 
   // activation row segment this lane fetches (row >= M: none)
   const int arow = lane / S::kLanesPerRow, aseg = lane % S::kLanesPerRow;
   const int act_base = arow < a.M ? arow * (int)a.K + gb * kGroup + 16 * aseg : oob;
   const int z_base = lane < 8 ? 4 * lane : oob;
+  // fused: LDS byte offset of this lane's A operand for unit 0 of the run
+  // (rows >= M read row M-1; their products are never stored)
+  const int lds_a = min(r16, (int)a.M - 1) * rstride + gb * kGroup + 16 * j;
 
   auto act_off = [&](int u) __attribute__((always_inline)) {  // unit u of the run, first byte
     return act_base == oob ? oob : act_base + u * kGroup;
@@ -111,18 +198,18 @@ skinny_kernel(GemmArgs a) {
   auto load_quad = [&](int q, uint32_t& s, uint32_t& z, v4i* act) __attribute__((always_inline)) {
     s = __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * q + j) * 64 + 4 * r16, 0, 0);
     z = __builtin_amdgcn_raw_buffer_load_b32(rz, z_base == oob ? oob : 4 * q * kZeroBlockBytes + z_base, 0, 0);
-    if constexpr (S::kQuadLoads > 0) {
+    if constexpr (kQuadLoads > 0) {
 #pragma unroll
-      for (int n = 0; n < S::kQuadLoads; ++n)
+      for (int n = 0; n < kQuadLoads; ++n)
         act[n] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                              ra, act_off(4 * q + n * S::kUnitsPerLoad), 0, 0));
     }
   };
   // per-unit operands of unit u: codes and (MP >= 8) the activations
   auto load_unit = [&](int u, v4u& w, v4i* act) __attribute__((always_inline)) {
-    if constexpr (S::kSlotLoads > 0) {
+    if constexpr (kSlotLoads > 0) {
 #pragma unroll
-      for (int h = 0; h < S::kSlotLoads; ++h)
+      for (int h = 0; h < kSlotLoads; ++h)
         act[h] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                              ra, act_off(u) == oob ? oob : act_off(u) + 64 * h, 0, 0));
     }
@@ -146,7 +233,11 @@ skinny_kernel(GemmArgs a) {
   auto compute = [&](int q, int i, const v4u& w, const v4i* au, const v4i* aqc, uint32_t sc,
                      uint32_t zc) __attribute__((always_inline)) {
     v4i a0, a1;
-    if constexpr (MP == 16) {
+    if constexpr (FUSED) {
+      const int off = lds_a + (4 * q + i) * kGroup;
+      a0 = *reinterpret_cast<const v4i*>(qs + off);
+      a1 = *reinterpret_cast<const v4i*>(qs + off + 64);
+    } else if constexpr (MP == 16) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         a0[t] = __builtin_amdgcn_ds_bpermute(perm_a, au[0][t]);
@@ -187,12 +278,48 @@ skinny_kernel(GemmArgs a) {
     for (int t = 0; t < 4; ++t) accf[t] += s * (float)acc[t];
   };
 
-  load_quad(0, sq[0], zq[0], aq[0]);
-  __builtin_amdgcn_sched_barrier(0);
+  // the first quad's loads (fused: after every wavefront has its
+  // activations, which would otherwise queue behind these weight reads)
+  auto load_first = [&]() __attribute__((always_inline)) {
+    load_quad(0, sq[0], zq[0], aq[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    load_unit(i, wr[i], ar[i]);
-    __builtin_amdgcn_sched_barrier(0);  // slot order = issue order, so waits stay exact
+    for (int i = 0; i < 4; ++i) {
+      load_unit(i, wr[i], ar[i]);
+      __builtin_amdgcn_sched_barrier(0);  // slot order = issue order, so waits stay exact
+    }
+  };
+  if constexpr (!FUSED) load_first();
+  if constexpr (FUSED) {
+    // row maximum: this thread's chunks, its wavefront (one row per
+    // wavefront, as a row spans 1024 / MP >= 64 threads), then the row's
+    // wavefronts through LDS
+    // (the raw chunks stay packed in registers; they are widened twice)
+    float amax = XChunk<T>::absmax(xr, NPT);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (lane == 0) s_wmax[wave] = amax;
+    __syncthreads();
+    load_first();
+    constexpr int kRowWaves = kRowThreads / 64;
+    amax = s_wmax[xrow * kRowWaves];
+#pragma unroll
+    for (int w = 1; w < kRowWaves; ++w) amax = fmaxf(amax, s_wmax[xrow * kRowWaves + w]);
+    const float scale = amax / 127.0f;
+    const float inv = 1.0f / scale;
+    if (xt == 0 && xrow < a.M) s_sa[xrow] = scale;
+    int8_t* qrow = qs + xrow * rstride + 8 * xt;
+#pragma unroll
+    for (int c = 0; c < NPT; ++c) {
+      if (c < nx) {
+        float v[8];
+        XChunk<T>::widen(xr[c], v);
+        // a zero row gives codes 0 (its quotients would be 0/0)
+        const uint2 codes = amax != 0.0f ? quant8_codes(v, scale, inv) : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(qrow + c * 8 * kRowThreads) = codes;
+      }
+    }
+    __syncthreads();
   }
   int q = 0;
   for (; q < nq - 1; ++q) {
@@ -222,7 +349,12 @@ skinny_kernel(GemmArgs a) {
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) v += red[w][t][lane];
       const int64_t m = 4 * j + t;
-      if (m < a.M) store_out(a, m, 16 * nb + r16, v);
+      if (m < a.M) {
+        if constexpr (FUSED)
+          a.y[m * a.N + 16 * nb + r16] = f32_to_bf16_rne(s_sa[m] * v);
+        else
+          store_out(a, m, 16 * nb + r16, v);
+      }
     }
   }
 }
@@ -251,31 +383,85 @@ int pick_ksplit(int64_t N, int64_t K) {
   return ks;
 }
 
-}  // namespace
-
-int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
-
 template <int MP>
 void launch_mp(const GemmArgs& a, dim3 grid, hipStream_t st) {
   if (a.partials)
-    hipLaunchKernelGGL((skinny_kernel<true, MP>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((skinny_kernel<false, MP>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t>), grid, dim3(kThreads), 0, st, a);
 }
+
+// Chunks of eight activations per thread of the fused variant, or 0 when it
+// does not apply: one workgroup per channel block covering all of K, the
+// M x (K + 16) codes within the LDS budget, and the thread's share of the
+// row within the register budget.
+constexpr int64_t kFusedLdsBytes = 128 * 1024;
+
+int pow2_rows(int64_t M) { return M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
+int fused_chunks(int64_t M, int64_t N, int64_t K, int x_dtype) {
+  if (M < 2 || M > 16 || pick_ksplit(N, K) != 1) return 0;
+  if (M * (K + 16) + 512 > kFusedLdsBytes) return 0;
+  const int64_t per_thread = (K / 8 + kThreads / pow2_rows(M) - 1) / (kThreads / pow2_rows(M));
+  const int64_t limit = x_dtype == 0 ? 10 : 4;
+  if (per_thread > limit) return 0;
+  return per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : 10;
+}
+
+template <int MP, typename T>
+void launch_fused_mp(const GemmArgs& a, dim3 grid, int npt, hipStream_t st) {
+  const size_t lds = (size_t)(a.M * (a.K + 16) + 512);
+  if (npt == 4)
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 4, T>), grid, dim3(kThreads), lds, st, a);
+  else if constexpr (sizeof(T) == 2) {
+    if (npt == 8)
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 8, T>), grid, dim3(kThreads), lds, st, a);
+    else
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 10, T>), grid, dim3(kThreads), lds, st, a);
+  }
+}
+
+template <typename T>
+void launch_fused(const GemmArgs& a, dim3 grid, int npt, hipStream_t st) {
+  if (a.M <= 2)
+    launch_fused_mp<2, T>(a, grid, npt, st);
+  else if (a.M <= 4)
+    launch_fused_mp<4, T>(a, grid, npt, st);
+  else if (a.M <= 8)
+    launch_fused_mp<8, T>(a, grid, npt, st);
+  else
+    launch_fused_mp<16, T>(a, grid, npt, st);
+}
+
+}  // namespace
+
+bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype) {
+  return fused_chunks(M, N, K, x_dtype) > 0;
+}
+
+int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 
 hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
   const int64_t G = a.K / kGroup, parts = (int64_t)a.ksplit * kWaves;
   a.gq = (int)(G / parts);
   a.gr = (int)(G % parts);
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
-  if (a.M <= 2)
+  if (a.x) {
+    const int npt = fused_chunks(a.M, a.N, a.K, a.x_dtype);
+    if (npt == 0 || a.ksplit != 1 || a.partials) return hipErrorInvalidValue;
+    if (a.x_dtype == 0)
+      launch_fused<uint16_t>(a, grid, npt, st);
+    else
+      launch_fused<float>(a, grid, npt, st);
+  } else if (a.M <= 2) {
     launch_mp<2>(a, grid, st);
-  else if (a.M <= 4)
+  } else if (a.M <= 4) {
     launch_mp<4>(a, grid, st);
-  else if (a.M <= 8)
+  } else if (a.M <= 8) {
     launch_mp<8>(a, grid, st);
-  else
+  } else {
     launch_mp<16>(a, grid, st);
+  }
   return hipGetLastError();
 }
 

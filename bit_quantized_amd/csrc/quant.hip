@@ -46,20 +46,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Codes of eight activations under one row scale (the same rule everywhere).
+// Codes of eight activations under one row scale (a zero row: codes 0).
 __device__ __forceinline__ uint2 quant8(const float* v, float amax, float scale) {
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float r = 0.0f;
-    if (amax != 0.0f) {
-      r = rintf(v[i] / scale);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-    }
-    const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
-    packed[i >> 2] |= b << (8 * (i & 3));
-  }
-  return make_uint2(packed[0], packed[1]);
+  return amax != 0.0f ? quant8_codes(v, scale, 1.0f / scale) : make_uint2(0u, 0u);
 }
 
 // Row maximum over the block's wavefronts (all threads get it).

@@ -48,6 +48,45 @@ __device__ __forceinline__ uint32_t sub_zero_bytes(uint32_t nib4, uint32_t zz) {
   return ((nib4 | 0x80808080u) - zz) ^ 0x80808080u;
 }
 
+// Codes of eight finite activations under a row scale s > 0 with inv the
+// correctly rounded 1 / s: rint(x / s) (IEEE quotient, ties to even) clamped
+// to [-127, 127], as bytes.  The quotient is taken as x * inv, which differs
+// from the IEEE x / s by less than 2.3e-5 for |x / s| <= 127.5 (each is
+// within 2 ulp-of-1 relative rounding of the real quotient); the two can
+// round to different integers only when the product lies within that
+// distance of a boundary n + 1/2, so such elements (|t - rint(t)| > 1/2 -
+// 2^-14) are redone with the IEEE quotient.  Adding 1.5 * 2^23 rounds a
+// float of magnitude <= 127 to an integer (round to nearest even) whose
+// low byte is then the two's-complement code.
+__device__ __forceinline__ uint2 quant8_codes(const float* v, float s, float inv) {
+  constexpr float kRound = 12582912.0f;  // 1.5 * 2^23
+  uint32_t b[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = __builtin_amdgcn_fmed3f(v[i] * inv, -127.0f, 127.0f);
+    const float f = t + kRound;
+    near |= fabsf(t - (f - kRound)) > 0.5f - 0x1p-14f;
+    b[i] = __float_as_uint(f);
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = fminf(fmaxf(rintf(v[i] / s), -127.0f), 127.0f);
+      b[i] = static_cast<uint32_t>(static_cast<int32_t>(r));
+    }
+  }
+  // v_perm_b32 picks bytes of {src0:src1}: selector 0..3 = src1, 4..7 = src0
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = __builtin_amdgcn_perm(b[4 * h + 1], b[4 * h], 0x0400u);      // b0, b1 low bytes
+    const uint32_t hi = __builtin_amdgcn_perm(b[4 * h + 3], b[4 * h + 2], 0x0400u);  // b2, b3 low bytes
+    w[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return make_uint2(w[0], w[1]);
+}
+
 // Zero point of column c in a zeros block.
 __device__ __forceinline__ uint32_t zero_of(const uint8_t* zblk, int c) {
   uint32_t b = zblk[c >> 1];
@@ -71,7 +110,7 @@ hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t
 struct GemmArgs {
   const int8_t* qa;       // quantised activations [M][K] (null when x is quantised in-kernel)
   const float* sa;        // per-token scales [M]
-  const void* x;          // raw activations for the fused-quant GEMV, else null
+  const void* x;          // raw activations quantised in-kernel (GEMV; skinny when it fuses), else null
   int x_dtype;            // W4A8_BF16 / W4A8_F32 when x is set
   PackedView w;
   int64_t M, N, K;
@@ -99,6 +138,9 @@ int device_cus();  // compute units of the current device (cached)
 GemvShape gemv_shape(int64_t N, int64_t K);
 bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s);
 int skinny_ksplit(int64_t M, int64_t N, int64_t K);
+// Whether the 2 <= M <= 16 kernel can quantise raw activations of this shape
+// itself (GemmArgs::x set); x_dtype as in GemmArgs.
+bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype);
 int prefill_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 hipError_t launch_skinny(GemmArgs a, hipStream_t st);

@@ -339,6 +339,18 @@ LINEAR_SPECS = [
     synth.LinearSpec("lin_wide_m1", 1, 384, 4608, seed=64),
     synth.LinearSpec("lin_m4", 4, 1024, 512, seed=65),
     synth.LinearSpec("lin_m40", 40, 512, 272, seed=66),
+    # 2 <= M <= 16 with in-kernel quantisation: every row-count bucket, chunk
+    # counts per thread of 4, 8 and 10 (exact and ragged), f32 input, and
+    # shapes past the LDS, register and split-K limits (two launches)
+    synth.LinearSpec("lin_fq_m2", 2, 3584, 3584, seed=67),
+    synth.LinearSpec("lin_fq_m3_k18944", 3, 18944, 3584, seed=68),
+    synth.LinearSpec("lin_fq_m5_k8192", 5, 8192, 1024, seed=69),
+    synth.LinearSpec("lin_fq_m8_k10240", 8, 10240, 4096, seed=70),
+    synth.LinearSpec("lin_fq_m9", 9, 3584, 2048, seed=71),
+    synth.LinearSpec("lin_fq_m16_f32", 16, 2048, 2048, seed=72, act="f32"),
+    synth.LinearSpec("lin_2l_m16_f32", 16, 5120, 2048, seed=73, act="f32"),
+    synth.LinearSpec("lin_2l_m8_ksplit", 8, 10240, 512, seed=74),
+    synth.LinearSpec("lin_2l_m16_lds", 16, 18944, 512, seed=75),
 ]
 
 
@@ -356,6 +368,27 @@ def test_linear_matches_quant_then_gemm(w4, spec):
     assert torch.equal(y_fused, y_two)
     _check_y(y_fused, lin, qa_ref, sa_ref)
     assert torch.equal(w4.linear(x, W), y_fused)
+
+
+def test_fused_skinny_zero_and_tie_rows(w4):
+    """In-kernel quantisation of the 2 <= M <= 16 kernel on rows that are all
+    zero (scale 0, codes 0) and rows of exact half-integer quotients (ties to
+    even): bitwise equal to the stand-alone quantiser + GEMM."""
+    say("fused skinny zero and tie rows")
+    spec = synth.LinearSpec("fq_rows", 6, 3584, 2048, seed=76, act="f32")
+    lin, W, _, _ = _setup(w4, spec)
+    x = lin["x"].copy()
+    x[1] = 0.0
+    rng = np.random.Generator(np.random.PCG64(77))
+    x[4] = (rng.integers(-127, 127, size=spec.K) + 0.5).astype(np.float32)
+    x[4, 0] = 127.0
+    xd = dev(x)
+    y_fused = w4.linear(xd, W)
+    qa, sa = w4.quant_act(xd)
+    assert torch.equal(y_fused, w4.gemm(qa, sa, W))
+    qa_ref, sa_ref = oracle.quant_act(x)
+    assert np.array_equal(qa.cpu().numpy(), qa_ref)
+    assert not y_fused[1].float().abs().sum().item()
 
 
 def test_gemv_partials_wide(w4):
