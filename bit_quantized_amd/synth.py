@@ -19,6 +19,14 @@ Draw order for one linear, from ``numpy.random.Generator(PCG64(seed))``:
   4. q ~ U{0..15}, uint8, [N][K]
   5. z ~ U{0..15}, uint8, [N][K/group]
   6. s = |N(0, 0.02)|, float32, [N][K/group]
+
+For the W8A8 linear ("Serve a pre-quantized int8 weight-only DiT ...",
+comment "Round two ...": int8 per-channel weights, int8 dynamic
+activations) the weights are drawn instead as (``make_w8_linear``):
+  4'. qw = clip(round(N(0, 32)), -127, 127), int8, [N][K]
+  5'. one column per row, U{0..K-1}, set to +127 or -127 (U{+-1}): every
+      channel reaches the full symmetric range, as a per-channel absmax grid does
+  6'. sw = |N(0, 0.0005)|, float32, [N]
 """
 from __future__ import annotations
 
@@ -91,6 +99,24 @@ def draw_activations(rng: np.random.Generator, M: int, K: int, act: str):
     cols = rng.choice(K, size=n_out, replace=False)
     x[:, cols] *= np.float32(20.0)
     return bf16_round_bits(x), np.sort(cols)
+
+
+def draw_w8_weights(rng: np.random.Generator, N: int, K: int):
+    qw = np.clip(np.rint(rng.normal(0.0, 32.0, size=(N, K))), -127, 127).astype(np.int8)
+    cols = rng.integers(0, K, size=N)
+    signs = rng.choice(np.array([-127, 127], dtype=np.int8), size=N)
+    qw[np.arange(N), cols] = signs
+    sw = np.abs(rng.normal(0.0, 0.0005, size=N)).astype(np.float32)
+    return qw, sw
+
+
+def make_w8_linear(spec: LinearSpec) -> dict:
+    """One W8A8 linear's inputs: ``x`` (as make_linear), ``qw`` int8 [N][K]
+    and ``sw`` float32 [N]."""
+    rng = np.random.Generator(np.random.PCG64(spec.seed))
+    x, cols = draw_activations(rng, spec.M, spec.K, spec.act)
+    qw, sw = draw_w8_weights(rng, spec.N, spec.K)
+    return {"spec": spec, "x": x, "outlier_cols": cols, "qw": qw, "sw": sw}
 
 
 def draw_weights(rng: np.random.Generator, N: int, K: int, group: int = GROUP):

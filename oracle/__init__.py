@@ -64,12 +64,18 @@ def load(mutant: int = 0) -> ctypes.CDLL:
         "oracle_linear": [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, i64, i64, i64, vp],
         "oracle_layout_pack": [vp, vp, vp, i64, i64, vp],
         "oracle_layout_unpack": [vp, i64, i64, vp, vp, vp],
+        "oracle_w8a8_totals": [vp, vp, i64, i64, i64, i64, i64, vp],
+        "oracle_w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp],
+        "oracle_w8_layout_pack": [vp, vp, i64, i64, vp],
+        "oracle_w8_layout_unpack": [vp, i64, i64, vp, vp],
     }.items():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int
     lib.oracle_layout_bytes.argtypes = [i64, i64]
     lib.oracle_layout_bytes.restype = i64
+    lib.oracle_w8_layout_bytes.argtypes = [i64, i64]
+    lib.oracle_w8_layout_bytes.restype = i64
     _LIBS[mutant] = lib
     return lib
 
@@ -135,6 +141,59 @@ def linear(qa, sa, q, z, s, group=128, rows=None, cols=None, mutant: int = 0):
     _check(lib.oracle_linear(_ptr(qa), _ptr(sa), _ptr(q), _ptr(z), _ptr(s), M, N, K, group,
                              m0, m1, n0, n1, _ptr(y)), "linear")
     return y
+
+
+def w8a8_totals(qa, qw, m0=0, m1=None, mutant: int = 0):
+    """W8A8: exact integer products over all of K, P[m1-m0][N] (int32)."""
+    lib = load(mutant)
+    qa = np.ascontiguousarray(qa, np.int8)
+    qw = np.ascontiguousarray(qw, np.int8)
+    M, K = qa.shape
+    N = qw.shape[0]
+    m1 = M if m1 is None else m1
+    P = np.empty((m1 - m0, N), np.int32)
+    _check(lib.oracle_w8a8_totals(_ptr(qa), _ptr(qw), M, N, K, m0, m1, _ptr(P)), "w8a8_totals")
+    return P
+
+
+def w8a8_linear(qa, sa, qw, sw, rows=None, cols=None, mutant: int = 0):
+    """W8A8: unrounded float64 y[rows][cols] = sa[m] * (sw[n] * P[m][n])."""
+    lib = load(mutant)
+    qa = np.ascontiguousarray(qa, np.int8)
+    sa = np.ascontiguousarray(sa, np.float32)
+    qw = np.ascontiguousarray(qw, np.int8)
+    sw = np.ascontiguousarray(sw, np.float32)
+    M, K = qa.shape
+    N = qw.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    n0, n1 = cols if cols is not None else (0, N)
+    y = np.empty((m1 - m0, n1 - n0), np.float64)
+    _check(lib.oracle_w8a8_linear(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, m0, m1, n0, n1,
+                                  _ptr(y)), "w8a8_linear")
+    return y
+
+
+def w8_layout_bytes(N: int, K: int) -> int:
+    return int(load().oracle_w8_layout_bytes(N, K))
+
+
+def w8_layout_pack(qw, sw):
+    lib = load()
+    qw = np.ascontiguousarray(qw, np.int8)
+    sw = np.ascontiguousarray(sw, np.float32)
+    N, K = qw.shape
+    out = np.empty((w8_layout_bytes(N, K),), np.uint8)
+    _check(lib.oracle_w8_layout_pack(_ptr(qw), _ptr(sw), N, K, _ptr(out)), "w8_layout_pack")
+    return out
+
+
+def w8_layout_unpack(buf, N: int, K: int):
+    lib = load()
+    buf = np.ascontiguousarray(buf, np.uint8)
+    qw = np.empty((N, K), np.int8)
+    sw = np.empty((N,), np.float32)
+    _check(lib.oracle_w8_layout_unpack(_ptr(buf), N, K, _ptr(qw), _ptr(sw)), "w8_layout_unpack")
+    return qw, sw
 
 
 def threads() -> int:

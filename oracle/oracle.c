@@ -34,6 +34,9 @@
  * precision the GPU kernel takes it in; everything after the integer products
  * is float64.
  *
+ * The W8A8 int8-dynamic linear (a second layer the pages describe) follows at
+ * the end of this file.
+ *
  * Parity pins live in tests/test_oracle_pins.py (brute force, closed forms,
  * invariants, planted mutants).  Compile-time ORACLE_MUTANT values plant one
  * plausible mistake each, so the tests can show every mistake is caught.
@@ -289,5 +292,120 @@ int oracle_layout_unpack(const uint8_t* in, int64_t N, int64_t K,
             const float* sb = (const float*)(in + s0) + (nb * G + g) * 16;
             for (int c = 0; c < 16; ++c) s[(16 * nb + c) * G + g] = sb[c];
         }
+    return ORACLE_OK;
+}
+
+/*
+ * W8A8 int8-dynamic linear ("Serve a pre-quantized int8 weight-only DiT ...",
+ * comment "Round two ...": int8 weights, activations quantised to int8 at run
+ * time, an integer matrix product, and the product scaled afterwards; the
+ * same comment warns that a reference must carry the activation scale).
+ * Readings taken where the page is silent (each also listed in the design doc):
+ *   - weights: W[n][k] = sw[n] * qw[n][k], symmetric int8 with one float32
+ *     scale per output channel and no zero point;
+ *   - activations: the per-token rule of quant_row above;
+ *   - P[m][n] = sum over all k of qa[m][k] * qw[n][k], exact (the library
+ *     keeps it in int32, so |P| must stay below 2^31);
+ *   - y[m][n] = sa[m] * (sw[n] * P[m][n]) in float64, not rounded.
+ */
+static int64_t w8_dot(const int8_t* a, const int8_t* w, int64_t K) {
+    int64_t p = 0;
+    for (int64_t k = 0; k < K; ++k) {
+#if ORACLE_MUTANT == 8
+        p += (int64_t)a[k] * (int64_t)(uint8_t)w[k];         /* planted: weights read unsigned */
+#else
+        p += (int64_t)a[k] * (int64_t)w[k];
+#endif
+    }
+    return p;
+}
+
+/* P[m][n] for rows m0..m1-1 (stored at P[(m-m0)][n]). */
+int oracle_w8a8_totals(const int8_t* qa, const int8_t* qw, int64_t M, int64_t N, int64_t K,
+                       int64_t m0, int64_t m1, int32_t* P) {
+    if (!qa || !qw || !P || M < 0 || N < 0 || K <= 0) return ORACLE_BAD_ARG;
+    if (m0 < 0 || m1 > M || m0 > m1) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t p = w8_dot(qa + m * K, qw + n * K, K);
+            if (p > 2147483647LL || p < -2147483647LL) {
+#pragma omp atomic write
+                rc = ORACLE_RANGE;
+            }
+            P[(m - m0) * N + n] = (int32_t)p;
+        }
+    }
+    return rc;
+}
+
+/* y[m][n] (float64, unrounded) for rows m0..m1-1 and columns n0..n1-1. */
+int oracle_w8a8_linear(const int8_t* qa, const float* sa, const int8_t* qw, const float* sw,
+                       int64_t M, int64_t N, int64_t K, int64_t m0, int64_t m1, int64_t n0,
+                       int64_t n1, double* y) {
+    if (!qa || !sa || !qw || !sw || !y || K <= 0) return ORACLE_BAD_ARG;
+    if (m0 < 0 || m1 > M || m0 > m1 || n0 < 0 || n1 > N || n0 > n1) return ORACLE_BAD_ARG;
+    int64_t W = n1 - n0;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = n0; n < n1; ++n) {
+            double p = (double)w8_dot(qa + m * K, qw + n * K, K);
+#if ORACLE_MUTANT == 7
+            y[(m - m0) * W + (n - n0)] = (double)sa[m] * p;           /* planted: weight scale dropped */
+#else
+            y[(m - m0) * W + (n - n0)] = (double)sa[m] * ((double)sw[n] * p);
+#endif
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The W8A8 packed weight format of the HIP library (W8 layout version 1),
+ * written out from its specification.  With G = K/128, NB = N/16:
+ *   codes plane, N*K bytes at offset 0: block (nb, g) = 2048 bytes at
+ *     (nb*G + g) * 2048; half h (0, 1) at +1024*h; lane L = 16*j + c
+ *     (j = 0..3, c = 0..15) at +16*L; byte i of that run is
+ *     qw[16nb+c][128g + 64h + 16j + i] (two's complement);
+ *   scales plane, 4*N bytes at S0 = round_up(N*K, 256): float32 sw[n] at
+ *     index n, bit for bit.
+ */
+int64_t oracle_w8_layout_bytes(int64_t N, int64_t K) { return round_up256(N * K) + 4 * N; }
+
+int oracle_w8_layout_pack(const int8_t* qw, const float* sw, int64_t N, int64_t K, uint8_t* out) {
+    if (!qw || !sw || !out || N <= 0 || K <= 0 || N % 16 || K % 128) return ORACLE_BAD_ARG;
+    int64_t G = K / 128, NB = N / 16;
+    memset(out, 0, (size_t)oracle_w8_layout_bytes(N, K));
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g)
+            for (int h = 0; h < 2; ++h)
+                for (int j = 0; j < 4; ++j)
+                    for (int c = 0; c < 16; ++c)
+                        for (int i = 0; i < 16; ++i) {
+                            int64_t n = 16 * nb + c, k = 128 * g + 64 * h + 16 * j + i;
+                            out[(nb * G + g) * 2048 + 1024 * h + 16 * (16 * j + c) + i] =
+                                (uint8_t)qw[n * K + k];
+                        }
+    float* sb = (float*)(out + round_up256(N * K));
+    for (int64_t n = 0; n < N; ++n) sb[n] = sw[n];
+    return ORACLE_OK;
+}
+
+int oracle_w8_layout_unpack(const uint8_t* in, int64_t N, int64_t K, int8_t* qw, float* sw) {
+    if (!in || !qw || !sw || N <= 0 || K <= 0 || N % 16 || K % 128) return ORACLE_BAD_ARG;
+    int64_t G = K / 128, NB = N / 16;
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g)
+            for (int h = 0; h < 2; ++h)
+                for (int j = 0; j < 4; ++j)
+                    for (int c = 0; c < 16; ++c)
+                        for (int i = 0; i < 16; ++i) {
+                            int64_t n = 16 * nb + c, k = 128 * g + 64 * h + 16 * j + i;
+                            qw[n * K + k] =
+                                (int8_t)in[(nb * G + g) * 2048 + 1024 * h + 16 * (16 * j + c) + i];
+                        }
+    const float* sb = (const float*)(in + round_up256(N * K));
+    for (int64_t n = 0; n < N; ++n) sw[n] = sb[n];
     return ORACLE_OK;
 }

@@ -9,7 +9,12 @@
   one linear against a reference dequant-then-matmul; comment "Round two ...":
   that reference must carry the activation scale);
 - the identity-scale case, which reduces to an exact integer GEMM;
-- the packed layout against hand-worked bytes and a round trip.
+- the packed layout against hand-worked bytes and a round trip;
+- for the W8A8 linear: integer totals against numpy int64 matmul and closed
+  forms, the float64 result against numpy dequant-then-matmul, and the exact
+  agreement with the W4A8 oracle on weights both can express (int8 weights
+  q - z with a per-channel scale repeated over every group);
+- the W8A8 packed layout against hand-worked bytes and a round trip.
 
 Every pin is a plain function taking ``mutant``; ``test_mutants_are_caught``
 rebuilds the oracle with one planted mistake at a time and checks that at
@@ -173,8 +178,63 @@ def pin_identity_scale(mutant=0):
     assert np.array_equal(y, exact.astype(np.float64))
 
 
+def _w8_case(seed, M, K, N):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    qw, sw = synth.draw_w8_weights(rng, N, K)
+    return x, qw, sw
+
+
+def pin_w8_totals_brute(mutant=0):
+    """W8A8 integer totals: numpy int64 matmul, and two closed forms."""
+    x, qw, sw = _w8_case(31, 4, 384, 24)
+    qa, _ = oracle.quant_act(x, mutant=mutant)
+    P = oracle.w8a8_totals(qa, qw, mutant=mutant)
+    assert np.array_equal(P.astype(np.int64), qa.astype(np.int64) @ qw.astype(np.int64).T)
+    K = 1024
+    ones = np.ones((2, K), np.int8)
+    assert np.all(oracle.w8a8_totals(ones, np.ones((16, K), np.int8), mutant=mutant) == K)
+    # +127 activations against -127 weights: every product is -16129
+    a = np.full((1, K), 127, np.int8)
+    w = np.full((16, K), -127, np.int8)
+    assert np.all(oracle.w8a8_totals(a, w, mutant=mutant) == -16129 * K)
+    P2 = oracle.w8a8_totals(qa, qw, m0=1, m1=3, mutant=mutant)
+    assert np.array_equal(P2, P[1:3])
+
+
+def pin_w8_dequant_matmul(mutant=0):
+    """W8A8 float64 result against numpy dequant-then-matmul (activation and
+    weight scales both applied)."""
+    x, qw, sw = _w8_case(32, 5, 512, 32)
+    qa, sa = oracle.quant_act(x, mutant=mutant)
+    y = oracle.w8a8_linear(qa, sa, qw, sw, mutant=mutant)
+    ref = (sa.astype(np.float64)[:, None] * qa.astype(np.float64)) @ (
+        sw.astype(np.float64)[:, None] * qw.astype(np.float64)).T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    yw = oracle.w8a8_linear(qa, sa, qw, sw, rows=(2, 4), cols=(3, 19), mutant=mutant)
+    assert np.array_equal(yw, y[2:4, 3:19])
+
+
+def pin_w8_equals_w4_special_case(mutant=0):
+    """Int4 weights with zero points are int8 weights q - z; with the group
+    scale equal for every group of a channel, the W4A8 and W8A8 results are
+    the same exact float64 values (every product of a float32 scale and an
+    integer below 2^29 is exact, so the two summation orders agree)."""
+    x, q, z, s = _tiny_case(seed=33, M=3, K=512, N=32)
+    sw = s[:, 0].copy()
+    s_rep = np.repeat(sw[:, None], 512 // 128, axis=1)
+    qw = (q.astype(np.int16) - np.repeat(z.astype(np.int16), 128, axis=1)).astype(np.int8)
+    qa, sa = oracle.quant_act(x, mutant=mutant)
+    y4 = oracle.linear(qa, sa, q, z, s_rep, mutant=mutant)
+    y8 = oracle.w8a8_linear(qa, sa, qw, sw, mutant=mutant)
+    assert np.array_equal(y4, y8)
+    P4 = oracle.group_partials(qa, q, z, mutant=mutant).astype(np.int64).sum(axis=2)
+    assert np.array_equal(P4, oracle.w8a8_totals(qa, qw, mutant=mutant).astype(np.int64))
+
+
 PINS = [pin_quant_golden, pin_quant_invariants, pin_partials_brute, pin_zero_shift_and_identity,
-        pin_zero_weights, pin_group_permutation, pin_dequant_matmul, pin_identity_scale]
+        pin_zero_weights, pin_group_permutation, pin_dequant_matmul, pin_identity_scale,
+        pin_w8_totals_brute, pin_w8_dequant_matmul, pin_w8_equals_w4_special_case]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -183,7 +243,8 @@ def test_pin(pin):
 
 
 MUTANTS = {1: "zero point dropped", 2: "ties away from zero", 3: "scale absmax/128",
-           4: "zero plane transposed", 5: "activation scale missing", 6: "weights shifted by one k"}
+           4: "zero plane transposed", 5: "activation scale missing", 6: "weights shifted by one k",
+           7: "W8A8 weight scale dropped", 8: "W8A8 weights read unsigned"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=[MUTANTS[m] for m in sorted(MUTANTS)])
@@ -263,3 +324,47 @@ def test_layout_round_trip_and_bijection():
         pos = (int(nz[0]), int(b[nz[0]]))
         assert pos not in seen
         seen.add(pos)
+
+
+def test_w8_layout_golden():
+    entries, scalars = [], {}
+    with open(os.path.join(GOLDEN, "layout_w8_v1.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            parts = line.split()
+            if parts[0] in ("scales_offset", "total_bytes"):
+                scalars[parts[0]] = int(parts[1])
+            else:
+                entries.append((int(parts[0]), int(parts[7]), int(parts[8], 16)))
+    N, K = 16, 128
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    qw = (((5 * n + 3 * k) % 255) - 127).astype(np.int8)
+    sw = np.linspace(0.25, 4.0, N, dtype=np.float32)
+    buf = oracle.w8_layout_pack(qw, sw)
+    assert buf.size == scalars["total_bytes"]
+    for off, value, b in entries:
+        assert (value & 0xFF) == b
+        assert buf[off] == b, (off, hex(buf[off]), hex(b))
+    s0 = scalars["scales_offset"]
+    assert np.array_equal(buf[s0:s0 + 4 * N].view(np.float32), sw)
+
+
+def test_w8_layout_round_trip_and_bijection():
+    rng = np.random.Generator(np.random.PCG64(34))
+    N, K = 48, 384
+    qw, sw = synth.draw_w8_weights(rng, N, K)
+    buf = oracle.w8_layout_pack(qw, sw)
+    qw2, sw2 = oracle.w8_layout_unpack(buf, N, K)
+    assert np.array_equal(qw, qw2) and np.array_equal(sw.view(np.uint32), sw2.view(np.uint32))
+    seen = set()
+    for (nn, kk) in [(0, 0), (0, 64), (1, 0), (15, 127), (16, 0), (47, 383), (20, 200), (33, 65)]:
+        q1 = np.zeros((N, K), np.int8)
+        q1[nn, kk] = 1
+        b = oracle.w8_layout_pack(q1, np.zeros_like(sw))[:N * K]
+        nz = np.flatnonzero(b)
+        assert nz.size == 1 and b[nz[0]] == 1
+        assert int(nz[0]) not in seen
+        seen.add(int(nz[0]))
