@@ -53,6 +53,17 @@ SIGNATURES = {
     "w4a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz,
                                    _vp]),
+    "w8a8_layout_version": (ctypes.c_int, []),
+    "w8a8_packed_weight_bytes": (_sz, [_i64, _i64]),
+    "w8a8_pack_weights": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "w8a8_unpack_weights": (ctypes.c_int, [_vp, _sz, _i64, _i64, _vp, _vp, _vp]),
+    "w8a8_select_path": (ctypes.c_int, [_i64, _i64, _i64]),
+    "w8a8_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "w8a8_gemm": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "w8a8_gemm_debug": (ctypes.c_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _i64, _i64,
+                                       _vp, _vp, _vp, _sz, _vp]),
+    "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "w8a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -286,5 +297,125 @@ def linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None) -> torch.
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.w4a8_linear(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, _p(out),
+                           _p(workspace), wsb, _stream(x.device)))
+    return out
+
+
+# ------------------------------------------------------------------ W8A8
+
+@dataclass
+class PackedW8:
+    """A packed W8A8 weight (int8 per channel) with its identity."""
+    buf: torch.Tensor          # uint8, w8a8_packed_weight_bytes(N, K)
+    N: int
+    K: int
+    layout_version: int
+
+    def check(self):
+        v = load().w8a8_layout_version()
+        if self.layout_version != v:
+            raise ValueError(f"packed with W8A8 layout {self.layout_version}, library has {v}")
+
+
+def w8a8_pack_weights(qw: torch.Tensor, sw: torch.Tensor, out: torch.Tensor | None = None) -> PackedW8:
+    """qw int8 [N][K], sw float32 [N] -> packed W8A8 weight."""
+    lib = load()
+    _need_cuda(qw, sw)
+    if qw.dtype != torch.int8 or sw.dtype != torch.float32:
+        raise TypeError("qw must be int8 and sw float32")
+    N, K = qw.shape
+    nbytes = lib.w8a8_packed_weight_bytes(N, K)
+    if nbytes == 0:
+        _check(lib.w8a8_pack_weights(None, None, N, K, None, 0, None))
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=qw.device)
+    _check(lib.w8a8_pack_weights(_p(qw), _p(sw), N, K, _p(out), out.numel(), _stream(qw.device)))
+    return PackedW8(out, N, K, lib.w8a8_layout_version())
+
+
+def w8a8_unpack_weights(w: PackedW8):
+    lib = load()
+    w.check()
+    dev = w.buf.device
+    qw = torch.empty((w.N, w.K), dtype=torch.int8, device=dev)
+    sw = torch.empty((w.N,), dtype=torch.float32, device=dev)
+    _check(lib.w8a8_unpack_weights(_p(w.buf), w.buf.numel(), w.N, w.K, _p(qw), _p(sw), _stream(dev)))
+    return qw, sw
+
+
+def w8a8_select_path(M: int, N: int, K: int) -> int:
+    return int(load().w8a8_select_path(M, N, K))
+
+
+def w8a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().w8a8_gemm_workspace_bytes(M, N, K))
+
+
+def _w8_workspace(M, w: PackedW8, workspace):
+    need = w8a8_workspace_bytes(M, w.N, w.K)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.buf.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def w8a8_gemm(qa: torch.Tensor, sa: torch.Tensor, w: PackedW8, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 y [M][N] from quantised activations and a packed W8A8 weight."""
+    lib = load()
+    w.check()
+    _need_cuda(qa, sa)
+    M, K = qa.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=qa.device) if out is None else out
+    ws, wsb = _w8_workspace(M, w, workspace)
+    _check(lib.w8a8_gemm(_p(qa), _p(sa), _p(w.buf), w.buf.numel(), M, w.N, w.K, _p(out), _p(ws),
+                         wsb, _stream(qa.device)))
+    return out
+
+
+def w8a8_gemm_debug(qa, sa, w: PackedW8, path: int = PATH_AUTO, rows=None, want_y: bool = True,
+                    workspace=None):
+    """(totals int32 [rows][N], y bf16 [M][N] or None) from a forced path."""
+    lib = load()
+    w.check()
+    M, K = qa.shape
+    m0, m1 = rows if rows is not None else (0, M)
+    P = torch.empty((m1 - m0, w.N), dtype=torch.int32, device=qa.device)
+    y = torch.empty((M, w.N), dtype=torch.bfloat16, device=qa.device) if want_y else None
+    ws, wsb = _w8_workspace(M, w, workspace)
+    _check(lib.w8a8_gemm_debug(_p(qa), _p(sa), _p(w.buf), w.buf.numel(), M, w.N, w.K, path, m0, m1,
+                               _p(P) if P.numel() else None, _p(y), _p(ws), wsb,
+                               _stream(qa.device)))
+    return P, y
+
+
+def w8a8_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().w8a8_linear_workspace_bytes(M, N, K))
+
+
+def w8a8_linear(x: torch.Tensor, w: PackedW8, out=None, workspace=None) -> torch.Tensor:
+    """W8A8 from raw bf16/f32 activations: per-token quantisation and the
+    int8 GEMM (one launch for M <= 16 when the rows fit in LDS)."""
+    lib = load()
+    w.check()
+    _need_cuda(x, out)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError(x.dtype)
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    need = w8a8_linear_workspace_bytes(M, w.N, w.K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w8a8_linear(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, _p(out),
                            _p(workspace), wsb, _stream(x.device)))
     return out

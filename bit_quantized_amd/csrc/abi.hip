@@ -186,6 +186,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   a.sa_ws = nullptr;
   a.ksplit = ks;
   a.cb = a.ks = 0;
+  a.w8 = false;
   const float* sa_for_reduce = act.sa;
   if (path == W4A8_PATH_GEMV) {
     const GemvShape gs = gemv_shape(N, K);
@@ -219,6 +220,136 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
 size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
   if (pick_path(M, K) == W4A8_PATH_GEMV) return workspace_for(W4A8_PATH_GEMV, M, N, K);
   return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+}
+
+// ------------------------------------------------------------------ W8A8
+
+// Exact int32 totals need |sum_k qa*qw| <= 127 * 127 * K < 2^31.
+constexpr int64_t kW8MaxK = 131072;
+
+int check_w8_shape(int64_t N, int64_t K) {
+  int rc = check_weight_shape(N, K, kGroup);
+  if (rc) return rc;
+  if (K > kW8MaxK)
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
+                "W8A8 keeps exact int32 totals, so K <= %lld (K=%lld)", (long long)kW8MaxK,
+                (long long)K);
+  return W4A8_OK;
+}
+
+int pick_w8_path(int64_t M) { return M <= 16 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL; }
+
+int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
+  return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K) : prefill_ksplit(M, N, K);
+}
+
+// int32 split-K partials [ksplit][M][N].
+size_t w8_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
+  const int ks = w8_ksplit(path, M, N, K);
+  return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
+}
+
+size_t w8_gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
+  size_t need = w8_workspace_for(W4A8_PATH_PREFILL, M, N, K);
+  if (M <= 16) {
+    const size_t w = w8_workspace_for(W4A8_PATH_SKINNY, M, N, K);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
+size_t w8_linear_workspace(int64_t M, int64_t N, int64_t K) {
+  return round256((size_t)M * K) + round256((size_t)M * 4) + w8_gemm_workspace_any(M, N, K);
+}
+
+int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
+                int64_t K, int32_t path, int64_t m_begin, int64_t m_end, int32_t* totals,
+                uint16_t* y, void* workspace, size_t workspace_bytes, void* stream, bool debug,
+                bool validate_only = false) {
+  int rc = check_w8_shape(N, K);
+  if (rc) return rc;
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  const bool fused = act.x != nullptr;
+  if (!packed || (!fused && (!act.qa || !act.sa)))
+    return fail(W4A8_ERR_INVALID_ARG, "null input pointer");
+  if (!debug && !validate_only && !y) return fail(W4A8_ERR_INVALID_ARG, "null output pointer");
+  if (!aligned16(packed) || (y && !aligned16(y)) ||
+      (!fused && (!aligned16(act.qa) || !aligned16(act.sa))) || (fused && !aligned16(act.x)))
+    return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const size_t need = (size_t)w8_packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  if (path == W4A8_PATH_AUTO) path = pick_w8_path(M);
+  if (path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
+    return fail(W4A8_ERR_INVALID_ARG, "W8A8 paths are SKINNY (M <= 16) and PREFILL (got %d)",
+                (int)path);
+  if (path == W4A8_PATH_SKINNY && M > 16)
+    return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
+  if (path == W4A8_PATH_PREFILL && (M * K > kPrefillMaxBytes || N * K > kPrefillMaxBytes))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
+                "PREFILL path addresses activations and codes with 32-bit offsets "
+                "(M*K=%lld, N*K=%lld, limit %lld)",
+                (long long)(M * K), (long long)(N * K), (long long)kPrefillMaxBytes);
+  if (fused && !(path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype) && !debug))
+    return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
+  if (debug) {
+    if (m_begin < 0 || m_end > M || m_begin > m_end)
+      return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
+                  (long long)m_begin, (long long)m_end, (long long)M);
+    if (totals && !aligned16(totals))
+      return fail(W4A8_ERR_MISALIGNED, "totals must be 16-byte aligned");
+  }
+  const int ks = w8_ksplit(path, M, N, K);
+  const size_t ws_need = w8_workspace_for(path, M, N, K);
+  if (ws_need && (!workspace || workspace_bytes < ws_need))
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                ws_need);
+  if (ws_need && !aligned16(workspace))
+    return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const size_t ybytes = (size_t)M * (size_t)N * 2;
+  const size_t xbytes = (size_t)M * K * (act.x_dtype == W4A8_F32 ? 4 : 2);
+  if (y && ((!fused && (overlaps(y, ybytes, act.qa, (size_t)M * K) ||
+                        overlaps(y, ybytes, act.sa, (size_t)M * 4))) ||
+            (fused && overlaps(y, ybytes, act.x, xbytes)) || overlaps(y, ybytes, packed, need) ||
+            (ws_need && overlaps(y, ybytes, workspace, ws_need))))
+    return fail(W4A8_ERR_INVALID_ARG, "output aliases an input or the workspace");
+  if (totals && m_end > m_begin) {
+    const size_t tb = (size_t)(m_end - m_begin) * (size_t)N * 4;
+    if ((y && overlaps(totals, tb, y, ybytes)) || overlaps(totals, tb, packed, need) ||
+        (ws_need && overlaps(totals, tb, workspace, ws_need)))
+      return fail(W4A8_ERR_INVALID_ARG, "totals alias another buffer");
+  }
+  if (validate_only) return ok();
+
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
+  GemmArgs a;
+  a.qa = act.qa;
+  a.sa = act.sa;
+  a.x = act.x;
+  a.x_dtype = act.x_dtype;
+  a.w.codes = base;
+  a.w.zeros = nullptr;
+  a.w.scales = reinterpret_cast<const float*>(base + w8_scales_offset(N, K));
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.partials = debug ? totals : nullptr;
+  a.m_begin = debug ? m_begin : 0;
+  a.m_end = debug ? m_end : 0;
+  a.workspace = static_cast<float*>(workspace);
+  a.sa_ws = nullptr;
+  a.ksplit = ks;
+  a.cb = a.ks = 0;
+  a.w8 = true;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e = path == W4A8_PATH_SKINNY ? launch_skinny(a, st) : launch_prefill(a, st);
+  if (e == hipSuccess && ks > 1 && (y || a.partials))
+    e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, act.sa, a.w.scales,
+                                M, N, y, a.partials, a.m_begin, a.m_end, st);
+  return device_status(e, "w8a8 gemm launch");
 }
 
 }  // namespace
@@ -386,6 +517,117 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (rc) return rc;
   return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group,
                   W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
+}
+
+// ------------------------------------------------------------------ W8A8
+
+int w8a8_layout_version(void) { return W8A8_LAYOUT_VERSION; }
+
+size_t w8a8_packed_weight_bytes(int64_t N, int64_t K) {
+  if (check_w8_shape(N, K)) return 0;
+  return (size_t)w8_packed_bytes(N, K);
+}
+
+int w8a8_pack_weights(const int8_t* qw, const float* sw, int64_t N, int64_t K, void* packed,
+                      size_t packed_bytes_, void* stream) {
+  int rc = check_w8_shape(N, K);
+  if (rc) return rc;
+  if (!qw || !sw || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(qw) || !aligned16(packed) || !aligned16(sw))
+    return fail(W4A8_ERR_MISALIGNED, "qw, sw and packed must be 16-byte aligned");
+  const size_t need = (size_t)w8_packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  if (overlaps(packed, need, qw, (size_t)(N * K)) || overlaps(packed, need, sw, (size_t)N * 4))
+    return fail(W4A8_ERR_INVALID_ARG, "packed buffer aliases an input");
+  (void)hipGetLastError();
+  return device_status(launch_w8_pack(qw, sw, N, K, static_cast<uint8_t*>(packed),
+                                      static_cast<hipStream_t>(stream)),
+                       "w8a8 pack launch");
+}
+
+int w8a8_unpack_weights(const void* packed, size_t packed_bytes_, int64_t N, int64_t K, int8_t* qw,
+                        float* sw, void* stream) {
+  int rc = check_w8_shape(N, K);
+  if (rc) return rc;
+  if (!qw || !sw || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(qw) || !aligned16(packed) || !aligned16(sw))
+    return fail(W4A8_ERR_MISALIGNED, "qw, sw and packed must be 16-byte aligned");
+  const size_t need = (size_t)w8_packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  if (overlaps(packed, need, qw, (size_t)(N * K)) || overlaps(packed, need, sw, (size_t)N * 4) ||
+      overlaps(qw, (size_t)(N * K), sw, (size_t)N * 4))
+    return fail(W4A8_ERR_INVALID_ARG, "buffers alias");
+  (void)hipGetLastError();
+  return device_status(launch_w8_unpack(static_cast<const uint8_t*>(packed), N, K, qw, sw,
+                                        static_cast<hipStream_t>(stream)),
+                       "w8a8 unpack launch");
+}
+
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_w8_shape(N, K) || M <= 0) return 0;
+  return w8_gemm_workspace_any(M, N, K);
+}
+
+int w8a8_select_path(int64_t M, int64_t, int64_t) { return M <= 0 ? 0 : pick_w8_path(M); }
+
+int w8a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
+              int64_t M, int64_t N, int64_t K, uint16_t* y, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0,
+                     0, nullptr, y, workspace, workspace_bytes, stream, false);
+}
+
+int w8a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
+                    int64_t M, int64_t N, int64_t K, int32_t path, int64_t m_begin, int64_t m_end,
+                    int32_t* totals, uint16_t* y_or_null, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, path, m_begin,
+                     m_end, totals, y_or_null, workspace, workspace_bytes, stream, true);
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (check_w8_shape(N, K) || M <= 0) return 0;
+  return w8_linear_workspace(M, N, K);
+}
+
+int w8a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes_, int64_t M,
+                int64_t N, int64_t K, uint16_t* y, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_w8_shape(N, K);
+  if (rc) return rc;
+  if (!x || !y) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
+    return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  const size_t need = w8_linear_workspace(M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  // One launch when the skinny kernel can quantise these rows itself.
+  if (pick_w8_path(M) == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, x_dtype))
+    return run_w8_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K,
+                       W4A8_PATH_SKINNY, 0, 0, nullptr, y, workspace, workspace_bytes, stream,
+                       false);
+  const size_t xbytes = (size_t)M * K * (x_dtype == W4A8_F32 ? 4 : 2);
+  if (overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, packed, packed_bytes_))
+    return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
+  if (overlaps(y, (size_t)M * N * 2, x, xbytes))
+    return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qa = reinterpret_cast<int8_t*>(ws);
+  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
+  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
+  rc = run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0, 0,
+                   nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+                   /*validate_only=*/true);
+  if (rc) return rc;
+  rc = w4a8_quant_act(x, x_dtype, M, K, qa, sa, stream);
+  if (rc) return rc;
+  return run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0,
+                     0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
 }  // extern "C"

@@ -125,10 +125,17 @@ template <> struct XChunk<float> {  // two 16-byte loads
 // the weight loads in flight); the wavefronts then read their A operands
 // from LDS (row stride K + 16 bytes, which keeps a 16-lane read on distinct
 // banks) instead of from memory.
-template <bool DEBUG, int MP, int NPT, typename T>
+//
+// W8: the W8A8 weights instead (int8 per channel, packed as two 1 KiB halves
+// per unit in MFMA operand order, one float scale per channel).  The bytes
+// are the B operand as loaded, the products accumulate in int32 over all of
+// K (exact), and the two scales are applied once, to the total.
+template <bool DEBUG, int MP, int NPT, typename T, bool W8>
 __global__ void __launch_bounds__(kThreads)
 skinny_kernel(GemmArgs a) {
   constexpr bool FUSED = NPT > 0;
+  constexpr int kUnitBytes = W8 ? 2 * kBlockBytes : kBlockBytes;  // codes per unit
+  constexpr int CW = W8 ? 2 : 1;                                  // code loads per unit
   using S = ActShape<MP>;
   constexpr int kQuadLoads = FUSED ? 0 : S::kQuadLoads;
   constexpr int kSlotLoads = FUSED ? 0 : S::kSlotLoads;
@@ -177,9 +184,12 @@ skinny_kernel(GemmArgs a) {
   const int nq = (nrun + 3) >> 2;
   const int64_t blk0 = nb * G + gb;  // first unit of the run in the packed planes
 
-  const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.w.codes + blk0 * kBlockBytes, (int64_t)nrun * kBlockBytes);
-  const __amdgpu_buffer_rsrc_t rs = rsrc_of(a.w.scales + blk0 * 16, (int64_t)nrun * 64);
-  const __amdgpu_buffer_rsrc_t rz = rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
+  const __amdgpu_buffer_rsrc_t rc = rsrc_of(a.w.codes + blk0 * kUnitBytes, (int64_t)nrun * kUnitBytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      W8 ? rsrc_of(a.w.scales, 0) : rsrc_of(a.w.scales + blk0 * 16, (int64_t)nrun * 64);
+  const __amdgpu_buffer_rsrc_t rz =
+      W8 ? rsrc_of(a.w.scales, 0)
+         : rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.qa, FUSED ? 0 : a.M * a.K);
   const int oob = 0x7FFFFFF0;  // beyond every descriptor
 
@@ -196,8 +206,12 @@ skinny_kernel(GemmArgs a) {
   };
   // per-quad operands of quad q: scales, zeros, and (MP <= 4) the activations
   auto load_quad = [&](int q, uint32_t& s, uint32_t& z, v4i* act) __attribute__((always_inline)) {
-    s = __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * q + j) * 64 + 4 * r16, 0, 0);
-    z = __builtin_amdgcn_raw_buffer_load_b32(rz, z_base == oob ? oob : 4 * q * kZeroBlockBytes + z_base, 0, 0);
+    if constexpr (!W8) {
+      s = __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * q + j) * 64 + 4 * r16, 0, 0);
+      z = __builtin_amdgcn_raw_buffer_load_b32(rz, z_base == oob ? oob : 4 * q * kZeroBlockBytes + z_base, 0, 0);
+    } else {
+      s = z = 0u;
+    }
     if constexpr (kQuadLoads > 0) {
 #pragma unroll
       for (int n = 0; n < kQuadLoads; ++n)
@@ -206,14 +220,17 @@ skinny_kernel(GemmArgs a) {
     }
   };
   // per-unit operands of unit u: codes and (MP >= 8) the activations
-  auto load_unit = [&](int u, v4u& w, v4i* act) __attribute__((always_inline)) {
+  auto load_unit = [&](int u, v4u* w, v4i* act) __attribute__((always_inline)) {
     if constexpr (kSlotLoads > 0) {
 #pragma unroll
       for (int h = 0; h < kSlotLoads; ++h)
         act[h] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                              ra, act_off(u) == oob ? oob : act_off(u) + 64 * h, 0, 0));
     }
-    w = __builtin_amdgcn_raw_buffer_load_b128(rc, u * kBlockBytes + 16 * lane, 0, kNontemporal);
+#pragma unroll
+    for (int h = 0; h < CW; ++h)
+      w[h] = __builtin_amdgcn_raw_buffer_load_b128(rc, u * kUnitBytes + h * kBlockBytes + 16 * lane,
+                                                   0, kNontemporal);
   };
 
   // ds_bpermute byte addresses: source lane of this lane's A operand for
@@ -225,12 +242,13 @@ skinny_kernel(GemmArgs a) {
   const int zshift = (r16 & 7) * 4;        // nibble of channel r16 in that dword
 
   float accf[4] = {0.f, 0.f, 0.f, 0.f};
-  v4u wr[4];                 // codes ring, one slot per unit of the quad
+  v4i acci = {0, 0, 0, 0};   // W8: int32 total over the run
+  v4u wr[4][CW];             // codes ring, one slot per unit of the quad
   v4i ar[4][SL];             // per-unit activations (MP >= 8)
   v4i aq[2][QL];             // per-quad activations (MP <= 4), current and next quad
   uint32_t sq[2], zq[2];     // per-quad scales and zeros, current and next quad
 
-  auto compute = [&](int q, int i, const v4u& w, const v4i* au, const v4i* aqc, uint32_t sc,
+  auto compute = [&](int q, int i, const v4u* w, const v4i* au, const v4i* aqc, uint32_t sc,
                      uint32_t zc) __attribute__((always_inline)) {
     v4i a0, a1;
     if constexpr (FUSED) {
@@ -252,13 +270,18 @@ skinny_kernel(GemmArgs a) {
         a1[t] = __builtin_amdgcn_ds_bpermute(perm_a + 32 * du + 16, src[t]);
       }
     }
+    if constexpr (W8) {
+      acci = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, __builtin_bit_cast(v4i, w[0]), acci, 0, 0, 0);
+      acci = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, __builtin_bit_cast(v4i, w[1]), acci, 0, 0, 0);
+      return;
+    }
     const float s = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_s + 64 * i, (int)sc));
     const uint32_t zw = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_z + 8 * i, (int)zc);
     const uint32_t zz = ((zw >> zshift) & 0xFu) * 0x01010101u;
     v4i b0, b1;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t d = w[t];
+      const uint32_t d = w[0][t];
       b0[t] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
       b1[t] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
     }
@@ -339,6 +362,37 @@ skinny_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) compute(q, i, wr[i], ar[i], aq[0], sq[0], zq[0]);
 
+  if constexpr (W8) {
+    // exact int32 totals: the sum over wavefronts is order-free
+    int (*redi)[4][64] = reinterpret_cast<int (*)[4][64]>(red);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) redi[wave][t][lane] = acci[t];
+    __syncthreads();
+    if (wave == 0) {
+      const int64_t n = 16 * nb + r16;
+      const float swn = a.w.scales[n];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int p = redi[0][t][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) p += redi[w][t][lane];
+        const int64_t m = 4 * j + t;
+        if (m >= a.M) continue;
+        if (a.ksplit > 1) {
+          reinterpret_cast<int32_t*>(a.workspace)[((int64_t)blockIdx.y * a.M + m) * a.N + n] = p;
+          continue;
+        }
+        if (DEBUG && a.partials && m >= a.m_begin && m < a.m_end) a.partials[(m - a.m_begin) * a.N + n] = p;
+        float sam;
+        if constexpr (FUSED)
+          sam = s_sa[m];
+        else
+          sam = a.sa[m];
+        if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(sam * (swn * (float)p));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t) red[wave][t][lane] = accf[t];
   __syncthreads();
@@ -373,6 +427,22 @@ splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __re
   y[t] = f32_to_bf16_rne(sa[m] * v);
 }
 
+// W8A8 split-K: the exact int32 totals summed over the slices (order-free),
+// then y[m][n] = bf16(sa[m] * (sw[n] * P)); totals also written for rows in
+// [m_begin, m_end) when asked.
+__global__ void __launch_bounds__(256)
+w8_splitk_reduce_kernel(const int32_t* __restrict__ ws, int ksplit, const float* __restrict__ sa,
+                        const float* __restrict__ sw, int64_t M, int64_t N, uint16_t* __restrict__ y,
+                        int32_t* __restrict__ totals, int64_t m_begin, int64_t m_end) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M * N) return;
+  const int64_t m = t / N, n = t % N;
+  int p = ws[t];
+  for (int k = 1; k < ksplit; ++k) p += ws[k * M * N + t];
+  if (totals && m >= m_begin && m < m_end) totals[(m - m_begin) * N + n] = p;
+  if (y) y[t] = f32_to_bf16_rne(sa[m] * (sw[n] * (float)p));
+}
+
 // Split K only while the channel blocks alone leave compute units idle, and
 // never below one group per wavefront.
 int pick_ksplit(int64_t N, int64_t K) {
@@ -383,12 +453,12 @@ int pick_ksplit(int64_t N, int64_t K) {
   return ks;
 }
 
-template <int MP>
+template <int MP, bool W8>
 void launch_mp(const GemmArgs& a, dim3 grid, hipStream_t st) {
   if (a.partials)
-    hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, a);
 }
 
 // Chunks of eight activations per thread of the fused variant, or 0 when it
@@ -408,29 +478,48 @@ int fused_chunks(int64_t M, int64_t N, int64_t K, int x_dtype) {
   return per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : 10;
 }
 
-template <int MP, typename T>
+template <int MP, typename T, bool W8>
 void launch_fused_mp(const GemmArgs& a, dim3 grid, int npt, hipStream_t st) {
   const size_t lds = (size_t)(a.M * (a.K + 16) + 512);
   if (npt == 4)
-    hipLaunchKernelGGL((skinny_kernel<false, MP, 4, T>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 4, T, W8>), grid, dim3(kThreads), lds, st, a);
   else if constexpr (sizeof(T) == 2) {
     if (npt == 8)
-      hipLaunchKernelGGL((skinny_kernel<false, MP, 8, T>), grid, dim3(kThreads), lds, st, a);
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 8, T, W8>), grid, dim3(kThreads), lds, st, a);
     else
-      hipLaunchKernelGGL((skinny_kernel<false, MP, 10, T>), grid, dim3(kThreads), lds, st, a);
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 10, T, W8>), grid, dim3(kThreads), lds, st, a);
   }
 }
 
-template <typename T>
+template <typename T, bool W8>
 void launch_fused(const GemmArgs& a, dim3 grid, int npt, hipStream_t st) {
   if (a.M <= 2)
-    launch_fused_mp<2, T>(a, grid, npt, st);
+    launch_fused_mp<2, T, W8>(a, grid, npt, st);
   else if (a.M <= 4)
-    launch_fused_mp<4, T>(a, grid, npt, st);
+    launch_fused_mp<4, T, W8>(a, grid, npt, st);
   else if (a.M <= 8)
-    launch_fused_mp<8, T>(a, grid, npt, st);
+    launch_fused_mp<8, T, W8>(a, grid, npt, st);
   else
-    launch_fused_mp<16, T>(a, grid, npt, st);
+    launch_fused_mp<16, T, W8>(a, grid, npt, st);
+}
+
+template <bool W8>
+void launch_any(const GemmArgs& a, dim3 grid, hipStream_t st) {
+  if (a.x) {
+    const int npt = fused_chunks(a.M, a.N, a.K, a.x_dtype);
+    if (a.x_dtype == 0)
+      launch_fused<uint16_t, W8>(a, grid, npt, st);
+    else
+      launch_fused<float, W8>(a, grid, npt, st);
+  } else if (a.M <= 2) {
+    launch_mp<2, W8>(a, grid, st);
+  } else if (a.M <= 4) {
+    launch_mp<4, W8>(a, grid, st);
+  } else if (a.M <= 8) {
+    launch_mp<8, W8>(a, grid, st);
+  } else {
+    launch_mp<16, W8>(a, grid, st);
+  }
 }
 
 }  // namespace
@@ -446,22 +535,21 @@ hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
   a.gq = (int)(G / parts);
   a.gr = (int)(G % parts);
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
-  if (a.x) {
-    const int npt = fused_chunks(a.M, a.N, a.K, a.x_dtype);
-    if (npt == 0 || a.ksplit != 1 || a.partials) return hipErrorInvalidValue;
-    if (a.x_dtype == 0)
-      launch_fused<uint16_t>(a, grid, npt, st);
-    else
-      launch_fused<float>(a, grid, npt, st);
-  } else if (a.M <= 2) {
-    launch_mp<2>(a, grid, st);
-  } else if (a.M <= 4) {
-    launch_mp<4>(a, grid, st);
-  } else if (a.M <= 8) {
-    launch_mp<8>(a, grid, st);
-  } else {
-    launch_mp<16>(a, grid, st);
-  }
+  if (a.x && (fused_chunks(a.M, a.N, a.K, a.x_dtype) == 0 || a.ksplit != 1 || a.partials))
+    return hipErrorInvalidValue;
+  if (a.w8)
+    launch_any<true>(a, grid, st);
+  else
+    launch_any<false>(a, grid, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,
+                                   int64_t M, int64_t N, uint16_t* y, int32_t* totals,
+                                   int64_t m_begin, int64_t m_end, hipStream_t st) {
+  const int64_t total = M * N;
+  hipLaunchKernelGGL(w8_splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     st, ws, ksplit, sa, sw, M, N, y, totals, m_begin, m_end);
   return hipGetLastError();
 }
 

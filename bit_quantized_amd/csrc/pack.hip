@@ -97,6 +97,41 @@ unpack_meta_kernel(const uint8_t* __restrict__ zeros, const float* __restrict__ 
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// W8A8 weights: one thread per 16-byte run of a packed block.  Run t is
+// (block nb*G + g, half h, lane L = 16j + c) and holds qw[16nb+c][128g +
+// 64h + 16j .. +15]: the int8 codes of the MFMA B operand, copied as they are.
+__global__ void __launch_bounds__(256)
+w8_pack_codes_kernel(const int8_t* __restrict__ qw, int64_t K, int64_t G, int64_t runs,
+                     uint8_t* __restrict__ codes) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= runs) return;
+  const int64_t blk = t >> 7;
+  const int h = (int)((t >> 6) & 1), L = (int)(t & 63);
+  const int64_t nb = blk / G, g = blk % G;
+  const int j = L >> 4, c = L & 15;
+  const int8_t* src = qw + (16 * nb + c) * K + 128 * g + 64 * h + 16 * j;
+  *reinterpret_cast<uint4*>(codes + 16 * t) = *reinterpret_cast<const uint4*>(src);
+}
+
+__global__ void __launch_bounds__(256)
+w8_unpack_codes_kernel(const uint8_t* __restrict__ codes, int64_t K, int64_t G, int64_t runs,
+                       int8_t* __restrict__ qw) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= runs) return;
+  const int64_t blk = t >> 7;
+  const int h = (int)((t >> 6) & 1), L = (int)(t & 63);
+  const int64_t nb = blk / G, g = blk % G;
+  const int j = L >> 4, c = L & 15;
+  int8_t* dst = qw + (16 * nb + c) * K + 128 * g + 64 * h + 16 * j;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(codes + 16 * t);
+}
+
+__global__ void __launch_bounds__(256)
+copy_f32_kernel(const float* __restrict__ src, int64_t n, float* __restrict__ dst) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) dst[t] = src[t];
+}
+
 }  // namespace
 
 // Packs a [N_part][K] weight into channels [n_offset, n_offset + N_part) of a
@@ -147,6 +182,27 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q
   hipLaunchKernelGGL(unpack_meta_kernel, dim3(blocks_for(cells)), dim3(256), 0, st,
                      packed + zeros_offset(N, K),
                      reinterpret_cast<const float*>(packed + scales_offset(N, K)), G, cells, z, s);
+  return hipGetLastError();
+}
+
+// W8A8: codes plane [N/16][G][2][64][16] at 0, scales [N] at w8_scales_offset.
+hipError_t launch_w8_pack(const int8_t* qw, const float* sw, int64_t N, int64_t K, uint8_t* packed,
+                          hipStream_t st) {
+  const int64_t G = K / kGroup, runs = N * K / 16;
+  hipLaunchKernelGGL(w8_pack_codes_kernel, dim3(blocks_for(runs)), dim3(256), 0, st, qw, K, G, runs,
+                     packed);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(N)), dim3(256), 0, st, sw, N,
+                     reinterpret_cast<float*>(packed + w8_scales_offset(N, K)));
+  return hipGetLastError();
+}
+
+hipError_t launch_w8_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* qw, float* sw,
+                            hipStream_t st) {
+  const int64_t G = K / kGroup, runs = N * K / 16;
+  hipLaunchKernelGGL(w8_unpack_codes_kernel, dim3(blocks_for(runs)), dim3(256), 0, st, packed, K, G,
+                     runs, qw);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks_for(N)), dim3(256), 0, st,
+                     reinterpret_cast<const float*>(packed + w8_scales_offset(N, K)), N, sw);
   return hipGetLastError();
 }
 

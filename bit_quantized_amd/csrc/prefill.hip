@@ -32,7 +32,9 @@ constexpr int kAChunks = BM * kGroup / 16 / kThreads;  // 16-B activation chunks
 // earlier groups compute.
 struct Stage {
   v4i a[kAChunks];
-  v4i b;          // this thread's 16 packed bytes: block t/64, lane t%64
+  v4i b;          // W4: this thread's 16 packed bytes: block t/64, lane t%64
+                  // W8: half 0 of block t/64, lane t%64 (16 int8 weights)
+  v4i b8;         // W8: half 1 of the same block and lane
   uint32_t zb;    // the byte holding that lane's zero point
   float s;        // scale of channel t%16 of block (t/16)%8
 };
@@ -48,6 +50,7 @@ struct Offsets {
   int zshift;
 };
 
+template <bool W8>
 __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
                                                 int64_t NB, int64_t G) {
   const int tid = threadIdx.x;
@@ -58,7 +61,7 @@ __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, i
     o.a[i] = (uint32_t)(min(m0 + (ch >> 3), a.M - 1) * a.K + (ch & 7) * 16);
   }
   const int64_t nb = min(cb0 + (tid >> 6), NB - 1);
-  o.b = (uint32_t)(nb * G * kBlockBytes + (tid & 63) * 16);
+  o.b = (uint32_t)(nb * G * (W8 ? 2 : 1) * kBlockBytes + (tid & 63) * 16);
   o.z = (uint32_t)(nb * G * kZeroBlockBytes + ((tid & 15) >> 1));
   o.zshift = (tid & 1) * 4;
   const int64_t nbs = min(cb0 + ((tid >> 4) & (NCB - 1)), NB - 1);
@@ -66,29 +69,44 @@ __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, i
   return o;
 }
 
+template <bool W8>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
                                            Stage& st) {
   const int8_t* qa = a.qa + g * kGroup;
-  const uint8_t* codes = a.w.codes + g * kBlockBytes;
-  const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
-  const float* scales = a.w.scales + g * 16;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) st.a[i] = *reinterpret_cast<const v4i*>(qa + o.a[i]);
-  st.b = *reinterpret_cast<const v4i*>(codes + o.b);
-  st.zb = zeros[o.z];
-  st.s = scales[o.s];
+  if constexpr (W8) {
+    const uint8_t* codes = a.w.codes + g * 2 * kBlockBytes;
+    st.b = *reinterpret_cast<const v4i*>(codes + o.b);
+    st.b8 = *reinterpret_cast<const v4i*>(codes + o.b + kBlockBytes);
+  } else {
+    const uint8_t* codes = a.w.codes + g * kBlockBytes;
+    const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
+    const float* scales = a.w.scales + g * 16;
+    st.b = *reinterpret_cast<const v4i*>(codes + o.b);
+    st.zb = zeros[o.z];
+    st.s = scales[o.s];
+  }
 }
 
 // Stage -> LDS.  The packed codes are unpacked here, once per workgroup, to
 // signed q - z bytes in exactly the order the MFMA B operand is read: block
 // u, half h (low nibbles = input channels 16j..16j+15 of the group, high =
 // 64+16j..), lane L.
+template <bool W8>
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int ch = tid + kThreads * i;
     *reinterpret_cast<v4i*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
+  }
+  if constexpr (W8) {
+    // the packed halves are already the MFMA B operand: copied as they are
+    const int u = tid >> 6, L = tid & 63;
+    *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = st.b;
+    *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = st.b8;
+    return;
   }
   const uint32_t zz = ((st.zb >> zshift) & 0xFu) * 0x01010101u;
   v4i lo, hi;
@@ -118,6 +136,37 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
 
 // One group on the matrix cores: fragments from LDS, the 16 tiles' MFMA
 // pairs, and the per-group rescale into the fp32 accumulators.
+template <bool DEBUG>
+__device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* buf, int64_t g,
+                                              int64_t m0, int64_t cb0, int64_t NB, int64_t G,
+                                              float (&accf)[4][4][4]);
+
+// W8: one group's MFMA pairs into the int32 totals (no per-group rescale).
+__device__ __forceinline__ void compute_group_w8(const uint8_t* buf, v4i (&acci)[16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  v4i b0[4], b1[4], a0[4], a1[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int cb = wn * 4 + u;
+    b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
+    b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
+    a0[i] = *reinterpret_cast<const v4i*>(arow);
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int i = t >> 2, u = t & 3;
+    acci[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], acci[t], 0, 0, 0);
+    acci[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acci[t], 0, 0, 0);
+  }
+}
+
 template <bool DEBUG>
 __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* buf, int64_t g,
                                               int64_t m0, int64_t cb0, int64_t NB, int64_t G,
@@ -171,7 +220,10 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
   }
 }
 
-template <bool DEBUG>
+// W8: the W8A8 weights (two 1 KiB halves per block, already in MFMA operand
+// order, one scale per channel).  Each group's products accumulate in int32
+// over the workgroup's whole K slice, and the scales are applied once.
+template <bool DEBUG, bool W8>
 __global__ void __launch_bounds__(kThreads)
 prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
@@ -196,30 +248,70 @@ prefill_kernel(GemmArgs a) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
+  v4i acci[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acci[t] = v4i{0, 0, 0, 0};
+  auto compute = [&](const uint8_t* buf, int64_t g) __attribute__((always_inline)) {
+    if constexpr (W8)
+      compute_group_w8(buf, acci);
+    else
+      compute_group<DEBUG>(a, buf, g, m0, cb0, NB, G, accf);
+  };
 
   // One group of 128 input channels per step: the operands of group g + 2
   // are loaded while group g computes and group g + 1 (loaded one step
   // earlier) is unpacked into the idle LDS buffer.  The two register stages
   // alternate, so the loop is unrolled by two.
 
-  const Offsets off = make_offsets(a, m0, cb0, NB, G);
+  const Offsets off = make_offsets<W8>(a, m0, cb0, NB, G);
   Stage s0, s1;
-  load_stage(a, off, gb, s0);
-  load_stage(a, off, min(gb + 1, ge - 1), s1);
-  store_stage(smem[0], s0, off.zshift);
+  load_stage<W8>(a, off, gb, s0);
+  load_stage<W8>(a, off, min(gb + 1, ge - 1), s1);
+  store_stage<W8>(smem[0], s0, off.zshift);
   __syncthreads();
   for (int64_t g = gb; g < ge; g += 2) {
     // (the last steps re-read group ge - 1 into stages nobody consumes, which
     // keeps each half free of branches)
-    load_stage(a, off, min(g + 2, ge - 1), s0);
-    compute_group<DEBUG>(a, smem[0], g, m0, cb0, NB, G, accf);
-    store_stage(smem[1], s1, off.zshift);  // buffer 1 was last read before the previous barrier
+    load_stage<W8>(a, off, min(g + 2, ge - 1), s0);
+    compute(smem[0], g);
+    store_stage<W8>(smem[1], s1, off.zshift);  // buffer 1 was last read before the previous barrier
     __syncthreads();
     if (g + 1 >= ge) break;
-    load_stage(a, off, min(g + 3, ge - 1), s1);
-    compute_group<DEBUG>(a, smem[1], g + 1, m0, cb0, NB, G, accf);
-    store_stage(smem[0], s0, off.zshift);
+    load_stage<W8>(a, off, min(g + 3, ge - 1), s1);
+    compute(smem[1], g + 1);
+    store_stage<W8>(smem[0], s0, off.zshift);
     __syncthreads();
+  }
+
+  if constexpr (W8) {
+    // int32 totals: to the workspace when K is split, else scaled to y (and
+    // written out for the debug row window)
+    float swv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) swv[u] = a.w.scales[min(cb0 + wn * 4 + u, NB - 1) * 16 + r16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+        if (m >= a.M) continue;
+        const float sam = gridDim.y > 1 ? 0.0f : a.sa[m];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t nb = cb0 + wn * 4 + u;
+          if (nb >= NB) continue;
+          const int64_t n = nb * 16 + r16;
+          const int p = acci[i * 4 + u][r];
+          if (gridDim.y > 1) {
+            reinterpret_cast<int32_t*>(a.workspace)[((int64_t)blockIdx.y * a.M + m) * a.N + n] = p;
+            continue;
+          }
+          if (DEBUG && a.partials && m >= a.m_begin && m < a.m_end)
+            a.partials[(m - a.m_begin) * a.N + n] = p;
+          if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(sam * (swv[u] * (float)p));
+        }
+      }
+    return;
   }
 
   if (gridDim.y > 1) {
@@ -277,10 +369,16 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
   const int64_t NB = a.N / kBlockCols;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((NB + NCB - 1) / NCB);
   const dim3 grid((unsigned)tiles, (unsigned)a.ksplit);
-  if (a.partials)
-    hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  if (a.w8) {
+    if (a.partials)
+      hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
+  } else if (a.partials) {
+    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

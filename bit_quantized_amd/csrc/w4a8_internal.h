@@ -30,6 +30,10 @@ inline int64_t scales_offset(int64_t N, int64_t K) {
 inline int64_t packed_bytes(int64_t N, int64_t K) {
   return scales_offset(N, K) + 4 * N * (K / kGroup);
 }
+// W8A8 packed weights: int8 codes [N/16][K/128][2 halves][64 lanes][16 B],
+// then one float scale per channel.
+inline int64_t w8_scales_offset(int64_t N, int64_t K) { return round_up256(N * K); }
+inline int64_t w8_packed_bytes(int64_t N, int64_t K) { return w8_scales_offset(N, K) + 4 * N; }
 
 // ---------------------------------------------------------------- device helpers
 
@@ -106,6 +110,10 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q
                          float* s, hipStream_t st);
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
                         hipStream_t st);
+hipError_t launch_w8_pack(const int8_t* qw, const float* sw, int64_t N, int64_t K, uint8_t* packed,
+                          hipStream_t st);
+hipError_t launch_w8_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* qw, float* sw,
+                            hipStream_t st);
 
 struct GemmArgs {
   const int8_t* qa;       // quantised activations [M][K] (null when x is quantised in-kernel)
@@ -123,6 +131,8 @@ struct GemmArgs {
   int cb, ks;             // GEMV: workgroups along N, wavefronts per workgroup
   int cb_q, cb_r;         // GEMV: N/16 = cb_q * cb + cb_r (set by the launcher)
   int gq, gr;             // skinny: G = gq * (ksplit * 16) + gr (set by the launcher)
+  bool w8;                // W8A8 weights (codes [N/16][G][2][1024], scales [N]); partials
+                          // are then the int32 totals [m_end-m_begin][N]
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
@@ -147,5 +157,8 @@ hipError_t launch_skinny(GemmArgs a, hipStream_t st);
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st);
+hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,
+                                   int64_t M, int64_t N, uint16_t* y, int32_t* totals,
+                                   int64_t m_begin, int64_t m_end, hipStream_t st);
 
 }  // namespace w4a8

@@ -192,18 +192,106 @@ int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
  * quantisation (the rule of w4a8_quant_act) followed by the GEMM of
  * w4a8_gemm.  For M == 1 (and K <= 32768) both run in ONE launch: the decode
  * GEMV quantises the token in its prologue, so a decode step has no separate
- * quantisation kernel.  Otherwise the codes are written to the workspace and
- * the GEMM of the selected path follows (two launches).  The result is
- * bitwise identical to w4a8_quant_act followed by w4a8_gemm.
+ * quantisation kernel.  For 2 <= M <= 16 it is also one launch when the rows
+ * fit: M*(K+16) <= 128 KiB, at most 10240*8/MP bf16 (4096*8/MP float) values
+ * per row with MP = M rounded up to a power of two >= 2, and N large enough
+ * that K is not split; the SKINNY kernel then quantises the rows into LDS.
+ * Otherwise the codes are written to the workspace and the GEMM of the
+ * selected path follows (two launches).  The result is bitwise identical to
+ * w4a8_quant_act followed by w4a8_gemm.
  *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
  *   y   device bfloat16 bits [M][N]
  *   workspace  device scratch of w4a8_linear_workspace_bytes(M, N, K, group)
- *     bytes (may be NULL when that is 0)
+ *     bytes (may be NULL when that is 0), required at that size on every path
  */
 size_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes,
                 int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ W8A8
+ *
+ * The W8A8 int8-dynamic linear ("Serve a pre-quantized int8 weight-only DiT
+ * ...", comment "Round two ...": int8 weights, activations quantised to int8
+ * at run time, an integer matrix product scaled afterwards; the comment's
+ * kernel check compares against a float reference that carries the
+ * activation scale).  Weights are symmetric int8 with one float scale per
+ * output channel, W[n][k] = sw[n] * qw[n][k]; activations use the rule of
+ * w4a8_quant_act.  The product over all of K is exact in int32:
+ *   P[m][n] = sum_k qa[m][k] * qw[n][k]      (K <= 131072, so |P| < 2^31)
+ *   y[m][n] = bf16_rne( sa[m] * (sw[n] * (float)P[m][n]) )
+ * As P is exact and the epilogue is fixed, y is the same bits on every path.
+ * Shapes: N % 16 == 0, K % 128 == 0, 0 < K <= 131072 (else
+ * W4A8_ERR_UNSUPPORTED_SHAPE).  The status codes, alignment, stream and
+ * ownership conventions are those of the W4A8 calls above.
+ */
+#define W8A8_LAYOUT_VERSION 1
+
+int w8a8_layout_version(void);
+
+/* Size in bytes of the packed W8A8 weight buffer; 0 if the shape is unsupported. */
+size_t w8a8_packed_weight_bytes(int64_t N, int64_t K);
+
+/*
+ * w8a8_pack_weights — load-time conversion into the packed W8A8 format.
+ *   qw  device int8 [N][K], row-major
+ *   sw  device float [N], per-channel scales (copied bit for bit)
+ *   packed  device buffer of at least w8a8_packed_weight_bytes(N, K)
+ * Format (W8A8 layout version 1; G = K/128, NB = N/16), two planes:
+ *   codes,  N*K bytes at offset 0: block (nb, g) is 2048 bytes at
+ *     (nb*G + g)*2048; half h (0, 1) at +1024*h; lane L = 16*j + c
+ *     (j = 0..3, c = 0..15) at +16*L; byte i of that run is
+ *     qw[16nb+c][128g + 64h + 16j + i].  A lane's 16 bytes are its operand
+ *     of one v_mfma_i32_16x16x64_i8 step as loaded.
+ *   scales, 4*N bytes at round_up(N*K, 256) = N*K: float sw[n] at index n.
+ * w8a8_unpack_weights is the exact inverse (qw [N][K], sw [N]).
+ */
+int w8a8_pack_weights(const int8_t* qw, const float* sw, int64_t N, int64_t K, void* packed,
+                      size_t packed_bytes, void* stream);
+int w8a8_unpack_weights(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* qw,
+                        float* sw, void* stream);
+
+/* Path for an M x N x K W8A8 product: W4A8_PATH_SKINNY for M <= 16 (M == 1
+ * included), W4A8_PATH_PREFILL otherwise. */
+int w8a8_select_path(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w8a8_gemm — y from pre-quantised activations.
+ *   qa  device int8 [M][K] and sa device float [M] (from w4a8_quant_act)
+ *   packed  from w8a8_pack_weights for the same (N, K)
+ *   y   device bfloat16 bits [M][N]
+ *   workspace  device scratch of w8a8_gemm_workspace_bytes(M, N, K) bytes
+ *     (int32 split-K partials; may be NULL when that is 0)
+ */
+size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int w8a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
+              int64_t M, int64_t N, int64_t K, uint16_t* y, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * w8a8_gemm_debug — the same kernels with a forced path (AUTO, SKINNY for
+ * M <= 16, or PREFILL) and the exact int32 totals written for rows
+ * [m_begin, m_end):  totals device int32 [m_end - m_begin][N] (may be NULL);
+ * y_or_null as in w4a8_gemm_debug.
+ */
+int w8a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
+                    int64_t M, int64_t N, int64_t K, int32_t path, int64_t m_begin, int64_t m_end,
+                    int32_t* totals, uint16_t* y_or_null, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * w8a8_linear — quantisation (the rule of w4a8_quant_act) and the W8A8 GEMM
+ * from raw activations; bitwise identical to w4a8_quant_act + w8a8_gemm.
+ * For M <= 16 whose rows fit (the same limits as w4a8_linear) it is one
+ * launch: the kernel quantises the rows into LDS itself.
+ *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
+ *   workspace  device scratch of w8a8_linear_workspace_bytes(M, N, K) bytes,
+ *     required on every path
+ */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int w8a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes, int64_t M,
+                int64_t N, int64_t K, uint16_t* y, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 #ifdef __cplusplus
 }

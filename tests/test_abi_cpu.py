@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "w4a8.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:w4a8|w8a8)_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -149,3 +149,79 @@ def test_pack_into_rejections(lib):
     assert f(FAKE, FAKE, FAKE, 20, 128, 128, FAKE2, big, 64, 0, None) == -2     # part tail
     pb = lib.w4a8_packed_weight_bytes(64, 128, 128)
     assert f(FAKE, FAKE, FAKE, 16, 128, 128, FAKE2, pb - 1, 64, 0, None) == -4  # sized for N_total
+
+
+# ------------------------------------------------------------------ W8A8
+
+@pytest.mark.parametrize("N,K", [(16, 128), (512, 3584), (3584, 18944), (48, 384)])
+def test_w8_packed_size_matches_spec(lib, N, K):
+    assert lib.w8a8_packed_weight_bytes(N, K) == oracle.w8_layout_bytes(N, K)
+
+
+def test_w8_packed_size_unsupported(lib):
+    assert lib.w8a8_packed_weight_bytes(84, 128) == 0
+    assert lib.w8a8_packed_weight_bytes(64, 100) == 0
+    assert lib.w8a8_packed_weight_bytes(16, 131072 + 128) == 0       # exact int32 totals
+    assert lib.w8a8_packed_weight_bytes(16, 131072) > 0
+    assert lib.w8a8_layout_version() == 1
+
+
+def test_w8_pack_rejections(lib):
+    f = lib.w8a8_pack_weights
+    pb = lib.w8a8_packed_weight_bytes(32, 256)
+    assert f(None, FAKE, 32, 256, FAKE2, pb, None) == -1
+    assert f(FAKE, FAKE, 32, 250, FAKE2, pb, None) == -2
+    assert f(FAKE, FAKE, 32, 131200, FAKE2, 1 << 40, None) == -2
+    assert f(MIS, FAKE, 32, 256, FAKE2, pb, None) == -3
+    assert f(FAKE, FAKE2, 32, 256, FAKE2, pb, None) == -1                # packed aliases sw
+    assert f(FAKE, FAKE2, 32, 256, ctypes.c_void_p(1 << 26), pb - 16, None) == -4
+    u = lib.w8a8_unpack_weights
+    assert u(FAKE, pb - 1, 32, 256, FAKE2, ctypes.c_void_p(1 << 26), None) == -4
+    assert u(FAKE, pb, 32, 256, FAKE2, FAKE2, None) == -1                 # qw aliases sw
+
+
+def test_w8_gemm_rejections(lib):
+    f = lib.w8a8_gemm
+    pb = lib.w8a8_packed_weight_bytes(256, 256)
+    y = ctypes.c_void_p(1 << 28)
+    assert f(None, FAKE, FAKE2, pb, 4, 256, 256, y, None, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE2, pb, 0, 256, 256, y, None, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 250, 256, y, None, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE2, pb - 16, 4, 256, 256, y, None, 0, None) == -4
+    assert f(FAKE, MIS, FAKE2, pb, 4, 256, 256, y, None, 0, None) == -3
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, FAKE2, None, 0, None) == -1   # y aliases packed
+    # small N with long K splits K on the M <= 16 path: the int32 partials
+    # need a workspace (device_cus() reads 256 when no device is present)
+    pb2 = lib.w8a8_packed_weight_bytes(512, 18944)
+    need = lib.w8a8_gemm_workspace_bytes(1, 512, 18944)
+    assert need >= 2 * 512 * 4
+    assert f(FAKE, FAKE, FAKE2, pb2, 1, 512, 18944, y, None, 0, None) == -4
+    # (the M <= 16 kernel splits K four ways here: 4 x 1 x 512 int32 partials)
+    assert f(FAKE, FAKE, FAKE2, pb2, 1, 512, 18944, y, ctypes.c_void_p(1 << 32), 4 * 512 * 4 - 16,
+             None) == -4
+    assert lib.w8a8_gemm_workspace_bytes(1, 18944, 3584) == 0
+
+
+def test_w8_debug_and_path_rejections(lib):
+    f = lib.w8a8_gemm_debug
+    pb = lib.w8a8_packed_weight_bytes(256, 256)
+    y = ctypes.c_void_p(1 << 28)
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 1, 0, 4, None, y, None, 0, None) == -1   # no GEMV
+    assert f(FAKE, FAKE, FAKE2, pb, 17, 256, 256, 2, 0, 17, None, y, None, 0, None) == -1  # SKINNY M
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 0, 2, 5, None, y, None, 0, None) == -1   # window
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 7, 0, 4, None, y, None, 0, None) == -1   # enum
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 0, 0, 4, MIS, y, None, 0, None) == -3
+    assert lib.w8a8_select_path(1, 18944, 3584) == 2
+    assert lib.w8a8_select_path(16, 3584, 18944) == 2
+    assert lib.w8a8_select_path(17, 3584, 18944) == 3
+
+
+def test_w8_linear_rejections(lib):
+    f = lib.w8a8_linear
+    pb = lib.w8a8_packed_weight_bytes(256, 256)
+    y = ctypes.c_void_p(1 << 28)
+    assert f(None, 0, FAKE2, pb, 1, 256, 256, y, None, 0, None) == -1
+    assert f(FAKE, 5, FAKE2, pb, 1, 256, 256, y, None, 0, None) == -1
+    assert f(FAKE, 0, FAKE2, pb, 1, 250, 256, y, None, 0, None) == -2
+    assert f(FAKE, 0, FAKE2, pb, 4, 256, 256, y, None, 0, None) == -4       # needs workspace
+    assert lib.w8a8_linear_workspace_bytes(4, 256, 256) >= 4 * 256 + 16
