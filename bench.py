@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the skinny and layer legs")
-    p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "copy"],
+    p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "w8a8", "copy"],
                    default="all", help="run one part only (for hardware-counter passes)")
     return p.parse_args()
 
@@ -247,6 +247,65 @@ def bench_prefill(torch, w4, args):
                      "ops_per_launch": ops, "avg_launch_us": round(kern_ms * 1e3, 2),
                      "timing": f"{n} launches replayed from one HIP graph"},
     }
+
+
+def w8_bytes(M, N, K, act_bytes=2):
+    """Bytes the W8A8 linear must move: int8 weights, per-channel scales,
+    activations in, bf16 output out."""
+    return N * K + 4 * N + act_bytes * M * K + 2 * M * N
+
+
+def bench_w8a8(torch, w4, args):
+    """W8A8 int8-dynamic linear: decode (M=1) and skinny (M=4, 16) against the
+    HBM roofline, prefill (M=2048) against int8 MFMA peak; each checked
+    against the oracle before timing."""
+    import oracle
+    from bit_quantized_amd import synth
+    out = []
+    cases = [(synth.LinearSpec("w8_decode_up", 1, 3584, 18944, seed=1), 16),
+             (synth.LinearSpec("w8_skinny_down_m4", 4, 18944, 3584, seed=2), 16),
+             (synth.LinearSpec("w8_skinny_down_m16", 16, 18944, 3584, seed=2), 16),
+             (synth.LinearSpec("w8_prefill_up", 2048, 3584, 18944, seed=3), 4)]
+    for spec, copies in cases:
+        lin = synth.make_w8_linear(spec)
+        qw, sw = to_dev(torch, lin["qw"]), to_dev(torch, lin["sw"])
+        Ws = [w4.w8a8_pack_weights(qw, sw) for _ in range(copies)]
+        del qw, sw
+        x = x_dev(torch, lin)
+        M, K, N = spec.M, spec.K, spec.N
+        rows = (0, min(M, 16))
+        y = w4.w8a8_linear(x, Ws[0])
+        qa_ref, sa_ref = oracle.quant_act(lin["x"])
+        ref = oracle.w8a8_linear(qa_ref, sa_ref, lin["qw"], lin["sw"], rows=rows)
+        ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy()[rows[0]:rows[1]], ref)
+        if not ok:
+            raise SystemExit(f"parity check failed ({spec.name}): {err:.3e} > {bound:.3e}")
+        R = len(Ws)
+        ws = torch.empty(max(w4.w8a8_linear_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
+                         device="cuda")
+        n = 64 if M <= 16 else args.prefill_steps
+        step_ms = graph_steps_ms(torch, lambda i: w4.w8a8_linear(x, Ws[i % R], out=y, workspace=ws),
+                                 max(2, n // 4), n) / n
+        qa, sa = w4.quant_act(x)
+        gws = torch.empty(max(w4.w8a8_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+        gemm_ms = graph_launches_ms(torch, lambda i: w4.w8a8_gemm(qa, sa, Ws[i % R], out=y,
+                                                                  workspace=gws), n)
+        r = {"workload": f"{spec.name} M={M} K={K} N={N} (W8A8: quant + int8 GEMM)",
+             "path": {2: "skinny", 3: "prefill"}[w4.w8a8_select_path(M, N, K)],
+             "us_per_step": round(step_ms * 1e3, 3), "gemm_us": round(gemm_ms * 1e3, 3),
+             "parity": {"rows": list(rows), "max_err": err, "bound": bound}}
+        if M <= 16:
+            b = w8_bytes(M, N, K)
+            r.update({"bytes_per_step": b, "GBps": round(b / (step_ms * 1e-3) / 1e9, 1),
+                      "frac": round(b / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        else:
+            ops = 2.0 * M * N * K
+            r.update({"ops": ops, "TOPS_step": round(ops / (step_ms * 1e-3) / 1e12, 1),
+                      "TOPS_gemm": round(ops / (gemm_ms * 1e-3) / 1e12, 1),
+                      "frac_gemm": round(ops / (gemm_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)})
+        out.append(r)
+        del Ws
+    return out
 
 
 def bench_skinny(torch, w4, args):
@@ -475,7 +534,7 @@ def main():
         copy_calibration(torch)
         return
 
-    dec = pre = skinny = layer = None
+    dec = pre = skinny = layer = w8 = None
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
@@ -484,6 +543,8 @@ def main():
         skinny = bench_skinny(torch, w4, args)
     if args.only == "layer" or (args.only == "all" and not args.no_extra):
         layer = bench_layer(torch, w4, args)
+    if args.only == "w8a8" or (args.only == "all" and not args.no_extra):
+        w8 = bench_w8a8(torch, w4, args)
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline and args.only == "all":
         if dec:
@@ -500,6 +561,8 @@ def main():
             out["skinny"] = skinny
         if layer:
             out["layer"] = layer
+        if w8:
+            out["w8a8"] = w8
         print(json.dumps(out))
         return
     spec = dec["spec"]
@@ -536,6 +599,8 @@ def main():
         line["skinny"] = skinny
     if layer:
         line["layer"] = layer
+    if w8:
+        line["w8a8"] = w8
     line["system"] = gpu_info(torch)
     print(json.dumps(line))
 

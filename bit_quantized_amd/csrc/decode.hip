@@ -273,6 +273,11 @@ skinny_kernel(GemmArgs a) {
     if constexpr (W8) {
       acci = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, __builtin_bit_cast(v4i, w[0]), acci, 0, 0, 0);
       acci = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, __builtin_bit_cast(v4i, w[1]), acci, 0, 0, 0);
+      // The running total is otherwise only read after the loop, so the
+      // compiler sinks every product there and keeps all slots' operands
+      // live; an empty statement that reads and writes it pins each unit's
+      // products in place (no instruction is emitted).
+      asm volatile("" : "+v"(acci));
       return;
     }
     const float s = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_s + 64 * i, (int)sc));
@@ -470,7 +475,7 @@ constexpr int64_t kFusedLdsBytes = 128 * 1024;
 int pow2_rows(int64_t M) { return M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
 int fused_chunks(int64_t M, int64_t N, int64_t K, int x_dtype) {
-  if (M < 2 || M > 16 || pick_ksplit(N, K) != 1) return 0;
+  if (M < 1 || M > 16 || pick_ksplit(N, K) != 1) return 0;
   if (M * (K + 16) + 512 > kFusedLdsBytes) return 0;
   const int64_t per_thread = (K / 8 + kThreads / pow2_rows(M) - 1) / (kThreads / pow2_rows(M));
   const int64_t limit = x_dtype == 0 ? 10 : 4;

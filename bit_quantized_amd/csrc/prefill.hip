@@ -165,6 +165,11 @@ __device__ __forceinline__ void compute_group_w8(const uint8_t* buf, v4i (&acci)
     acci[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], acci[t], 0, 0, 0);
     acci[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acci[t], 0, 0, 0);
   }
+  // the totals are otherwise only read after the loop, and the compiler would
+  // sink every group's products there; reading and writing them in an empty
+  // statement keeps this group's products here (no instruction is emitted)
+#pragma unroll
+  for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(acci[t]));
 }
 
 template <bool DEBUG>
