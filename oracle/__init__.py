@@ -65,6 +65,8 @@ def load(mutant: int = 0) -> ctypes.CDLL:
         "oracle_layout_pack": [vp, vp, vp, i64, i64, vp],
         "oracle_layout_unpack": [vp, i64, i64, vp, vp, vp],
         "oracle_w8a8_totals": [vp, vp, i64, i64, i64, i64, i64, vp],
+        "oracle_hadamard_rows": [vp, i32, i64, i64, vp],
+        "oracle_hadamard_quant_act": [vp, i32, i64, i64, vp, vp],
         "oracle_w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp],
         "oracle_w8_layout_pack": [vp, vp, i64, i64, vp],
         "oracle_w8_layout_unpack": [vp, i64, i64, vp, vp],
@@ -107,6 +109,34 @@ def quant_act(x: np.ndarray, mutant: int = 0):
         _check(lib.oracle_quant_act_bf16(_ptr(x), M, K, _ptr(qa), _ptr(sa)), "quant_act_bf16")
     else:
         raise TypeError(x.dtype)
+    return qa, sa
+
+
+def hadamard_rows(x, mutant: int = 0):
+    """Rows rotated group by group by the unnormalised 128 x 128 Walsh-Hadamard
+    matrix, in float32 by the butterflies of increasing stride."""
+    lib = load(mutant)
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    if x.dtype not in (np.float32, np.uint16):
+        raise TypeError(x.dtype)
+    xr = np.empty((M, K), np.float32)
+    _check(lib.oracle_hadamard_rows(_ptr(x), int(x.dtype == np.uint16), M, K, _ptr(xr)),
+           "hadamard_rows")
+    return xr
+
+
+def hadamard_quant_act(x, mutant: int = 0):
+    """Rotation, then the per-token quantisation: (qa int8, sa float32)."""
+    lib = load(mutant)
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    if x.dtype not in (np.float32, np.uint16):
+        raise TypeError(x.dtype)
+    qa = np.empty((M, K), np.int8)
+    sa = np.empty((M,), np.float32)
+    _check(lib.oracle_hadamard_quant_act(_ptr(x), int(x.dtype == np.uint16), M, K, _ptr(qa),
+                                         _ptr(sa)), "hadamard_quant_act")
     return qa, sa
 
 

@@ -409,3 +409,62 @@ int oracle_w8_layout_unpack(const uint8_t* in, int64_t N, int64_t K, int8_t* qw,
     for (int64_t n = 0; n < N; ++n) sw[n] = sb[n];
     return ORACLE_OK;
 }
+
+/*
+ * Online Hadamard rotation before the per-token quantisation.  "EgoPQ
+ * Real-Serving Handoff", section "1. Source Checkpoint", serves a packed
+ * QuaRot model, and section "2. External Artifacts" exports it from QuaRot
+ * caches; the page names the method and nothing more.  QuaRot (the published
+ * method) multiplies activations by a Hadamard matrix before quantising them
+ * and folds the inverse rotation into the weights, so that a few large
+ * channels no longer set a whole token's absmax.  Readings taken (each also
+ * listed in the design doc):
+ *   - the rotation is block-diagonal over the quantisation groups: every
+ *     group of 128 input channels is multiplied by the 128 x 128
+ *     Walsh-Hadamard matrix H (Sylvester order, H[i][j] = (-1)^popcount(i&j)),
+ *     unnormalised; the factor 1/128 of H * H^T = 128 I belongs to the
+ *     weights (W' = W H / 128), since per-token quantisation is blind to a
+ *     common scale;
+ *   - the product is taken in float32 by the radix-2 butterflies in order of
+ *     increasing stride h = 1, 2, 4, ..., 64, each pair (i, i + h) becoming
+ *     (a + b, a - b); the kernel takes the same steps, so the rotated values,
+ *     and hence the codes, agree bit for bit;
+ *   - then the quantisation rule of quant_row, on the rotated row.
+ */
+static void fwht128(float* v) {
+    for (int h = 1; h < 128; h *= 2)
+        for (int i0 = 0; i0 < 128; i0 += 2 * h)
+            for (int i = i0; i < i0 + h; ++i) {
+                float a = v[i], b = v[i + h];
+#if ORACLE_MUTANT == 9
+                v[i] = a + b;                      /* planted: upper half not negated */
+                v[i + h] = a + b;
+#else
+                v[i] = a + b;
+                v[i + h] = a - b;
+#endif
+            }
+}
+
+/* x float32 or bfloat16 bits (is_bf16) [M][K] -> rotated float32 rows xr [M][K]. */
+int oracle_hadamard_rows(const void* x, int is_bf16, int64_t M, int64_t K, float* xr) {
+    if (!x || !xr || M < 0 || K <= 0 || K % 128) return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            xr[m * K + k] = is_bf16 ? widen_bf16(((const uint16_t*)x)[m * K + k])
+                                    : ((const float*)x)[m * K + k];
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < K / 128; ++g) fwht128(xr + m * K + 128 * g);
+    return ORACLE_OK;
+}
+
+int oracle_hadamard_quant_act(const void* x, int is_bf16, int64_t M, int64_t K, int8_t* qa,
+                              float* sa) {
+    if (!x || !qa || !sa || M < 0 || K <= 0 || K % 128) return ORACLE_BAD_ARG;
+    float* xr = (float*)malloc((size_t)(M * K) * sizeof(float) + 1);
+    if (!xr) return ORACLE_BAD_ARG;
+    int rc = oracle_hadamard_rows(x, is_bf16, M, K, xr);
+    if (rc == ORACLE_OK) rc = oracle_quant_act_f32(xr, M, K, qa, sa);
+    free(xr);
+    return rc;
+}

@@ -14,7 +14,11 @@
   forms, the float64 result against numpy dequant-then-matmul, and the exact
   agreement with the W4A8 oracle on weights both can express (int8 weights
   q - z with a per-channel scale repeated over every group);
-- the W8A8 packed layout against hand-worked bytes and a round trip.
+- the W8A8 packed layout against hand-worked bytes and a round trip;
+- for the online Hadamard rotation: unit rows give the rows of the
+  Sylvester matrix (closed form), rotating twice gives 128 x the input
+  (H H = 128 I) exactly on integer rows, and the float32 result matches a
+  float64 block-diagonal matrix product within float32 rounding.
 
 Every pin is a plain function taking ``mutant``; ``test_mutants_are_caught``
 rebuilds the oracle with one planted mistake at a time and checks that at
@@ -232,9 +236,58 @@ def pin_w8_equals_w4_special_case(mutant=0):
     assert np.array_equal(P4, oracle.w8a8_totals(qa, qw, mutant=mutant).astype(np.int64))
 
 
+def _sylvester(n):
+    i = np.arange(n)
+    return np.array([[(-1) ** bin(a & b).count("1") for b in i] for a in i], np.float64)
+
+
+def pin_hadamard_unit_rows(mutant=0):
+    """A unit row e_k (k in group g) becomes row k % 128 of H in group g."""
+    K = 384
+    H = _sylvester(128)
+    ks = [0, 1, 5, 64, 127, 130, 255, 300]
+    x = np.zeros((len(ks), K), np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    xr = oracle.hadamard_rows(x, mutant=mutant)
+    for r, k in enumerate(ks):
+        g = k // 128
+        want = np.zeros(K)
+        want[128 * g:128 * g + 128] = H[k % 128]
+        assert np.array_equal(xr[r].astype(np.float64), want), k
+
+
+def pin_hadamard_twice(mutant=0):
+    """H H = 128 I: on small integer rows (exact in float32) rotating twice
+    returns 128 x the row, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    x = rng.integers(-100, 101, size=(3, 256)).astype(np.float32)
+    twice = oracle.hadamard_rows(oracle.hadamard_rows(x, mutant=mutant), mutant=mutant)
+    assert np.array_equal(twice, 128.0 * x)
+
+
+def pin_hadamard_matmul(mutant=0):
+    """Float32 butterflies against a float64 block-diagonal product, from bf16
+    and float32 inputs; the codes are the quantiser's on the rotated rows."""
+    rng = np.random.Generator(np.random.PCG64(42))
+    H = _sylvester(128)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    x[:, 77] *= 20.0
+    for xin in (x, synth.bf16_round_bits(x)):
+        xr = oracle.hadamard_rows(xin, mutant=mutant).astype(np.float64)
+        x64 = synth.bf16_bits_to_f32(xin).astype(np.float64) if xin.dtype == np.uint16 else \
+            xin.astype(np.float64)
+        ref = np.concatenate([x64[:, 128 * g:128 * g + 128] @ H for g in range(4)], axis=1)
+        assert np.max(np.abs(xr - ref)) <= 1e-5 * np.max(np.abs(ref))
+        qa, sa = oracle.hadamard_quant_act(xin, mutant=mutant)
+        qa2, sa2 = oracle.quant_act(oracle.hadamard_rows(xin, mutant=mutant), mutant=mutant)
+        assert np.array_equal(qa, qa2) and np.array_equal(sa, sa2)
+
+
 PINS = [pin_quant_golden, pin_quant_invariants, pin_partials_brute, pin_zero_shift_and_identity,
         pin_zero_weights, pin_group_permutation, pin_dequant_matmul, pin_identity_scale,
-        pin_w8_totals_brute, pin_w8_dequant_matmul, pin_w8_equals_w4_special_case]
+        pin_w8_totals_brute, pin_w8_dequant_matmul, pin_w8_equals_w4_special_case,
+        pin_hadamard_unit_rows, pin_hadamard_twice, pin_hadamard_matmul]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -244,7 +297,8 @@ def test_pin(pin):
 
 MUTANTS = {1: "zero point dropped", 2: "ties away from zero", 3: "scale absmax/128",
            4: "zero plane transposed", 5: "activation scale missing", 6: "weights shifted by one k",
-           7: "W8A8 weight scale dropped", 8: "W8A8 weights read unsigned"}
+           7: "W8A8 weight scale dropped", 8: "W8A8 weights read unsigned",
+           9: "Hadamard upper half not negated"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=[MUTANTS[m] for m in sorted(MUTANTS)])
