@@ -53,6 +53,10 @@ SIGNATURES = {
     "w4a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz,
                                    _vp]),
+    "w4a8_quant_act_hadamard": (ctypes.c_int, [_vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "w4a8_linear_hadamard_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "w4a8_linear_hadamard": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp,
+                                            _sz, _vp]),
     "w8a8_layout_version": (ctypes.c_int, []),
     "w8a8_packed_weight_bytes": (_sz, [_i64, _i64]),
     "w8a8_pack_weights": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
@@ -220,6 +224,47 @@ def quant_act(x: torch.Tensor, qa: torch.Tensor | None = None, sa: torch.Tensor 
     sa = torch.empty((M,), dtype=torch.float32, device=x.device) if sa is None else sa
     _check(lib.w4a8_quant_act(_p(x), dt, M, K, _p(qa), _p(sa), _stream(x.device)))
     return qa, sa
+
+
+def quant_act_hadamard(x: torch.Tensor, qa: torch.Tensor | None = None,
+                       sa: torch.Tensor | None = None):
+    """Online Hadamard rotation (each group of 128 by the unnormalised
+    Walsh-Hadamard matrix) and the per-token quantisation."""
+    lib = load()
+    _need_cuda(x)
+    M, K = x.shape
+    if x.dtype == torch.bfloat16:
+        dt = BF16
+    elif x.dtype == torch.float32:
+        dt = F32
+    else:
+        raise TypeError(x.dtype)
+    qa = torch.empty((M, K), dtype=torch.int8, device=x.device) if qa is None else qa
+    sa = torch.empty((M,), dtype=torch.float32, device=x.device) if sa is None else sa
+    _check(lib.w4a8_quant_act_hadamard(_p(x), dt, M, K, _p(qa), _p(sa), _stream(x.device)))
+    return qa, sa
+
+
+def linear_hadamard(x: torch.Tensor, w: PackedWeight, out=None, workspace=None) -> torch.Tensor:
+    """The layer with the online rotation: rotated quantisation, then the GEMM
+    against a weight packed from W H / 128."""
+    lib = load()
+    w.check()
+    _need_cuda(x, out)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    dt = BF16 if x.dtype == torch.bfloat16 else F32 if x.dtype == torch.float32 else None
+    if dt is None:
+        raise TypeError(x.dtype)
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    need = int(lib.w4a8_linear_hadamard_workspace_bytes(M, w.N, w.K, w.group))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(lib.w4a8_linear_hadamard(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group,
+                                    _p(out), _p(workspace), wsb, _stream(x.device)))
+    return out
 
 
 def workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:

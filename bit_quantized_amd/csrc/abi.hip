@@ -427,8 +427,8 @@ int w4a8_unpack_weights(const void* packed, size_t packed_bytes_, int64_t N, int
                        "unpack launch");
 }
 
-int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
-                   void* stream) {
+static int quant_act_any(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa,
+                         float* sa, void* stream, bool hadamard) {
   if (!x || !qa || !sa) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
   if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
     return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
@@ -443,8 +443,19 @@ int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t*
       overlaps(qa, (size_t)M * K, sa, (size_t)M * 4))
     return fail(W4A8_ERR_INVALID_ARG, "outputs alias the input or each other");
   (void)hipGetLastError();
-  return device_status(launch_quant(x, x_dtype, M, K, qa, sa, static_cast<hipStream_t>(stream)),
-                       "quant launch");
+  return device_status(
+      launch_quant(x, x_dtype, M, K, qa, sa, static_cast<hipStream_t>(stream), hadamard),
+      "quant launch");
+}
+
+int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
+                   void* stream) {
+  return quant_act_any(x, x_dtype, M, K, qa, sa, stream, false);
+}
+
+int w4a8_quant_act_hadamard(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa,
+                            float* sa, void* stream) {
+  return quant_act_any(x, x_dtype, M, K, qa, sa, stream, true);
 }
 
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
@@ -517,6 +528,47 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (rc) return rc;
   return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group,
                   W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
+}
+
+// The layer with the online rotation: rotated quantisation into the
+// workspace, then the GEMM of w4a8_gemm against weights that carry the
+// inverse rotation (two launches on every path).
+size_t w4a8_linear_hadamard_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (check_weight_shape(N, K, group) || M <= 0) return 0;
+  return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+}
+
+int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed,
+                         size_t packed_bytes_, int64_t M, int64_t N, int64_t K, int32_t group,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (!x || !y) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
+    return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  const size_t need = round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const size_t xbytes = (size_t)M * K * (x_dtype == W4A8_F32 ? 4 : 2);
+  if (overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, packed, packed_bytes_))
+    return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
+  if (overlaps(y, (size_t)M * N * 2, x, xbytes))
+    return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* qa = reinterpret_cast<int8_t*>(ws);
+  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
+  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
+  rc = run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
+                0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+                /*validate_only=*/true);
+  if (rc) return rc;
+  rc = w4a8_quant_act_hadamard(x, x_dtype, M, K, qa, sa, stream);
+  if (rc) return rc;
+  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
+                  0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
 // ------------------------------------------------------------------ W8A8

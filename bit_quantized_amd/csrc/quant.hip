@@ -51,6 +51,37 @@ __device__ __forceinline__ uint2 quant8(const float* v, float amax, float scale)
   return amax != 0.0f ? quant8_codes(v, scale, 1.0f / scale) : make_uint2(0u, 0u);
 }
 
+// Online Hadamard rotation of one chunk of eight, in place: this thread's
+// chunk is chunk (threadIdx.x & 15) of a group of 128 input channels whose
+// other 15 chunks sit in the neighbouring threads of the same 16-lane row.
+// The group is multiplied by the unnormalised 128 x 128 Walsh-Hadamard
+// matrix (Sylvester order) by radix-2 butterflies of increasing stride
+// h = 1, ..., 64, each pair (i, i + h) becoming (a + b, a - b): strides below
+// 8 inside the chunk, the rest across lanes.  Every element sees the same
+// float32 operations in the same order as the straightforward in-place
+// transform, so the rotated values are exact reproductions of it.
+__device__ __forceinline__ void hadamard_chunk(float* v) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  const int pos = threadIdx.x & 15;
+#pragma unroll
+  for (int d = 1; d < 16; d *= 2) {  // stride 8 d: the partner chunk is lane ^ d
+    const bool upper = (pos & d) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float u = __shfl_xor(v[i], d);
+      v[i] = upper ? u - v[i] : v[i] + u;
+    }
+  }
+}
+
 // Row maximum over the block's wavefronts (all threads get it).
 template <int THREADS>
 __device__ __forceinline__ float block_max(float amax, float* red) {
@@ -64,7 +95,9 @@ __device__ __forceinline__ float block_max(float amax, float* red) {
 }
 
 // Long rows: the row is read twice (maximum, then codes) in a strided loop.
-template <typename T>
+// HAD: rotated first (recomputed identically in the second pass); the
+// stride of 256 chunks keeps every group in one 16-lane row.
+template <typename T, bool HAD>
 __global__ void __launch_bounds__(kQuantThreads)
 quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
                  float* __restrict__ sa) {
@@ -77,6 +110,7 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   for (int64_t ch = threadIdx.x; ch < chunks; ch += kQuantThreads) {
     float v[8];
     Chunk8<T>::load(row + ch * 8, v);
+    if (HAD) hadamard_chunk(v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
@@ -88,6 +122,7 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   for (int64_t ch = threadIdx.x; ch < chunks; ch += kQuantThreads) {
     float v[8];
     Chunk8<T>::load(row + ch * 8, v);
+    if (HAD) hadamard_chunk(v);
     *reinterpret_cast<uint2*>(out + ch * 8) = quant8(v, amax, scale);
   }
 }
@@ -98,7 +133,7 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
 // blocks run and each one's latency is the whole cost).
 constexpr int kRowThreads = 1024;
 
-template <typename T, int NPT>
+template <typename T, int NPT, bool HAD>
 __global__ void __launch_bounds__(kRowThreads)
 quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
                  float* __restrict__ sa) {
@@ -118,6 +153,13 @@ quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
       for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
     }
   }
+  if (HAD) {
+    // whole groups are either all present or all absent (K % 128 == 0), so
+    // the lanes of a group agree on every branch here
+#pragma unroll
+    for (int c = 0; c < NPT; ++c)
+      if (threadIdx.x + c * kRowThreads < chunks) hadamard_chunk(v[c]);
+  }
 #pragma unroll
   for (int c = 0; c < NPT; ++c)
 #pragma unroll
@@ -133,31 +175,38 @@ quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   }
 }
 
-template <typename T>
+template <typename T, bool HAD>
 void launch_typed(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipStream_t st) {
   const int64_t chunks = K / 8;
   const dim3 grid((unsigned)M);
   // many rows fill the machine by themselves; few rows want one round trip each
   if (M > 64 || chunks > 8 * kRowThreads)
-    hipLaunchKernelGGL(quant_act_kernel<T>, grid, dim3(kQuantThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_act_kernel<T, HAD>), grid, dim3(kQuantThreads), 0, st, x, K, qa, sa);
   else if (chunks <= kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 1>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 1, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
   else if (chunks <= 2 * kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 2>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 2, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
   else if (chunks <= 4 * kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 4>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 4, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
   else
-    hipLaunchKernelGGL((quant_row_kernel<T, 8>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 8, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
 }
 
 }  // namespace
 
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
-                        hipStream_t st) {
-  if (x_dtype == 0)
-    launch_typed(static_cast<const uint16_t*>(x), M, K, qa, sa, st);
-  else
-    launch_typed(static_cast<const float*>(x), M, K, qa, sa, st);
+                        hipStream_t st, bool hadamard) {
+  if (x_dtype == 0) {
+    if (hadamard)
+      launch_typed<uint16_t, true>(static_cast<const uint16_t*>(x), M, K, qa, sa, st);
+    else
+      launch_typed<uint16_t, false>(static_cast<const uint16_t*>(x), M, K, qa, sa, st);
+  } else {
+    if (hadamard)
+      launch_typed<float, true>(static_cast<const float*>(x), M, K, qa, sa, st);
+    else
+      launch_typed<float, false>(static_cast<const float*>(x), M, K, qa, sa, st);
+  }
   return hipGetLastError();
 }
 

@@ -108,8 +108,10 @@ hipError_t launch_pack_into(const uint8_t* q, const uint8_t* z, const float* s, 
                             hipStream_t st);
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q, uint8_t* z,
                          float* s, hipStream_t st);
+// hadamard: rotate every group of 128 by the unnormalised Walsh-Hadamard
+// matrix before quantising (the online rotation of QuaRot).
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
-                        hipStream_t st);
+                        hipStream_t st, bool hadamard = false);
 hipError_t launch_w8_pack(const int8_t* qw, const float* sw, int64_t N, int64_t K, uint8_t* packed,
                           hipStream_t st);
 hipError_t launch_w8_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* qw, float* sw,

@@ -209,6 +209,36 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
                 int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------- online rotation
+ *
+ * The per-token quantisation preceded by an online Hadamard rotation, as in
+ * the packed QuaRot model of "EgoPQ Real-Serving Handoff" (section "1.
+ * Source Checkpoint"; its caches in section "2. External Artifacts"): the
+ * rotation spreads a token's few large channels over the group, so they no
+ * longer set the token's absmax.  Each group of 128 input channels of every
+ * row is multiplied by the unnormalised 128 x 128 Walsh-Hadamard matrix H
+ * (Sylvester order, H[i][j] = (-1)^popcount(i & j)), in float32, by the
+ * radix-2 butterflies of increasing stride 1, 2, ..., 64 (pair (i, i + h)
+ * becomes (a + b, a - b)); the rotated row is then quantised by the rule of
+ * w4a8_quant_act.  Weights used with it must carry the inverse rotation
+ * W' = W H / 128 (group by group), made offline.
+ */
+
+/* Arguments as w4a8_quant_act; K % 128 == 0. */
+int w4a8_quant_act_hadamard(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa,
+                            float* sa, void* stream);
+
+/*
+ * w4a8_linear_hadamard — w4a8_quant_act_hadamard into the workspace, then
+ * w4a8_gemm with weights packed from the rotated W' (two launches on every
+ * path).  Arguments as w4a8_linear; workspace of
+ * w4a8_linear_hadamard_workspace_bytes(M, N, K, group) bytes.
+ */
+size_t w4a8_linear_hadamard_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes,
+                         int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ W8A8
  *
  * The W8A8 int8-dynamic linear ("Serve a pre-quantized int8 weight-only DiT

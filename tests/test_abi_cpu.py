@@ -225,3 +225,22 @@ def test_w8_linear_rejections(lib):
     assert f(FAKE, 0, FAKE2, pb, 1, 250, 256, y, None, 0, None) == -2
     assert f(FAKE, 0, FAKE2, pb, 4, 256, 256, y, None, 0, None) == -4       # needs workspace
     assert lib.w8a8_linear_workspace_bytes(4, 256, 256) >= 4 * 256 + 16
+
+
+def test_hadamard_rejections(lib):
+    f = lib.w4a8_quant_act_hadamard
+    assert f(None, 0, 4, 256, FAKE2, FAKE, None) == -1
+    assert f(FAKE, 3, 4, 256, FAKE2, ctypes.c_void_p(1 << 26), None) == -1
+    assert f(FAKE, 0, 4, 200, FAKE2, ctypes.c_void_p(1 << 26), None) == -2
+    assert f(MIS, 0, 4, 256, FAKE2, ctypes.c_void_p(1 << 26), None) == -3
+    g = lib.w4a8_linear_hadamard
+    pb = lib.w4a8_packed_weight_bytes(256, 256, 128)
+    y = ctypes.c_void_p(1 << 28)
+    need = lib.w4a8_linear_hadamard_workspace_bytes(1, 256, 256, 128)
+    assert need >= 256 + 4
+    assert g(FAKE, 0, FAKE2, pb, 1, 256, 256, 128, y, None, 0, None) == -4     # codes need room
+    assert g(FAKE, 0, FAKE2, pb, 1, 256, 256, 128, y, ctypes.c_void_p(1 << 32), need - 16,
+             None) == -4
+    assert g(FAKE, 0, FAKE2, pb - 16, 1, 256, 256, 128, y, ctypes.c_void_p(1 << 32), need,
+             None) == -4
+    assert g(FAKE, 0, FAKE2, pb, 1, 256, 256, 64, y, ctypes.c_void_p(1 << 32), need, None) == -2
