@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the skinny and layer legs")
-    p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "w8a8", "copy"],
+    p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "w8a8", "hadamard",
+                                      "copy"],
                    default="all", help="run one part only (for hardware-counter passes)")
     return p.parse_args()
 
@@ -308,6 +309,60 @@ def bench_w8a8(torch, w4, args):
     return out
 
 
+def _rtn_int4(w):
+    """Round-to-nearest asymmetric int4 per group of 128 (offline weight
+    preparation for the accuracy comparison only): codes, zeros, scales."""
+    N, K = w.shape
+    g = w.reshape(N, K // 128, 128)
+    lo, hi = g.min(axis=2), g.max(axis=2)
+    s = np.maximum((hi - lo) / 15.0, 1e-12)
+    z = np.clip(np.rint(-lo / s), 0, 15)
+    q = np.clip(np.rint(g / s[:, :, None]) + z[:, :, None], 0, 15)
+    return (q.reshape(N, K).astype(np.uint8), z.astype(np.uint8), s.astype(np.float32))
+
+
+def bench_hadamard(torch, w4, args):
+    """Online Hadamard rotation + quantisation: its cost against the plain
+    quantiser (M = 1, 4, 2048), and what it buys on activations with a few
+    large channels: the layer's error against a float64 product, with and
+    without the rotation (weights rounded to int4 per group either way, the
+    rotated ones from W H / 128)."""
+    from bit_quantized_amd import synth
+    res = {"timing": []}
+    for M, K in ((1, 3584), (4, 18944), (2048, 3584)):
+        lin = synth.make_linear(synth.LinearSpec("had", M, K, 16, seed=5), with_weights=False)
+        x = x_dev(torch, lin)
+        qa = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        sa = torch.empty((M,), dtype=torch.float32, device="cuda")
+        n = 64
+        plain = graph_launches_ms(torch, lambda i: w4.quant_act(x, qa, sa), n)
+        rot = graph_launches_ms(torch, lambda i: w4.quant_act_hadamard(x, qa, sa), n)
+        res["timing"].append({"M": M, "K": K, "quant_us": round(plain * 1e3, 3),
+                              "hadamard_quant_us": round(rot * 1e3, 3),
+                              "bytes": M * K * 3 + 4 * M})
+    # accuracy: 7B-shaped down projection input with 0.5 % of channels x 20
+    M, K, N = 16, 3584, 2048
+    lin = synth.make_linear(synth.LinearSpec("had_acc", M, K, N, seed=6))
+    rng = np.random.Generator(np.random.PCG64(7))
+    wf = rng.standard_normal((N, K)) * 0.02
+    H = np.array([[(-1) ** bin(a & b).count("1") for b in range(128)] for a in range(128)], np.float64)
+    wr = np.concatenate([wf[:, 128 * g:128 * g + 128] @ H / 128.0 for g in range(K // 128)], axis=1)
+    xf = synth.x_as_f32(lin).astype(np.float64)
+    y_ref = xf @ wf.T
+    x = x_dev(torch, lin)
+    errs = {}
+    for name, wmat, fn in (("plain", wf, w4.linear), ("hadamard", wr, w4.linear_hadamard)):
+        q, z, s = _rtn_int4(wmat)
+        W = w4.pack_weights(to_dev(torch, q), to_dev(torch, z), to_dev(torch, s))
+        y = fn(x, W).float().cpu().numpy().astype(np.float64)
+        errs[name] = float(np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref))
+    res["accuracy"] = {"workload": f"M={M} K={K} N={N}, bf16 N(0,1) activations, 0.5% channels x20, "
+                                   "weights N(0, 0.02) rounded to int4 per group",
+                       "rel_l2_error_plain": round(errs["plain"], 5),
+                       "rel_l2_error_hadamard": round(errs["hadamard"], 5)}
+    return res
+
+
 def bench_skinny(torch, w4, args):
     """Skinny decode (2 <= M <= 16): K=18944 -> N=3584, as quant + GEMM
     through w4a8_linear, against the HBM roofline."""
@@ -534,7 +589,7 @@ def main():
         copy_calibration(torch)
         return
 
-    dec = pre = skinny = layer = w8 = None
+    dec = pre = skinny = layer = w8 = had = None
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
@@ -545,6 +600,8 @@ def main():
         layer = bench_layer(torch, w4, args)
     if args.only == "w8a8" or (args.only == "all" and not args.no_extra):
         w8 = bench_w8a8(torch, w4, args)
+    if args.only == "hadamard" or (args.only == "all" and not args.no_extra):
+        had = bench_hadamard(torch, w4, args)
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline and args.only == "all":
         if dec:
@@ -563,6 +620,8 @@ def main():
             out["layer"] = layer
         if w8:
             out["w8a8"] = w8
+        if had:
+            out["hadamard"] = had
         print(json.dumps(out))
         return
     spec = dec["spec"]
@@ -601,6 +660,8 @@ def main():
         line["layer"] = layer
     if w8:
         line["w8a8"] = w8
+    if had:
+        line["hadamard"] = had
     line["system"] = gpu_info(torch)
     print(json.dumps(line))
 

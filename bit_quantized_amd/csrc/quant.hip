@@ -51,6 +51,30 @@ __device__ __forceinline__ uint2 quant8(const float* v, float amax, float scale)
   return amax != 0.0f ? quant8_codes(v, scale, 1.0f / scale) : make_uint2(0u, 0u);
 }
 
+// v of lane (lane ^ d) for d = 1, 2, 4, 8, within each 16-lane row, by DPP
+// moves (no LDS traffic).  Only symmetric lane maps are used, so the result
+// does not depend on the direction conventions of shifts: quad permutations
+// [1,0,3,2] and [2,3,0,1] for d = 1, 2; for d = 4 a mirror of each 8-lane
+// half (p -> 7 - p) and then a reversal of each quad: position p of a half
+// reads mirror position 7 - q(p), q(p) = (p & 4) | (3 - (p & 3)), which is
+// p ^ 4; for d = 8 a rotation of the 16-lane row by half its length.
+__device__ __forceinline__ float lane_xor_in_row(float v, int d) {
+  constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kQuadReverse = 0x1B;
+  constexpr int kRowHalfMirror = 0x141, kRowRotate8 = 0x128;
+  int x = __float_as_int(v);
+  if (d == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, kQuadSwap1, 0xF, 0xF, true);
+  } else if (d == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, kQuadSwap2, 0xF, 0xF, true);
+  } else if (d == 4) {
+    x = __builtin_amdgcn_mov_dpp(x, kRowHalfMirror, 0xF, 0xF, true);
+    x = __builtin_amdgcn_mov_dpp(x, kQuadReverse, 0xF, 0xF, true);
+  } else {
+    x = __builtin_amdgcn_mov_dpp(x, kRowRotate8, 0xF, 0xF, true);
+  }
+  return __int_as_float(x);
+}
+
 // Online Hadamard rotation of one chunk of eight, in place: this thread's
 // chunk is chunk (threadIdx.x & 15) of a group of 128 input channels whose
 // other 15 chunks sit in the neighbouring threads of the same 16-lane row.
@@ -76,7 +100,7 @@ __device__ __forceinline__ void hadamard_chunk(float* v) {
     const bool upper = (pos & d) != 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float u = __shfl_xor(v[i], d);
+      const float u = lane_xor_in_row(v[i], d);
       v[i] = upper ? u - v[i] : v[i] + u;
     }
   }
@@ -127,13 +151,12 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   }
 }
 
-// Rows of up to 8 * kRowThreads * NPT activations: every thread loads its NPT
+// Rows of up to 8 * THREADS * NPT activations: every thread loads its NPT
 // chunks of eight at once and keeps them in registers, so the row is read
-// once and the block waits for memory once (the small-M case, where only M
-// blocks run and each one's latency is the whole cost).
-constexpr int kRowThreads = 1024;
-
-template <typename T, int NPT, bool HAD>
+// once (and rotated once) and the block waits for memory once.  1024
+// threads per row serve few rows, where each block's latency is the whole
+// cost; 256 serve many rows, which fill the machine by themselves.
+template <typename T, int NPT, bool HAD, int kRowThreads>
 __global__ void __launch_bounds__(kRowThreads)
 quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
                  float* __restrict__ sa) {
@@ -175,21 +198,30 @@ quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   }
 }
 
+template <typename T, bool HAD, int THREADS>
+void launch_rows(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipStream_t st) {
+  const int64_t chunks = K / 8;
+  const dim3 grid((unsigned)M), block(THREADS);
+  if (chunks <= THREADS)
+    hipLaunchKernelGGL((quant_row_kernel<T, 1, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+  else if (chunks <= 2 * THREADS)
+    hipLaunchKernelGGL((quant_row_kernel<T, 2, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+  else if (chunks <= 4 * THREADS)
+    hipLaunchKernelGGL((quant_row_kernel<T, 4, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+  else
+    hipLaunchKernelGGL((quant_row_kernel<T, 8, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+}
+
 template <typename T, bool HAD>
 void launch_typed(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipStream_t st) {
   const int64_t chunks = K / 8;
-  const dim3 grid((unsigned)M);
-  // many rows fill the machine by themselves; few rows want one round trip each
-  if (M > 64 || chunks > 8 * kRowThreads)
-    hipLaunchKernelGGL((quant_act_kernel<T, HAD>), grid, dim3(kQuantThreads), 0, st, x, K, qa, sa);
-  else if (chunks <= kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 1, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
-  else if (chunks <= 2 * kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 2, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
-  else if (chunks <= 4 * kRowThreads)
-    hipLaunchKernelGGL((quant_row_kernel<T, 4, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+  if (M <= 64 && chunks <= 8 * 1024)
+    launch_rows<T, HAD, 1024>(x, M, K, qa, sa, st);
+  else if (M > 64 && chunks <= 8 * 256)
+    launch_rows<T, HAD, 256>(x, M, K, qa, sa, st);
   else
-    hipLaunchKernelGGL((quant_row_kernel<T, 8, HAD>), grid, dim3(kRowThreads), 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_act_kernel<T, HAD>), dim3((unsigned)M), dim3(kQuantThreads), 0, st, x,
+                       K, qa, sa);
 }
 
 }  // namespace

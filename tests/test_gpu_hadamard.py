@@ -52,7 +52,8 @@ def x_tensor(x):
 HAD_CASES = [(1, 3584, "bf16_outliers"), (3, 8192, "bf16_outliers"), (2, 8320, "f32"),
              (4, 18944, "bf16_outliers"), (5, 32896, "f32"), (1, 65536, "bf16_outliers"),
              (2, 65664, "bf16_outliers"), (65, 1024, "f32"), (300, 3584, "bf16_outliers"),
-             (2048, 3584, "bf16_outliers")]
+             (2048, 3584, "bf16_outliers"), (100, 8192, "f32"), (80, 16384, "bf16_outliers"),
+             (70, 16512, "bf16_outliers")]
 
 
 @pytest.mark.parametrize("M,K,act", HAD_CASES, ids=[f"M{m}_K{k}_{a[:4]}" for m, k, a in HAD_CASES])

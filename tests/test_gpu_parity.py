@@ -114,11 +114,16 @@ def test_quant_bit_exact(w4, spec):
 
 
 # Row lengths on both sides of each register-resident variant's limit (1, 2,
-# 4 and 8 chunks of eight per thread of a 1024-thread block), the strided
-# two-pass kernel past them, and M on both sides of the few-rows limit.
+# 4 and 8 chunks of eight per thread of a 1024-thread block for up to 64
+# rows, of a 256-thread block beyond), the strided two-pass kernel past them,
+# and M on both sides of the few-rows limit.
 QUANT_EDGES = [(3, 8192, "bf16_outliers"), (2, 8320, "bf16_outliers"), (5, 16384, "f32"),
                (5, 16512, "f32"), (4, 32896, "bf16_outliers"), (1, 65536, "bf16_outliers"),
-               (2, 65664, "f32"), (64, 1152, "bf16_outliers"), (65, 256, "bf16_outliers")]
+               (2, 65664, "f32"), (64, 1152, "bf16_outliers"), (65, 256, "bf16_outliers"),
+               # many rows: 256 threads per row, 2, 4 and 8 chunks per thread, then
+               # the two-pass kernel past 16384 values
+               (300, 3584, "bf16_outliers"), (100, 8192, "f32"), (70, 16384, "bf16_outliers"),
+               (66, 16512, "bf16_outliers")]
 
 
 @pytest.mark.parametrize("M,K,act", QUANT_EDGES, ids=[f"M{m}_K{k}_{a[:4]}" for m, k, a in QUANT_EDGES])
