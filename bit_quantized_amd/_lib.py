@@ -133,12 +133,14 @@ def packed_weight_bytes(N: int, K: int, group: int = GROUP) -> int:
     return int(load().w4a8_packed_weight_bytes(N, K, group))
 
 
-def pack_weights(q: torch.Tensor, z: torch.Tensor, s: torch.Tensor, group: int = GROUP,
+def pack_weights(q: torch.Tensor, z: torch.Tensor | None, s: torch.Tensor, group: int = GROUP,
                  out: torch.Tensor | None = None) -> PackedWeight:
-    """q uint8 [N][K] codes 0..15, z uint8 [N][K/group], s float32 [N][K/group]."""
+    """q uint8 [N][K] codes 0..15, z uint8 [N][K/group] (None: the symmetric
+    grid, every zero point 8), s float32 [N][K/group]."""
     lib = load()
     _need_cuda(q, z, s)
-    if q.dtype != torch.uint8 or z.dtype != torch.uint8 or s.dtype != torch.float32:
+    if q.dtype != torch.uint8 or (z is not None and z.dtype != torch.uint8) or \
+            s.dtype != torch.float32:
         raise TypeError("q, z must be uint8 and s float32")
     N, K = q.shape
     nbytes = lib.w4a8_packed_weight_bytes(N, K, group)

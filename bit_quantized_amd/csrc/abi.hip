@@ -389,7 +389,7 @@ int w4a8_pack_weights_into(const uint8_t* q, const uint8_t* z, const float* s, i
     return fail(W4A8_ERR_INVALID_ARG,
                 "channels [%lld, %lld) are not a 16-aligned range of the %lld packed ones",
                 (long long)n_offset, (long long)(n_offset + N_part), (long long)N_total);
-  if (!q || !z || !s || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!q || !s || !packed) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(q) || !aligned16(packed) || !aligned16(s))
     return fail(W4A8_ERR_MISALIGNED, "q, s and packed must be 16-byte aligned");
   const size_t need = (size_t)packed_bytes(N_total, K);
@@ -397,7 +397,7 @@ int w4a8_pack_weights_into(const uint8_t* q, const uint8_t* z, const float* s, i
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
   const size_t G = (size_t)(K / kGroup);
   if (overlaps(packed, need, q, (size_t)(N_part * K)) ||
-      overlaps(packed, need, z, (size_t)N_part * G) ||
+      (z && overlaps(packed, need, z, (size_t)N_part * G)) ||
       overlaps(packed, need, s, (size_t)N_part * G * 4))
     return fail(W4A8_ERR_INVALID_ARG, "packed buffer aliases an input");
   (void)hipGetLastError();

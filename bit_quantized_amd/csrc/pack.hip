@@ -44,8 +44,9 @@ pack_meta_kernel(const uint8_t* __restrict__ z, const float* __restrict__ s, int
   const int64_t n = 16 * nb + c;
   scales[t] = s[n * G + g];
   if ((c & 1) == 0) {
-    uint32_t lo = z[n * G + g] & 0xFu;
-    uint32_t hi = z[(n + 1) * G + g] & 0xFu;
+    // no zero points: the symmetric grid, every zero point 8
+    uint32_t lo = z ? z[n * G + g] & 0xFu : 8u;
+    uint32_t hi = z ? z[(n + 1) * G + g] & 0xFu : 8u;
     zeros[blk * kZeroBlockBytes + (c >> 1)] = (uint8_t)(lo | (hi << 4));
   }
 }

@@ -86,7 +86,10 @@ size_t w4a8_packed_weight_bytes(int64_t N, int64_t K, int32_t group);
  * w4a8_pack_weights — load-time conversion of GPTQ metadata into the gfx950
  * packed format (layout version 1).
  *   q  device uint8 [N][K], int4 codes 0..15, one per byte, row-major
- *   z  device uint8 [N][K/group], integer zero points 0..15
+ *   z  device uint8 [N][K/group], integer zero points 0..15; or NULL for a
+ *      symmetric grid, where every zero point is the constant 8 ("The 4-bit
+ *      CPU path", section "W4A8": the kernel takes the checkpoint's zero
+ *      points when it has them and synthesises 8 otherwise)
  *   s  device float [N][K/group], per-group scales (copied bit for bit)
  *   packed  device buffer of at least w4a8_packed_weight_bytes(N, K, group)
  * Requirements: group == 128, K % 128 == 0, N % 16 == 0, N, K > 0.

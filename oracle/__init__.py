@@ -66,6 +66,7 @@ def load(mutant: int = 0) -> ctypes.CDLL:
         "oracle_layout_unpack": [vp, i64, i64, vp, vp, vp],
         "oracle_w8a8_totals": [vp, vp, i64, i64, i64, i64, i64, vp],
         "oracle_hadamard_rows": [vp, i32, i64, i64, vp],
+        "oracle_w4a16_linear": [vp, i32, vp, vp, vp, i64, i64, i64, i32, i64, i64, i64, i64, vp],
         "oracle_hadamard_quant_act": [vp, i32, i64, i64, vp, vp],
         "oracle_w8a8_linear": [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp],
         "oracle_w8_layout_pack": [vp, vp, i64, i64, vp],
@@ -224,6 +225,26 @@ def w8_layout_unpack(buf, N: int, K: int):
     sw = np.empty((N,), np.float32)
     _check(lib.oracle_w8_layout_unpack(_ptr(buf), N, K, _ptr(qw), _ptr(sw)), "w8_layout_unpack")
     return qw, sw
+
+
+def w4a16_linear(x, q, z, s, group=128, rows=None, cols=None, mutant: int = 0):
+    """W4A16: unrounded float64 y = sum_g s * sum_k x * (q - z), x as given
+    (float32, or uint16 bf16 bit patterns widened exactly)."""
+    lib = load(mutant)
+    x = np.ascontiguousarray(x)
+    if x.dtype not in (np.float32, np.uint16):
+        raise TypeError(x.dtype)
+    q = np.ascontiguousarray(q, np.uint8)
+    z = np.ascontiguousarray(z, np.uint8)
+    s = np.ascontiguousarray(s, np.float32)
+    M, K = x.shape
+    N = q.shape[0]
+    m0, m1 = rows if rows is not None else (0, M)
+    n0, n1 = cols if cols is not None else (0, N)
+    y = np.empty((m1 - m0, n1 - n0), np.float64)
+    _check(lib.oracle_w4a16_linear(_ptr(x), int(x.dtype == np.uint16), _ptr(q), _ptr(z), _ptr(s),
+                                   M, N, K, group, m0, m1, n0, n1, _ptr(y)), "w4a16_linear")
+    return y
 
 
 def threads() -> int:

@@ -468,3 +468,46 @@ int oracle_hadamard_quant_act(const void* x, int is_bf16, int64_t M, int64_t K, 
     free(xr);
     return rc;
 }
+
+/*
+ * W4A16 ("The 4-bit CPU path", section "W4A16": activations stay bf16 and
+ * multiply the same int4 weights, each weight being s * (q - z)).  Reading
+ * taken (also listed in the design doc): the activations enter as given (bf16
+ * widened exactly, or float32), no quantisation; per group the exact
+ * products x * (q - z) are summed, and y[m][n] = sum_g s[n][g] * that sum,
+ * all in float64 and not rounded.
+ */
+int oracle_w4a16_linear(const void* x, int is_bf16, const uint8_t* q, const uint8_t* z,
+                        const float* s, int64_t M, int64_t N, int64_t K, int32_t group,
+                        int64_t m0, int64_t m1, int64_t n0, int64_t n1, double* y) {
+    if (!x || !q || !z || !s || !y || group <= 0 || K % group) return ORACLE_BAD_ARG;
+    if (m0 < 0 || m1 > M || m0 > m1 || n0 < 0 || n1 > N || n0 > n1) return ORACLE_BAD_ARG;
+    int64_t G = K / group, W = n1 - n0;
+    int rc = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t n = n0; n < n1; ++n) {
+            double acc = 0.0;
+            for (int64_t g = 0; g < G; ++g) {
+                double p = 0.0;
+                int zero = zero_at(z, N, G, n, g);
+                for (int64_t k = g * group; k < (g + 1) * group; ++k) {
+                    double xv = is_bf16 ? (double)widen_bf16(((const uint16_t*)x)[m * K + k])
+                                        : (double)((const float*)x)[m * K + k];
+                    if (!isfinite(xv)) {
+#pragma omp atomic write
+                        rc = ORACLE_NONFINITE;
+                    }
+#if ORACLE_MUTANT == 10
+                    p += xv * (double)q[n * K + k];                 /* planted: zero point dropped */
+#else
+                    p += xv * ((double)q[n * K + k] - (double)zero);
+#endif
+                }
+                acc += (double)s[n * G + g] * p;
+            }
+            y[(m - m0) * W + (n - n0)] = acc;
+        }
+    }
+    return rc;
+}

@@ -396,6 +396,25 @@ def test_fused_skinny_zero_and_tie_rows(w4):
     assert not y_fused[1].float().abs().sum().item()
 
 
+@pytest.mark.parametrize("M", [1, 4, 300])
+def test_symmetric_grid(w4, M):
+    """Weights without zero points ("The 4-bit CPU path", section "W4A8": the
+    constant 8 is synthesised when a checkpoint has none): the packed bytes
+    are those of a zero plane of 8s, and every path computes q - 8."""
+    say(f"symmetric grid M={M}")
+    lin = synth.make_linear(synth.LinearSpec("sym", M, 1024, 512, seed=100 + M))
+    z8 = np.full_like(lin["z"], 8)
+    W = w4.pack_weights(dev(lin["q"]), None, dev(lin["s"]))
+    assert np.array_equal(W.buf.cpu().numpy(), oracle.layout_pack(lin["q"], z8, lin["s"]))
+    x = x_tensor(lin)
+    y = w4.linear(x, W)
+    qa_ref, sa_ref = oracle.quant_act(lin["x"])
+    m1 = min(M, 16)
+    ref = oracle.linear(qa_ref, sa_ref, lin["q"], z8, lin["s"], rows=(0, m1))
+    ok, err, bound = oracle.tolerance_ok(to_f32(y)[:m1], ref, REL)
+    assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+
+
 def test_gemv_partials_wide(w4):
     """GEMV partials where workgroup runs straddle channel blocks (N large
     enough for the balanced split) and where K is split across workgroups."""

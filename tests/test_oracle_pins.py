@@ -284,10 +284,43 @@ def pin_hadamard_matmul(mutant=0):
         assert np.array_equal(qa, qa2) and np.array_equal(sa, sa2)
 
 
+def pin_w4a16_dequant_matmul(mutant=0):
+    """W4A16 float64 result against numpy dequant-then-matmul (bf16 and f32
+    activations), with windows; zero weights give zeros."""
+    x, q, z, s = _tiny_case(seed=44, M=4, K=384, N=24)
+    w = np.repeat(s.astype(np.float64), 128, axis=1) * (
+        q.astype(np.float64) - np.repeat(z.astype(np.float64), 128, axis=1))
+    for xin in (x, synth.bf16_round_bits(x)):
+        x64 = synth.bf16_bits_to_f32(xin).astype(np.float64) if xin.dtype == np.uint16 else \
+            xin.astype(np.float64)
+        y = oracle.w4a16_linear(xin, q, z, s, mutant=mutant)
+        ref = x64 @ w.T
+        assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+        assert np.array_equal(oracle.w4a16_linear(xin, q, z, s, rows=(1, 3), cols=(2, 10),
+                                                  mutant=mutant), y[1:3, 2:10])
+    zq = np.broadcast_to(np.repeat(z, 128, axis=1), q.shape).astype(np.uint8)
+    assert not oracle.w4a16_linear(x, zq, z, s, mutant=mutant).any()
+
+
+def pin_w4a16_equals_w4a8_on_integer_rows(mutant=0):
+    """Integer activation rows with absmax 127 quantise to themselves with
+    scale 1, so W4A16 and W4A8 compute the same exact float64 values."""
+    rng = np.random.Generator(np.random.PCG64(45))
+    M, K, N = 3, 512, 32
+    xi = rng.integers(-127, 128, size=(M, K))
+    xi[:, 3] = -127
+    x = xi.astype(np.float32)
+    q, z, s = synth.draw_weights(rng, N, K)
+    qa, sa = oracle.quant_act(x, mutant=mutant)
+    assert np.array_equal(oracle.w4a16_linear(x, q, z, s, mutant=mutant),
+                          oracle.linear(qa, sa, q, z, s, mutant=mutant))
+
+
 PINS = [pin_quant_golden, pin_quant_invariants, pin_partials_brute, pin_zero_shift_and_identity,
         pin_zero_weights, pin_group_permutation, pin_dequant_matmul, pin_identity_scale,
         pin_w8_totals_brute, pin_w8_dequant_matmul, pin_w8_equals_w4_special_case,
-        pin_hadamard_unit_rows, pin_hadamard_twice, pin_hadamard_matmul]
+        pin_hadamard_unit_rows, pin_hadamard_twice, pin_hadamard_matmul, pin_w4a16_dequant_matmul,
+        pin_w4a16_equals_w4a8_on_integer_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -298,7 +331,7 @@ def test_pin(pin):
 MUTANTS = {1: "zero point dropped", 2: "ties away from zero", 3: "scale absmax/128",
            4: "zero plane transposed", 5: "activation scale missing", 6: "weights shifted by one k",
            7: "W8A8 weight scale dropped", 8: "W8A8 weights read unsigned",
-           9: "Hadamard upper half not negated"}
+           9: "Hadamard upper half not negated", 10: "W4A16 zero point dropped"}
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=[MUTANTS[m] for m in sorted(MUTANTS)])
