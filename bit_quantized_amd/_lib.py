@@ -57,6 +57,11 @@ SIGNATURES = {
     "w4a8_linear_hadamard_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "w4a8_linear_hadamard": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp,
                                             _sz, _vp]),
+    "w4a16_linear_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "w4a16_select_path": (ctypes.c_int, [_i64, _i64, _i64]),
+    "w4a16_linear": (ctypes.c_int, [_vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp, _sz, _vp]),
+    "w4a16_linear_path": (ctypes.c_int, [_vp, _vp, _sz, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz,
+                                         _vp]),
     "w8a8_layout_version": (ctypes.c_int, []),
     "w8a8_packed_weight_bytes": (_sz, [_i64, _i64]),
     "w8a8_pack_weights": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
@@ -465,4 +470,36 @@ def w8a8_linear(x: torch.Tensor, w: PackedW8, out=None, workspace=None) -> torch
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.w8a8_linear(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, _p(out),
                            _p(workspace), wsb, _stream(x.device)))
+    return out
+
+
+# ----------------------------------------------------------------- W4A16
+
+def w4a16_workspace_bytes(M: int, N: int, K: int, group: int = GROUP) -> int:
+    return int(load().w4a16_linear_workspace_bytes(M, N, K, group))
+
+
+def w4a16_select_path(M: int, N: int, K: int) -> int:
+    return int(load().w4a16_select_path(M, N, K))
+
+
+def w4a16_linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None,
+                 path: int = PATH_AUTO) -> torch.Tensor:
+    """W4A16: bf16 activations times the packed int4 weights (no activation
+    quantisation), bf16 out; `path` forces SKINNY or PREFILL."""
+    lib = load()
+    w.check()
+    _need_cuda(x, out)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("W4A16 takes bfloat16 activations")
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    need = w4a16_workspace_bytes(M, w.N, w.K, w.group)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w4a16_linear_path(_p(x), _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, path,
+                                 _p(out), _p(workspace), wsb, _stream(x.device)))
     return out

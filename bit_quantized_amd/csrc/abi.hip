@@ -222,6 +222,92 @@ size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
   return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
 }
 
+// ------------------------------------------------------------------ W4A16
+
+int a16_ksplit(int path, int64_t M, int64_t N, int64_t K) {
+  return path == W4A8_PATH_SKINNY ? skinny_a16_plan(M, N, K).ksplit : prefill_a16_ksplit(M, N, K);
+}
+
+size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
+  const int ks = a16_ksplit(path, M, N, K);
+  return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
+}
+
+int pick_a16_path(int64_t M, int64_t N, int64_t K) {
+  return M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL;
+}
+
+size_t a16_workspace_any(int64_t M, int64_t N, int64_t K) {
+  size_t need = a16_workspace_for(W4A8_PATH_PREFILL, M, N, K);
+  if (M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0) {
+    const size_t w = a16_workspace_for(W4A8_PATH_SKINNY, M, N, K);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
+int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
+            int64_t K, int32_t group, int32_t path, uint16_t* y, void* workspace,
+            size_t workspace_bytes, void* stream) {
+  int rc = check_weight_shape(N, K, group);
+  if (rc) return rc;
+  if (M <= 0 || M > ((int64_t)1 << 24))
+    return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (!x || !packed || !y) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(y))
+    return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+  const size_t need = (size_t)packed_bytes(N, K);
+  if (packed_bytes_ < need)
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
+  if (path == W4A8_PATH_AUTO) path = pick_a16_path(M, N, K);
+  if (path == W4A8_PATH_SKINNY && (M > 16 || skinny_a16_plan(M, N, K).ksplit == 0))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "no W4A16 M <= 16 plan for M=%lld K=%lld",
+                (long long)M, (long long)K);
+  if (path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
+    return fail(W4A8_ERR_INVALID_ARG, "W4A16 paths are SKINNY and PREFILL (got %d)", (int)path);
+  if (path == W4A8_PATH_PREFILL && (2 * M * K > kPrefillMaxBytes || N * K / 2 > kPrefillMaxBytes))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
+                "PREFILL path addresses activations and codes with 32-bit offsets");
+  const int ks = a16_ksplit(path, M, N, K);
+  const size_t ws_need = a16_workspace_for(path, M, N, K);
+  if (ws_need && (!workspace || workspace_bytes < ws_need))
+    return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                ws_need);
+  if (ws_need && !aligned16(workspace))
+    return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  const size_t ybytes = (size_t)M * (size_t)N * 2, xbytes = (size_t)M * (size_t)K * 2;
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, packed, need) ||
+      (ws_need && (overlaps(y, ybytes, workspace, ws_need) ||
+                   overlaps(workspace, ws_need, x, xbytes) ||
+                   overlaps(workspace, ws_need, packed, need))))
+    return fail(W4A8_ERR_INVALID_ARG, "output or workspace aliases another buffer");
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
+  GemmArgs a;
+  a.qa = nullptr;
+  a.sa = nullptr;
+  a.x = x;
+  a.x_dtype = W4A8_BF16;
+  a.w.codes = base;
+  a.w.zeros = base + zeros_offset(N, K);
+  a.w.scales = reinterpret_cast<const float*>(base + scales_offset(N, K));
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.partials = nullptr;
+  a.m_begin = a.m_end = 0;
+  a.workspace = static_cast<float*>(workspace);
+  a.sa_ws = nullptr;
+  a.ksplit = ks;
+  a.cb = a.ks = 0;
+  a.w8 = false;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e = path == W4A8_PATH_SKINNY ? launch_skinny_a16(a, st) : launch_prefill_a16(a, st);
+  if (e == hipSuccess && ks > 1) e = launch_splitk_reduce(a.workspace, ks, nullptr, M, N, y, st);
+  return device_status(e, "w4a16 launch");
+}
+
 // ------------------------------------------------------------------ W8A8
 
 // Exact int32 totals need |sum_k qa*qw| <= 127 * 127 * K < 2^31.
@@ -680,6 +766,32 @@ int w8a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (rc) return rc;
   return run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0,
                      0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
+}
+
+// ------------------------------------------------------------------ W4A16
+
+size_t w4a16_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (check_weight_shape(N, K, group) || M <= 0) return 0;
+  return a16_workspace_any(M, N, K);
+}
+
+int w4a16_select_path(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % kGroup || N % kBlockCols) return 0;
+  return pick_a16_path(M, N, K);
+}
+
+int w4a16_linear(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
+                 int64_t K, int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return run_a16(x, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO, y, workspace,
+                 workspace_bytes, stream);
+}
+
+int w4a16_linear_path(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t M,
+                      int64_t N, int64_t K, int32_t group, int32_t path, uint16_t* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return run_a16(x, packed, packed_bytes_, M, N, K, group, path, y, workspace, workspace_bytes,
+                 stream);
 }
 
 }  // extern "C"

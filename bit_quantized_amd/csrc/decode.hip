@@ -23,6 +23,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int6
                                            kBufferWord3);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Four codes q (one per byte, 0..15) minus a zero point z (0..15) as four
+// bfloat16, two per dword in byte order.  q + 16 - z lies in 1..31, so the
+// per-byte subtraction borrows nothing; each byte converts exactly to float
+// as an unsigned value and 16 is taken off exactly; small integers are exact
+// in bf16, so the float's high half is the bf16.
+__device__ __forceinline__ void codes_to_bf16x2(uint32_t nib4, uint32_t zz, int& lo, int& hi) {
+  const uint32_t u = (nib4 + 0x10101010u) - zz;
+  const float f0 = (float)(u & 0xFFu) - 16.0f, f1 = (float)((u >> 8) & 0xFFu) - 16.0f;
+  const float f2 = (float)((u >> 16) & 0xFFu) - 16.0f, f3 = (float)(u >> 24) - 16.0f;
+  lo = (int)__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = (int)__builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
 __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, float v) {
   if (a.ksplit == 1) {
     if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(a.sa[m] * v);
@@ -130,15 +146,26 @@ template <> struct XChunk<float> {  // two 16-byte loads
 // per unit in MFMA operand order, one float scale per channel).  The bytes
 // are the B operand as loaded, the products accumulate in int32 over all of
 // K (exact), and the two scales are applied once, to the total.
-template <bool DEBUG, int MP, int NPT, typename T, bool W8>
+//
+// A16: W4A16 instead (bf16 activations, no quantisation).  Each workgroup
+// copies its K slice of the M rows into LDS (row stride 2 * slice + 16
+// bytes) and the wavefronts run four v_mfma_f32_16x16x32_bf16 per unit: B is
+// q - z converted exactly to bf16, A the matching eight activations per lane
+// (the four steps take input channels 16j.., 16j+8.., 64+16j.., 64+16j+8..
+// of the group, the same slots in A and B), and the fp32 group sum is scaled
+// by s into the accumulator.
+constexpr int kA16Slack = 1536;  // LDS past the staged rows that padded quads may read
+
+template <bool DEBUG, int MP, int NPT, typename T, bool W8, bool A16 = false>
 __global__ void __launch_bounds__(kThreads)
 skinny_kernel(GemmArgs a) {
-  constexpr bool FUSED = NPT > 0;
+  constexpr bool STAGE = NPT > 0;            // activations staged in LDS
+  constexpr bool FUSED = STAGE && !A16;      // ... as int8 codes quantised here
   constexpr int kUnitBytes = W8 ? 2 * kBlockBytes : kBlockBytes;  // codes per unit
   constexpr int CW = W8 ? 2 : 1;                                  // code loads per unit
   using S = ActShape<MP>;
-  constexpr int kQuadLoads = FUSED ? 0 : S::kQuadLoads;
-  constexpr int kSlotLoads = FUSED ? 0 : S::kSlotLoads;
+  constexpr int kQuadLoads = STAGE ? 0 : S::kQuadLoads;
+  constexpr int kSlotLoads = STAGE ? 0 : S::kSlotLoads;
   constexpr int QL = kQuadLoads > 0 ? kQuadLoads : 1;
   constexpr int SL = kSlotLoads > 0 ? kSlotLoads : 1;
   __shared__ float red[kWaves][4][64];
@@ -152,19 +179,24 @@ skinny_kernel(GemmArgs a) {
   const int64_t G = a.K / kGroup;
   const int rstride = (int)a.K + 16;  // fused: LDS row stride of the codes
 
-  // fused: this thread's row and chunks of eight, loaded before anything else
-  constexpr int XL = FUSED ? XChunk<T>::kLoads : 1;
-  constexpr int NX = FUSED ? NPT : 1;
+  // A16: groups [g_first, g_last) of K are this workgroup's slice
+  const int g_first = (int)blockIdx.y * kWaves * a.gq + min((int)blockIdx.y * kWaves, a.gr);
+  const int g_last = ((int)blockIdx.y + 1) * kWaves * a.gq + min(((int)blockIdx.y + 1) * kWaves, a.gr);
+  const int rs16 = 2 * kGroup * (g_last - g_first) + 16;  // A16: LDS row stride in bytes
+
+  // staged: this thread's row and chunks of eight, loaded before anything else
+  constexpr int XL = STAGE ? XChunk<T>::kLoads : 1;
+  constexpr int NX = STAGE ? NPT : 1;
   constexpr int kRowThreads = kThreads / MP;
   const int xrow = threadIdx.x / kRowThreads, xt = threadIdx.x % kRowThreads;
-  const int cpr = (int)(a.K / 8);  // chunks per row
+  const int cpr = A16 ? kGroup / 8 * (g_last - g_first) : (int)(a.K / 8);  // chunks per row
   // chunks xt, xt + 1024/MP, ... of row xrow: the first nx of them exist
   const int nx = xrow < a.M && xt < cpr ? (cpr - xt + kRowThreads - 1) / kRowThreads : 0;
   v4u xr[NX][XL];
-  if constexpr (FUSED) {
+  if constexpr (STAGE) {
     const __amdgpu_buffer_rsrc_t rx = rsrc_of(a.x, a.M * a.K * (int64_t)sizeof(T));
     const int oob = 0x7FFFFFF0;
-    const int off0 = (xrow * (int)a.K + 8 * xt) * (int)sizeof(T);
+    const int off0 = (xrow * (int)a.K + (A16 ? kGroup * g_first : 0) + 8 * xt) * (int)sizeof(T);
 #pragma unroll
     for (int c = 0; c < NPT; ++c) {
       const int off = c < nx ? off0 + c * 8 * kRowThreads * (int)sizeof(T) : oob;
@@ -199,7 +231,8 @@ skinny_kernel(GemmArgs a) {
   const int z_base = lane < 8 ? 4 * lane : oob;
   // fused: LDS byte offset of this lane's A operand for unit 0 of the run
   // (rows >= M read row M-1; their products are never stored)
-  const int lds_a = min(r16, (int)a.M - 1) * rstride + gb * kGroup + 16 * j;
+  const int lds_a = A16 ? min(r16, (int)a.M - 1) * rs16 + (gb - g_first) * 2 * kGroup + 32 * j
+                        : min(r16, (int)a.M - 1) * rstride + gb * kGroup + 16 * j;
 
   auto act_off = [&](int u) __attribute__((always_inline)) {  // unit u of the run, first byte
     return act_base == oob ? oob : act_base + u * kGroup;
@@ -250,6 +283,27 @@ skinny_kernel(GemmArgs a) {
 
   auto compute = [&](int q, int i, const v4u* w, const v4i* au, const v4i* aqc, uint32_t sc,
                      uint32_t zc) __attribute__((always_inline)) {
+    if constexpr (A16) {
+      const float s = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_s + 64 * i, (int)sc));
+      const uint32_t zw = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_z + 8 * i, (int)zc);
+      const uint32_t zz = ((zw >> zshift) & 0xFu) * 0x01010101u;
+      const int off = lds_a + (4 * q + i) * 2 * kGroup;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // step t: nibble half t / 2, code bytes 8 (t % 2) ..
+        const v4i av = *reinterpret_cast<const v4i*>(qs + off + (t >> 1) * kGroup + (t & 1) * 16);
+        const int sh = (t >> 1) * 4;
+        int b0, b1, b2, b3;
+        codes_to_bf16x2((w[0][2 * (t & 1)] >> sh) & 0x0F0F0F0Fu, zz, b0, b1);
+        codes_to_bf16x2((w[0][2 * (t & 1) + 1] >> sh) & 0x0F0F0F0Fu, zz, b2, b3);
+        const v4i bv = {b0, b1, b2, b3};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                      __builtin_bit_cast(v8bf, bv), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) accf[t] += s * acc[t];
+      return;
+    }
     v4i a0, a1;
     if constexpr (FUSED) {
       const int off = lds_a + (4 * q + i) * kGroup;
@@ -317,7 +371,23 @@ skinny_kernel(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);  // slot order = issue order, so waits stay exact
     }
   };
-  if constexpr (!FUSED) load_first();
+  if constexpr (A16) {
+    // copy the slice's rows to LDS as they are, then the first weight loads.
+    // The units that pad a run's last quad multiply zero weights by whatever
+    // lies past the run (row pads, the slack after the rows): zeroed here,
+    // since 0 times a bf16 NaN pattern would not be 0.
+    int8_t* qrow = qs + xrow * rs16 + 16 * xt;
+#pragma unroll
+    for (int c = 0; c < NPT; ++c)
+      if (c < nx) *reinterpret_cast<v4u*>(qrow + c * 16 * kRowThreads) = xr[c][0];
+    if (threadIdx.x < (unsigned)a.M)
+      *reinterpret_cast<v4u*>(qs + threadIdx.x * rs16 + rs16 - 16) = v4u{0u, 0u, 0u, 0u};
+    if (threadIdx.x < kA16Slack / 16)
+      *reinterpret_cast<v4u*>(qs + a.M * rs16 + 16 * threadIdx.x) = v4u{0u, 0u, 0u, 0u};
+    __syncthreads();
+    load_first();
+  }
+  if constexpr (!STAGE) load_first();
   if constexpr (FUSED) {
     // row maximum: this thread's chunks, its wavefront (one row per
     // wavefront, as a row spans 1024 / MP >= 64 threads), then the row's
@@ -409,10 +479,16 @@ skinny_kernel(GemmArgs a) {
       for (int w = 1; w < kWaves; ++w) v += red[w][t][lane];
       const int64_t m = 4 * j + t;
       if (m < a.M) {
-        if constexpr (FUSED)
+        if constexpr (FUSED) {
           a.y[m * a.N + 16 * nb + r16] = f32_to_bf16_rne(s_sa[m] * v);
-        else
+        } else if constexpr (A16) {
+          if (a.ksplit == 1)
+            a.y[m * a.N + 16 * nb + r16] = f32_to_bf16_rne(v);
+          else
+            a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + 16 * nb + r16] = v;
+        } else {
           store_out(a, m, 16 * nb + r16, v);
+        }
       }
     }
   }
@@ -429,7 +505,7 @@ splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __re
   const int64_t m = t / N;
   float v = ws[t];
   for (int k = 1; k < ksplit; ++k) v += ws[k * M * N + t];
-  y[t] = f32_to_bf16_rne(sa[m] * v);
+  y[t] = f32_to_bf16_rne(sa ? sa[m] * v : v);
 }
 
 // W8A8 split-K: the exact int32 totals summed over the slices (order-free),
@@ -534,6 +610,47 @@ bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype) {
 }
 
 int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
+
+// W4A16 on the M <= 16 kernel: K is split at least as much as filling the
+// machine asks, and further until one workgroup's slice of the rows fits the
+// LDS budget and takes at most 8 chunks of eight per thread.
+A16Plan skinny_a16_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t G = K / kGroup;
+  const int64_t mp = pow2_rows(M);
+  for (int ks = pick_ksplit(N, K); ks <= G && ks <= 64; ks *= 2) {
+    // the first workgroup's slice is the longest: 16 runs of gq groups, plus
+    // one more group for each of the first gr runs
+    const int64_t parts = (int64_t)ks * kWaves, gq = G / parts, gr = G % parts;
+    const int64_t slice = kWaves * gq + (gr < kWaves ? gr : kWaves);
+    // (slack: a wavefront's padded last quad reads up to three units, 3 x 256
+    // bytes, plus one operand span past its run)
+    const int64_t lds = M * (2 * kGroup * slice + 16) + kA16Slack;
+    const int64_t npt = (kGroup / 8 * slice + kThreads / mp - 1) / (kThreads / mp);
+    if (lds <= kFusedLdsBytes && npt <= 8) return A16Plan{ks, npt <= 4 ? 4 : 8, (size_t)lds};
+  }
+  return A16Plan{0, 0, 0};
+}
+
+hipError_t launch_skinny_a16(GemmArgs a, hipStream_t st) {
+  const A16Plan p = skinny_a16_plan(a.M, a.N, a.K);
+  if (p.ksplit == 0 || p.ksplit != a.ksplit || a.x_dtype != 0) return hipErrorInvalidValue;
+  const int64_t G = a.K / kGroup, parts = (int64_t)a.ksplit * kWaves;
+  a.gq = (int)(G / parts);
+  a.gr = (int)(G % parts);
+  const dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit), block(kThreads);
+  const int mp = pow2_rows(a.M);
+#define W4A16_LAUNCH(MPV, NPTV) \
+  hipLaunchKernelGGL((skinny_kernel<false, MPV, NPTV, uint16_t, false, true>), grid, block, p.lds, st, a)
+  if (p.npt == 4) {
+    if (mp == 2) W4A16_LAUNCH(2, 4); else if (mp == 4) W4A16_LAUNCH(4, 4);
+    else if (mp == 8) W4A16_LAUNCH(8, 4); else W4A16_LAUNCH(16, 4);
+  } else {
+    if (mp == 2) W4A16_LAUNCH(2, 8); else if (mp == 4) W4A16_LAUNCH(4, 8);
+    else if (mp == 8) W4A16_LAUNCH(8, 8); else W4A16_LAUNCH(16, 8);
+  }
+#undef W4A16_LAUNCH
+  return hipGetLastError();
+}
 
 hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
   const int64_t G = a.K / kGroup, parts = (int64_t)a.ksplit * kWaves;

@@ -358,6 +358,202 @@ prefill_kernel(GemmArgs a) {
   }
 }
 
+// --------------------------------------------------------------- W4A16
+//
+// "The 4-bit CPU path", section "W4A16": large batches of bf16 activations
+// take their own GEMM path, the int4 weights expanded once per batch rather
+// than per activation row.  Here they are expanded once per workgroup and
+// group, in LDS, to exact bf16 q - z, and multiplied on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, float32 sums); each group's float sum is
+// scaled by s[n][g] into the accumulators, as the W4A8 path does with its
+// integer sums.
+//
+// Tile: 128 tokens x 128 channels per 512-thread workgroup, eight wavefronts
+// of 32 x 64 (the bf16 activation tile is twice the int8 one, so the token
+// side is halved to keep two stages in LDS).  Per group the wavefront runs
+// its 8 tiles x 4 steps; step t takes input channels 16j + 8t'.. of half
+// t / 2 (t' = t % 2) in both operands.
+namespace a16 {
+
+constexpr int BM = 128;
+constexpr int kAStride = 2 * kGroup + 16;             // bf16 row of one group, bank-spread
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + BM * kAStride;          // bf16 q - z, [NCB][4 steps][64 lanes][16 B]
+constexpr int kSOff = kBOff + NCB * 4 * kBlockBytes;  // scales [NCB][16]
+constexpr int kBufBytes = kSOff + NCB * 16 * 4;
+constexpr int kAChunks = BM * 2 * kGroup / 16 / kThreads;  // 16-B activation chunks per thread (4)
+
+struct Stage {
+  v4i a[kAChunks];
+  v4i b;          // 16 packed code bytes: block t/64, lane t%64
+  uint32_t zb;    // the byte holding that lane's zero point
+  float s;        // scale of channel t%16 of block (t/16)%8
+};
+
+struct Offsets {
+  uint32_t a[kAChunks];
+  uint32_t b, z, s;
+  int zshift;
+};
+
+__device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
+                                                int64_t NB, int64_t G) {
+  const int tid = threadIdx.x;
+  Offsets o;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    const int ch = tid + kThreads * i;  // 16 chunks of 16 B per row and group
+    o.a[i] = (uint32_t)((min(m0 + (ch >> 4), a.M - 1) * a.K + (ch & 15) * 8) * 2);
+  }
+  const int64_t nb = min(cb0 + (tid >> 6), NB - 1);
+  o.b = (uint32_t)(nb * G * kBlockBytes + (tid & 63) * 16);
+  o.z = (uint32_t)(nb * G * kZeroBlockBytes + ((tid & 15) >> 1));
+  o.zshift = (tid & 1) * 4;
+  const int64_t nbs = min(cb0 + ((tid >> 4) & (NCB - 1)), NB - 1);
+  o.s = (uint32_t)(nbs * G * 16 + (tid & 15));
+  return o;
+}
+
+__device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
+                                           Stage& st) {
+  const uint8_t* x = static_cast<const uint8_t*>(a.x) + g * kGroup * 2;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) st.a[i] = *reinterpret_cast<const v4i*>(x + o.a[i]);
+  st.b = *reinterpret_cast<const v4i*>(a.w.codes + g * kBlockBytes + o.b);
+  st.zb = (a.w.zeros + g * kZeroBlockBytes)[o.z];
+  st.s = (a.w.scales + g * 16)[o.s];
+}
+
+// Four codes (0..15, one per byte) minus a zero point as four bf16, two per
+// dword in byte order: q + 16 - z (1..31, no borrow across bytes) converts
+// exactly from each unsigned byte, 16 comes off exactly, and small integers
+// are exact in bf16 (the float's high half).
+__device__ __forceinline__ void codes_to_bf16x2(uint32_t nib4, uint32_t zz, int& lo, int& hi) {
+  const uint32_t u = (nib4 + 0x10101010u) - zz;
+  const float f0 = (float)(u & 0xFFu) - 16.0f, f1 = (float)((u >> 8) & 0xFFu) - 16.0f;
+  const float f2 = (float)((u >> 16) & 0xFFu) - 16.0f, f3 = (float)(u >> 24) - 16.0f;
+  lo = (int)__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = (int)__builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+}
+
+// Stage -> LDS: the activation rows as they are, the codes expanded once to
+// bf16 q - z in MFMA operand order (block u, step t, lane L), the scales.
+__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kAChunks; ++i) {
+    const int ch = tid + kThreads * i;
+    *reinterpret_cast<v4i*>(buf + kAOff + (ch >> 4) * kAStride + (ch & 15) * 16) = st.a[i];
+  }
+  const uint32_t zz = ((st.zb >> zshift) & 0xFu) * 0x01010101u;
+  const int u = tid >> 6, L = tid & 63;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {  // step t: nibble half t / 2, code bytes 8 (t % 2) .. + 7
+    const int sh = (t >> 1) * 4;
+    int b0, b1, b2, b3;
+    codes_to_bf16x2(((uint32_t)st.b[2 * (t & 1)] >> sh) & 0x0F0F0F0Fu, zz, b0, b1);
+    codes_to_bf16x2(((uint32_t)st.b[2 * (t & 1) + 1] >> sh) & 0x0F0F0F0Fu, zz, b2, b3);
+    *reinterpret_cast<v4i*>(buf + kBOff + (u * 4 + t) * kBlockBytes + L * 16) = v4i{b0, b1, b2, b3};
+  }
+  reinterpret_cast<float*>(buf + kSOff)[tid & (NCB * 16 - 1)] = st.s;
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// One group: fragments from LDS, 8 tiles x 4 bf16 MFMA steps, and the
+// group's float sums scaled into the accumulators.
+__device__ __forceinline__ void compute_group(const uint8_t* buf, float (&accf)[2][4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  float sv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sv[u] = reinterpret_cast<const float*>(buf + kSOff)[(wn * 4 + u) * 16 + r16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint8_t* arow = buf + kAOff + (wm * 32 + i * 16 + r16) * kAStride + 32 * j;
+    v4i av[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const v4i*>(arow + (t >> 1) * kGroup + (t & 1) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4i bv = *reinterpret_cast<const v4i*>(buf + kBOff + ((wn * 4 + u) * 4 + t) * kBlockBytes + lane * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[t]),
+                                                      __builtin_bit_cast(v8bf, bv), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * acc[r];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads)
+prefill_a16_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  const int64_t G = a.K / kGroup;
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (NB + NCB - 1) / NCB;
+  const int64_t t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  const int64_t tm = t % tiles_m, tn = t / tiles_m;
+  const int64_t m0 = tm * BM, cb0 = tn * NCB;
+  const int64_t gb = G * blockIdx.y / gridDim.y, ge = G * (blockIdx.y + 1) / gridDim.y;
+
+  float accf[2][4][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
+
+  const Offsets off = make_offsets(a, m0, cb0, NB, G);
+  Stage s0, s1;
+  load_stage(a, off, gb, s0);
+  load_stage(a, off, min(gb + 1, ge - 1), s1);
+  store_stage(smem[0], s0, off.zshift);
+  __syncthreads();
+  for (int64_t g = gb; g < ge; g += 2) {
+    load_stage(a, off, min(g + 2, ge - 1), s0);
+    compute_group(smem[0], accf);
+    store_stage(smem[1], s1, off.zshift);
+    __syncthreads();
+    if (g + 1 >= ge) break;
+    load_stage(a, off, min(g + 3, ge - 1), s1);
+    compute_group(smem[1], accf);
+    store_stage(smem[0], s0, off.zshift);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm * 32 + i * 16 + 4 * j + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t nb = cb0 + wn * 4 + u;
+        if (nb >= NB) continue;
+        const int64_t n = nb * 16 + r16;
+        if (gridDim.y > 1)
+          a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + n] = accf[i][u][r];
+        else
+          a.y[m * a.N + n] = f32_to_bf16_rne(accf[i][u][r]);
+      }
+    }
+}
+
+}  // namespace a16
+
 }  // namespace
 
 // Split K only while the output tiles leave compute units idle, keeping at
@@ -384,6 +580,24 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
   }
+  return hipGetLastError();
+}
+
+// W4A16 prefill: K is split (float partials, deterministic reduce) only while
+// the output tiles leave compute units idle.
+int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + a16::BM - 1) / a16::BM) * ((N / kBlockCols + NCB - 1) / NCB);
+  const int64_t G = K / kGroup, cus = device_cus();
+  int ks = 1;
+  while (tiles * ks * 2 <= cus && G >= (int64_t)ks * 2 * 2) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st) {
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles = ((a.M + a16::BM - 1) / a16::BM) * ((NB + NCB - 1) / NCB);
+  hipLaunchKernelGGL(a16::prefill_a16_kernel, dim3((unsigned)tiles, (unsigned)a.ksplit),
+                     dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -156,7 +156,19 @@ bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype);
 int prefill_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 hipError_t launch_skinny(GemmArgs a, hipStream_t st);
+// W4A16 (bf16 activations in GemmArgs::x, x_dtype 0) on the M <= 16 kernel:
+// its K split, chunks per thread and dynamic LDS; ksplit 0 when no split fits.
+struct A16Plan {
+  int ksplit;
+  int npt;
+  size_t lds;
+};
+A16Plan skinny_a16_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_skinny_a16(GemmArgs a, hipStream_t st);
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
+// W4A16 prefill (bf16 activations in GemmArgs::x): K split and launch.
+int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K);
+hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st);
 hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,

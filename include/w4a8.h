@@ -242,6 +242,32 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed, siz
                          int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ----------------------------------------------------------------- W4A16
+ *
+ * W4A16 ("The 4-bit CPU path", section "W4A16": the same int4 weights with
+ * the activations kept in bf16; small batches expand the weights per row,
+ * large ones once per batch).  Weights are the W4A8 packed buffer
+ * (w4a8_pack_weights).  No activation quantisation:
+ *   y[m][n] = bf16_rne( sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]) )
+ * with q - z expanded exactly to bf16 and each group's products summed in
+ * float32 on the bf16 matrix cores, then scaled by s in float32.
+ *   x   device bfloat16 bits [M][K]
+ *   y   device bfloat16 bits [M][N]
+ *   workspace  device scratch of w4a16_linear_workspace_bytes(M, N, K, group)
+ *     bytes (float split-K partials; may be NULL when that is 0)
+ * Paths: SKINNY (M <= 16; each workgroup stages its K slice of the rows in
+ * LDS, K split until it fits) and PREFILL (128-token tiles).
+ * w4a16_linear_path forces one of the two (AUTO allowed), for tests.
+ */
+size_t w4a16_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
+int w4a16_select_path(int64_t M, int64_t N, int64_t K);
+int w4a16_linear(const uint16_t* x, const void* packed, size_t packed_bytes, int64_t M, int64_t N,
+                 int64_t K, int32_t group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                 void* stream);
+int w4a16_linear_path(const uint16_t* x, const void* packed, size_t packed_bytes, int64_t M,
+                      int64_t N, int64_t K, int32_t group, int32_t path, uint16_t* y,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ W8A8
  *
  * The W8A8 int8-dynamic linear ("Serve a pre-quantized int8 weight-only DiT

@@ -244,3 +244,23 @@ def test_hadamard_rejections(lib):
     assert g(FAKE, 0, FAKE2, pb - 16, 1, 256, 256, 128, y, ctypes.c_void_p(1 << 32), need,
              None) == -4
     assert g(FAKE, 0, FAKE2, pb, 1, 256, 256, 64, y, ctypes.c_void_p(1 << 32), need, None) == -2
+
+
+def test_w4a16_rejections(lib):
+    f = lib.w4a16_linear
+    pb = lib.w4a8_packed_weight_bytes(256, 256, 128)
+    y = ctypes.c_void_p(1 << 28)
+    assert f(None, FAKE2, pb, 4, 256, 256, 128, y, None, 0, None) == -1
+    assert f(FAKE, FAKE2, pb, 4, 250, 256, 128, y, None, 0, None) == -2
+    assert f(MIS, FAKE2, pb, 4, 256, 256, 128, y, None, 0, None) == -3
+    assert f(FAKE, FAKE2, pb - 16, 4, 256, 256, 128, y, None, 0, None) == -4
+    assert f(FAKE, FAKE2, pb, 4, 256, 256, 128, FAKE2, None, 0, None) == -1   # y aliases packed
+    g = lib.w4a16_linear_path
+    assert g(FAKE, FAKE2, pb, 4, 256, 256, 128, 1, y, None, 0, None) == -1    # no GEMV path
+    assert g(FAKE, FAKE2, pb, 17, 256, 256, 128, 2, y, None, 0, None) == -2   # SKINNY needs M <= 16
+    pb2 = lib.w4a8_packed_weight_bytes(512, 18944, 128)
+    need = lib.w4a16_linear_workspace_bytes(1, 512, 18944, 128)
+    assert need > 0
+    assert f(FAKE, FAKE2, pb2, 1, 512, 18944, 128, y, None, 0, None) == -4    # split K: workspace
+    assert lib.w4a16_select_path(4, 3584, 18944) == 2
+    assert lib.w4a16_select_path(17, 3584, 18944) == 3
