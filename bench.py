@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "W4A8 linear: decode GB/s (% HBM peak) at M=1; prefill int8 TOPS (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 
 
 def parse():
@@ -52,7 +53,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the skinny and layer legs")
     p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "w8a8", "hadamard",
-                                      "copy"],
+                                      "w4a16", "copy"],
                    default="all", help="run one part only (for hardware-counter passes)")
     return p.parse_args()
 
@@ -363,6 +364,43 @@ def bench_hadamard(torch, w4, args):
     return res
 
 
+def bench_w4a16(torch, w4, args):
+    """W4A16 (bf16 activations x the packed int4 weights): decode and skinny
+    against the HBM roofline, prefill against bf16 MFMA peak; each checked
+    against the oracle before timing."""
+    import oracle
+    from bit_quantized_amd import synth
+    out = []
+    for spec, copies in ((synth.DECODE_UP, 16), (synth.SKINNY_DOWN_4, 16), (synth.SKINNY_DOWN_16, 16),
+                         (synth.PREFILL_UP, 4)):
+        lin, x, Ws = setup_linear(torch, w4, spec, copies)
+        M, K, N = spec.M, spec.K, spec.N
+        rows = (0, min(M, 16))
+        y = w4.w4a16_linear(x, Ws[0])
+        ref = oracle.w4a16_linear(lin["x"], lin["q"], lin["z"], lin["s"], rows=rows)
+        ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy()[rows[0]:rows[1]], ref)
+        if not ok:
+            raise SystemExit(f"parity check failed ({spec.name}): {err:.3e} > {bound:.3e}")
+        R = len(Ws)
+        ws = torch.empty(max(w4.w4a16_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+        n = 64 if M <= 16 else args.prefill_steps
+        ms = graph_launches_ms(torch, lambda i: w4.w4a16_linear(x, Ws[i % R], out=y, workspace=ws), n)
+        r = {"workload": f"{spec.name} M={M} K={K} N={N} (W4A16: bf16 activations)",
+             "path": {2: "skinny", 3: "prefill"}[w4.w4a16_select_path(M, N, K)],
+             "us": round(ms * 1e3, 3), "parity": {"rows": list(rows), "max_err": err, "bound": bound}}
+        if M <= 16:
+            b = algorithmic_bytes(M, N, K)
+            r.update({"bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        else:
+            flops = 2.0 * M * N * K
+            tf = flops / (ms * 1e-3) / 1e12
+            r.update({"TFLOPS": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        out.append(r)
+        del Ws
+    return out
+
+
 def bench_skinny(torch, w4, args):
     """Skinny decode (2 <= M <= 16): K=18944 -> N=3584, as quant + GEMM
     through w4a8_linear, against the HBM roofline."""
@@ -589,7 +627,7 @@ def main():
         copy_calibration(torch)
         return
 
-    dec = pre = skinny = layer = w8 = had = None
+    dec = pre = skinny = layer = w8 = had = a16 = None
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
@@ -602,6 +640,8 @@ def main():
         w8 = bench_w8a8(torch, w4, args)
     if args.only == "hadamard" or (args.only == "all" and not args.no_extra):
         had = bench_hadamard(torch, w4, args)
+    if args.only == "w4a16" or (args.only == "all" and not args.no_extra):
+        a16 = bench_w4a16(torch, w4, args)
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline and args.only == "all":
         if dec:
@@ -622,6 +662,8 @@ def main():
             out["w8a8"] = w8
         if had:
             out["hadamard"] = had
+        if a16:
+            out["w4a16"] = a16
         print(json.dumps(out))
         return
     spec = dec["spec"]
@@ -662,6 +704,8 @@ def main():
         line["w8a8"] = w8
     if had:
         line["hadamard"] = had
+    if a16:
+        line["w4a16"] = a16
     line["system"] = gpu_info(torch)
     print(json.dumps(line))
 
