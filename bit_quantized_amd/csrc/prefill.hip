@@ -10,8 +10,11 @@
 // wavefronts of 64 x 64.  Per group of 128 input channels the workgroup
 // stages the activation tile (256 x 128 int8), the eight code blocks of the
 // tile unpacked once to q - z bytes, and their scales in LDS, double-buffered,
-// with the next group's global loads in flight while the current group
-// computes.
+// with the next group's loads in flight while the current group computes.
+// The activation tile goes from memory straight into LDS (buffer loads with
+// the LDS bit: no registers, no LDS store instructions); its 16-byte chunks
+// are swizzled by row so that both the 1 KiB load chunks and the MFMA
+// fragment reads are free of bank conflicts.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -21,17 +24,21 @@ constexpr int kThreads = 512;           // 8 wavefronts, 2 per SIMD
 constexpr int BM = 256;                 // tokens per tile
 constexpr int BN = 128;                 // output channels per tile
 constexpr int NCB = BN / kBlockCols;    // packed blocks per tile (8)
-constexpr int kAStride = kGroup + 16;   // LDS row pitch of the activation tile (bank spread)
-constexpr int kAOff = 0;
-constexpr int kBOff = kAOff + BM * kAStride;          // unpacked q - z, [NCB][2][64 lanes][16 B]
+constexpr int kAOff = 0;                              // activation tile [BM][128], chunks swizzled
+constexpr int kBOff = kAOff + BM * kGroup;            // unpacked q - z, [NCB][2][64 lanes][16 B]
 constexpr int kSOff = kBOff + NCB * 2 * kBlockBytes;  // scales [NCB][16]
 constexpr int kBufBytes = kSOff + NCB * 16 * 4;
-constexpr int kAChunks = BM * kGroup / 16 / kThreads;  // 16-B activation chunks per thread (4)
+constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 descriptor format
+constexpr int kADmaRows = 1024 / kGroup;                      // tile rows per 1 KiB load (8)
+constexpr int kADma = BM / kADmaRows / (kThreads / 64);       // such loads per wavefront (4)
 
-// One group's operands as they come from HBM, held in registers while
-// earlier groups compute.
+// 16-byte chunk c (input channels 16c..16c+15 of the group) of tile row r
+// sits at chunk c ^ (r % 8) of the row's 128 bytes.
+__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ (r & 7); }
+
+// One group's weight operands as they come from HBM, held in registers
+// while the previous group computes.
 struct Stage {
-  v4i a[kAChunks];
   v4i b;          // W4: this thread's 16 packed bytes: block t/64, lane t%64
                   // W8: half 0 of block t/64, lane t%64 (16 int8 weights)
   v4i b8;         // W8: half 1 of the same block and lane
@@ -45,7 +52,7 @@ struct Stage {
 // stored, so nothing needs masking and every thread issues the same loads.
 // (The host keeps M*K and N*K/2 below 2^31 on this path.)
 struct Offsets {
-  uint32_t a[kAChunks];
+  uint32_t a[kADma];  // activation bytes this lane brings into LDS chunk kADma * wave + i
   uint32_t b, z, s;
   int zshift;
 };
@@ -53,12 +60,14 @@ struct Offsets {
 template <bool W8>
 __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
                                                 int64_t NB, int64_t G) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Offsets o;
+  // 1 KiB load chunk i of the wavefront holds tile rows kADmaRows (kADma wave
+  // + i) + lane / 8; lane writes physical chunk lane % 8 of its row
 #pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int ch = tid + kThreads * i;
-    o.a[i] = (uint32_t)(min(m0 + (ch >> 3), a.M - 1) * a.K + (ch & 7) * 16);
+  for (int i = 0; i < kADma; ++i) {
+    const int r = kADmaRows * (kADma * wave + i) + (lane >> 3);
+    o.a[i] = (uint32_t)(min(m0 + r, a.M - 1) * a.K + 16 * a_chunk(r, lane & 7));
   }
   const int64_t nb = min(cb0 + (tid >> 6), NB - 1);
   o.b = (uint32_t)(nb * G * (W8 ? 2 : 1) * kBlockBytes + (tid & 63) * 16);
@@ -72,9 +81,6 @@ __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, i
 template <bool W8>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
                                            Stage& st) {
-  const int8_t* qa = a.qa + g * kGroup;
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) st.a[i] = *reinterpret_cast<const v4i*>(qa + o.a[i]);
   if constexpr (W8) {
     const uint8_t* codes = a.w.codes + g * 2 * kBlockBytes;
     st.b = *reinterpret_cast<const v4i*>(codes + o.b);
@@ -96,11 +102,6 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, 
 template <bool W8>
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int ch = tid + kThreads * i;
-    *reinterpret_cast<v4i*>(buf + kAOff + (ch >> 3) * kAStride + (ch & 7) * 16) = st.a[i];
-  }
   if constexpr (W8) {
     // the packed halves are already the MFMA B operand: copied as they are
     const int u = tid >> 6, L = tid & 63;
@@ -154,10 +155,10 @@ __device__ __forceinline__ void compute_group_w8(const uint8_t* buf, v4i (&acci)
     b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
-    a0[i] = *reinterpret_cast<const v4i*>(arow);
-    a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
+  for (int i = 0; i < 4; ++i) {  // rows wm*64 + 16i + r16: the swizzle is r16 % 8
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kGroup;
+    a0[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, j));
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, 4 + j));
   }
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
@@ -190,10 +191,10 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
   }
   v4i a0[4], a1[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kAStride + 16 * j;
-    a0[i] = *reinterpret_cast<const v4i*>(arow);
-    a1[i] = *reinterpret_cast<const v4i*>(arow + 64);
+  for (int i = 0; i < 4; ++i) {  // rows wm*64 + 16i + r16: the swizzle is r16 % 8
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kGroup;
+    a0[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, j));
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, 4 + j));
   }
   // MFMA pair of tile t, then the rescale of tile t - 2 (whose result is
   // ready by then): the vector ALU and the matrix cores work side by side.
@@ -233,7 +234,8 @@ __global__ void __launch_bounds__(kThreads)
 prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 wavefronts of 64 x 64
   const int r16 = lane & 15, j = lane >> 4;
   const int64_t G = a.K / kGroup;
@@ -263,30 +265,43 @@ prefill_kernel(GemmArgs a) {
       compute_group<DEBUG>(a, buf, g, m0, cb0, NB, G, accf);
   };
 
-  // One group of 128 input channels per step: the operands of group g + 2
-  // are loaded while group g computes and group g + 1 (loaded one step
-  // earlier) is unpacked into the idle LDS buffer.  The two register stages
-  // alternate, so the loop is unrolled by two.
-
+  // One group of 128 input channels per step: while group g computes from
+  // one LDS buffer, group g + 1's activation tile streams into the other and
+  // its weight operands into registers, unpacked there after the compute.
+  // The buffers alternate, so the loop is unrolled by two.  (The barrier
+  // waits for this wavefront's loads, the LDS ones included.)
   const Offsets off = make_offsets<W8>(a, m0, cb0, NB, G);
-  Stage s0, s1;
-  load_stage<W8>(a, off, gb, s0);
-  load_stage<W8>(a, off, min(gb + 1, ge - 1), s1);
-  store_stage<W8>(smem[0], s0, off.zshift);
+  const __amdgpu_buffer_rsrc_t rqa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.qa), (short)0, (int)(a.M * a.K),
+                                        kBufferWord3);
+  // activation tile of group g into buffer B (wave-uniform LDS address)
+#define PREFILL_DMA_A(B, g)                                                                 \
+  _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_)                                     \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rqa, &smem[B][kAOff + (kADma * wave + i_) * 1024], 16, \
+                                             off.a[i_], (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * kGroup)), 0, 0)
+  Stage sb;
+  PREFILL_DMA_A(0, gb);
+  load_stage<W8>(a, off, gb, sb);
+  store_stage<W8>(smem[0], sb, off.zshift);
   __syncthreads();
   for (int64_t g = gb; g < ge; g += 2) {
-    // (the last steps re-read group ge - 1 into stages nobody consumes, which
-    // keeps each half free of branches)
-    load_stage<W8>(a, off, min(g + 2, ge - 1), s0);
+    if (g + 1 < ge) {  // buffer 1 was last read before the previous barrier
+      PREFILL_DMA_A(1, g + 1);
+      load_stage<W8>(a, off, g + 1, sb);
+    }
     compute(smem[0], g);
-    store_stage<W8>(smem[1], s1, off.zshift);  // buffer 1 was last read before the previous barrier
+    if (g + 1 < ge) store_stage<W8>(smem[1], sb, off.zshift);
     __syncthreads();
     if (g + 1 >= ge) break;
-    load_stage<W8>(a, off, min(g + 3, ge - 1), s1);
+    if (g + 2 < ge) {
+      PREFILL_DMA_A(0, g + 2);
+      load_stage<W8>(a, off, g + 2, sb);
+    }
     compute(smem[1], g + 1);
-    store_stage<W8>(smem[0], s0, off.zshift);
+    if (g + 2 < ge) store_stage<W8>(smem[0], sb, off.zshift);
     __syncthreads();
   }
+#undef PREFILL_DMA_A
 
   if constexpr (W8) {
     // int32 totals: to the workspace when K is split, else scaled to y (and
