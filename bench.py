@@ -386,7 +386,7 @@ def bench_w4a16(torch, w4, args):
         n = 64 if M <= 16 else args.prefill_steps
         ms = graph_launches_ms(torch, lambda i: w4.w4a16_linear(x, Ws[i % R], out=y, workspace=ws), n)
         r = {"workload": f"{spec.name} M={M} K={K} N={N} (W4A16: bf16 activations)",
-             "path": {2: "skinny", 3: "prefill"}[w4.w4a16_select_path(M, N, K)],
+             "path": {1: "gemv", 2: "skinny", 3: "prefill"}[w4.w4a16_select_path(M, N, K)],
              "us": round(ms * 1e3, 3), "parity": {"rows": list(rows), "max_err": err, "bound": bound}}
         if M <= 16:
             b = algorithmic_bytes(M, N, K)

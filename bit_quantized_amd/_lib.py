@@ -486,7 +486,7 @@ def w4a16_select_path(M: int, N: int, K: int) -> int:
 def w4a16_linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None,
                  path: int = PATH_AUTO) -> torch.Tensor:
     """W4A16: bf16 activations times the packed int4 weights (no activation
-    quantisation), bf16 out; `path` forces SKINNY or PREFILL."""
+    quantisation), bf16 out; `path` forces GEMV (M == 1), SKINNY or PREFILL."""
     lib = load()
     w.check()
     _need_cuda(x, out)

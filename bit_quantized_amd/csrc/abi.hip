@@ -224,7 +224,14 @@ size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
 
 // ------------------------------------------------------------------ W4A16
 
+// The GEMV serves W4A16 at M == 1 when the token and its quarter sums fit LDS
+// and the grid fits the kernel's tables.
+bool a16_gemv_ok(int64_t M, int64_t N, int64_t K) {
+  return M == 1 && K <= kGemvMaxK && gemv_shape_ok(N, K, gemv_shape(N, K));
+}
+
 int a16_ksplit(int path, int64_t M, int64_t N, int64_t K) {
+  if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   return path == W4A8_PATH_SKINNY ? skinny_a16_plan(M, N, K).ksplit : prefill_a16_ksplit(M, N, K);
 }
 
@@ -234,6 +241,7 @@ size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
 }
 
 int pick_a16_path(int64_t M, int64_t N, int64_t K) {
+  if (a16_gemv_ok(M, N, K)) return W4A8_PATH_GEMV;
   return M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL;
 }
 
@@ -241,6 +249,10 @@ size_t a16_workspace_any(int64_t M, int64_t N, int64_t K) {
   size_t need = a16_workspace_for(W4A8_PATH_PREFILL, M, N, K);
   if (M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0) {
     const size_t w = a16_workspace_for(W4A8_PATH_SKINNY, M, N, K);
+    if (w > need) need = w;
+  }
+  if (a16_gemv_ok(M, N, K)) {
+    const size_t w = a16_workspace_for(W4A8_PATH_GEMV, M, N, K);
     if (w > need) need = w;
   }
   return need;
@@ -263,8 +275,12 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
   if (path == W4A8_PATH_SKINNY && (M > 16 || skinny_a16_plan(M, N, K).ksplit == 0))
     return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "no W4A16 M <= 16 plan for M=%lld K=%lld",
                 (long long)M, (long long)K);
-  if (path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
-    return fail(W4A8_ERR_INVALID_ARG, "W4A16 paths are SKINNY and PREFILL (got %d)", (int)path);
+  if (path == W4A8_PATH_GEMV && !a16_gemv_ok(M, N, K))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "no W4A16 GEMV plan for M=%lld N=%lld K=%lld",
+                (long long)M, (long long)N, (long long)K);
+  if (path != W4A8_PATH_GEMV && path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
+    return fail(W4A8_ERR_INVALID_ARG, "W4A16 paths are GEMV, SKINNY and PREFILL (got %d)",
+                (int)path);
   if (path == W4A8_PATH_PREFILL && (2 * M * K > kPrefillMaxBytes || N * K / 2 > kPrefillMaxBytes))
     return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
                 "PREFILL path addresses activations and codes with 32-bit offsets");
@@ -301,9 +317,16 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
   a.ksplit = ks;
   a.cb = a.ks = 0;
   a.w8 = false;
+  if (path == W4A8_PATH_GEMV) {
+    const GemvShape gs = gemv_shape(N, K);
+    a.cb = gs.cb;
+    a.ks = gs.ks;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = path == W4A8_PATH_SKINNY ? launch_skinny_a16(a, st) : launch_prefill_a16(a, st);
+  hipError_t e = path == W4A8_PATH_GEMV     ? launch_gemv_a16(a, st)
+                 : path == W4A8_PATH_SKINNY ? launch_skinny_a16(a, st)
+                                            : launch_prefill_a16(a, st);
   if (e == hipSuccess && ks > 1) e = launch_splitk_reduce(a.workspace, ks, nullptr, M, N, y, st);
   return device_status(e, "w4a16 launch");
 }

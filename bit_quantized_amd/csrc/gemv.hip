@@ -48,7 +48,8 @@ constexpr int D = 4;                        // code blocks a wavefront keeps in 
 constexpr int kMaxRun = 12;                 // units per wavefront
 constexpr int kMaxCb = 12;                  // channel blocks per workgroup
 
-enum { X_BF16 = 0, X_F32 = 1, X_QUANTISED = 2 };
+// X_A16: W4A16, the bf16 token is used as it is (no quantisation)
+enum { X_BF16 = 0, X_F32 = 1, X_QUANTISED = 2, X_A16 = 3 };
 
 // Start of wavefront w's run in share units.
 __host__ __device__ constexpr int share_prefix(int w) {
@@ -73,6 +74,13 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int byte_sum8(uint2 v) {
   return __builtin_amdgcn_sdot4((int)v.y, 0x01010101,
                                 __builtin_amdgcn_sdot4((int)v.x, 0x01010101, 0, false), false);
+}
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+// a.lo * b.lo + a.hi * b.hi + c over two bf16 pairs, in float
+__device__ __forceinline__ float bf16_dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c,
+                                         false);
 }
 
 // Codes-plane block index of unit u of a workgroup's run.
@@ -113,7 +121,7 @@ __device__ __forceinline__ void load_next(__amdgpu_buffer_rsrc_t rsrc, int oob, 
 // two, pre-quantised codes -> one uint2 (in .x, .y).
 template <int XT>
 __device__ __forceinline__ void load_chunk(const GemmArgs& a, int ch, uint4* r) {
-  if constexpr (XT == X_BF16) {
+  if constexpr (XT == X_BF16 || XT == X_A16) {
     r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + 8 * ch);
   } else if constexpr (XT == X_F32) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + 8 * ch);
@@ -127,7 +135,7 @@ __device__ __forceinline__ void load_chunk(const GemmArgs& a, int ch, uint4* r) 
 
 template <int XT>
 __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
-  if constexpr (XT == X_BF16) {
+  if constexpr (XT == X_BF16 || XT == X_A16) {
     const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
     return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
   } else {
@@ -150,6 +158,9 @@ gemv_kernel(GemmArgs a) {
   const int K = (int)a.K, G = K / kGroup, NB = (int)(a.N / kBlockCols);
   int8_t* qs = reinterpret_cast<int8_t*>(smem);               // [K] activation codes
   int* rs = reinterpret_cast<int*>(smem + K);                  // [4G] per-quarter code sums
+  // W4A16 instead: the bf16 token [K] and its per-quarter float sums [4G]
+  constexpr bool A16 = XT == X_A16;
+  float* xsum = reinterpret_cast<float*>(smem + 2 * K);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -209,11 +220,46 @@ gemv_kernel(GemmArgs a) {
   __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
 
   for (int t = tid; t < kMaxCb * kWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
-  for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
+  if constexpr (!A16)
+    for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
   if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
 
-  if (wave < kQ) {
+  if (wave < kQ && A16) {
+    // ---- W4A16 stager: the token chunks go to LDS as they are, with the
+    // float sum of each lane quarter (chunks 2j, 2j+1, 8+2j, 9+2j of a
+    // group: the 32 inputs a streamer lane multiplies) taken in a fixed
+    // order across the four lanes that hold them
+    const int nbatch = (nch + kQChunks * kQThreads - 1) / (kQChunks * kQThreads);
+    for (int b = 0; b < nbatch; ++b) {
+      if (b > 0) {
+#pragma unroll
+        for (int i = 0; i < kQChunks; ++i)
+          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + tid, nch - 1), xr[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kQChunks; ++i) {
+        const int ch = (b * kQChunks + i) * kQThreads + tid;  // ch % 16 == lane % 16
+        const bool live = ch < nch;  // the same for the 16 lanes of a row (nch % 16 == 0)
+        float v = 0.0f;
+        if (live) {
+          *reinterpret_cast<uint4*>(smem + 16 * ch) = xr[i][0];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v += chunk_value<XT>(xr[i], e);
+        }
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 8);
+        if (live && (lane & 9) == 0) xsum[4 * (ch >> 4) + ((ch & 7) >> 1)] = v;
+      }
+    }
+    scale = 1.0f;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
+    if (lane == 0)
+      __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+  } else if (wave < kQ) {
     // ---- quantiser: token chunks (8 elements) qt, qt + 256, ... in batches
     // of kQChunks (the first batch is in flight already); the last batch
     // stays in registers for the second pass
@@ -298,7 +344,9 @@ gemv_kernel(GemmArgs a) {
     while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
            (unsigned)kQ)
       __builtin_amdgcn_s_sleep(1);
-    if constexpr (XT != X_QUANTISED)
+    if constexpr (A16)
+      scale = 1.0f;
+    else if constexpr (XT != X_QUANTISED)
       scale = __uint_as_float(
           __hip_atomic_load(&s_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) / 127.0f;
   }
@@ -324,6 +372,33 @@ gemv_kernel(GemmArgs a) {
             cur = ccb;
           }
           const int g = g0 + cg;
+          if constexpr (A16) {
+            // sum x (128 + q) over the lane's 32 inputs with bf16 pair dots:
+            // a code q (0..15) below the bf16 of 128 (0x4300) is exactly
+            // 128 + q; then minus (128 + z) times the quarter's sum of x
+            const uint8_t* xb = smem + 2 * (kGroup * g + 16 * j);
+            const uint4 xl0 = *reinterpret_cast<const uint4*>(xb);
+            const uint4 xl1 = *reinterpret_cast<const uint4*>(xb + 16);
+            const uint4 xh0 = *reinterpret_cast<const uint4*>(xb + 128);
+            const uint4 xh1 = *reinterpret_cast<const uint4*>(xb + 144);
+            const uint32_t xl[8] = {xl0.x, xl0.y, xl0.z, xl0.w, xl1.x, xl1.y, xl1.z, xl1.w};
+            const uint32_t xh[8] = {xh0.x, xh0.y, xh0.z, xh0.w, xh1.x, xh1.y, xh1.z, xh1.w};
+            const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              // code bytes 4w, 4w+1 (and 4w+2, 4w+3) into the low bytes of two halves
+              const uint32_t t01 = __builtin_amdgcn_perm(d[w], d[w], 0x0C010C00u);
+              const uint32_t t23 = __builtin_amdgcn_perm(d[w], d[w], 0x0C030C02u);
+              acc = bf16_dot2(xl[2 * w], (t01 & 0x000F000Fu) | 0x43004300u, acc);
+              acc = bf16_dot2(xl[2 * w + 1], (t23 & 0x000F000Fu) | 0x43004300u, acc);
+              acc = bf16_dot2(xh[2 * w], ((t01 >> 4) & 0x000F000Fu) | 0x43004300u, acc);
+              acc = bf16_dot2(xh[2 * w + 1], ((t23 >> 4) & 0x000F000Fu) | 0x43004300u, acc);
+            }
+            const uint32_t zbyte = reinterpret_cast<const uint8_t*>(&s_zero[wave][r])[c >> 1];
+            const float zf = (float)(int)(((zbyte >> zshift) & 0xFu) + 128u);
+            accf += s_scale[wave][r][c] * fmaf(-zf, xsum[4 * g + j], acc);
+          } else {
           const uint4 al = *reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * j);
           const uint4 ah = *reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * j);
           const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
@@ -346,6 +421,7 @@ gemv_kernel(GemmArgs a) {
               a.partials[((int64_t)16 * (nb0 + ccb) + c) * G + g] = pg;
           }
           accf += s_scale[wave][r][c] * (float)p;
+          }
           ++cg;
           const int wrap = (cg == gk) ? 1 : 0;
           cg -= wrap * gk;
@@ -381,7 +457,7 @@ template <int XT, bool KSPLIT, int QC>
 hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
-  const size_t lds = (size_t)a.K + 16 * (size_t)G;
+  const size_t lds = (XT == X_A16 ? 2 : 1) * (size_t)a.K + 16 * (size_t)G;
   if (a.partials)
     hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a);
   else
@@ -472,6 +548,8 @@ bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s) {
   const int64_t run = (ncb * gk_max * 4 + kShareTotal - 1) / kShareTotal;
   return ncb <= kMaxCb && run <= kMaxRun;
 }
+
+hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st) { return launch_xt<X_A16>(a, st); }
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st) {
   if (!a.x) return launch_xt<X_QUANTISED>(a, st);

@@ -155,6 +155,8 @@ int skinny_ksplit(int64_t M, int64_t N, int64_t K);
 bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype);
 int prefill_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
+// W4A16 (bf16 token in GemmArgs::x, M == 1) on the GEMV kernel; same grid rules.
+hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_skinny(GemmArgs a, hipStream_t st);
 // W4A16 (bf16 activations in GemmArgs::x, x_dtype 0) on the M <= 16 kernel:
 // its K split, chunks per thread and dynamic LDS; ksplit 0 when no split fits.

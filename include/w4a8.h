@@ -250,14 +250,19 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed, siz
  * (w4a8_pack_weights).  No activation quantisation:
  *   y[m][n] = bf16_rne( sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]) )
  * with q - z expanded exactly to bf16 and each group's products summed in
- * float32 on the bf16 matrix cores, then scaled by s in float32.
+ * float32 on the bf16 matrix cores, then scaled by s in float32 (the M == 1
+ * GEMV sums x * (128 + q) with float32 bf16-pair dots and subtracts
+ * (128 + z) times the float32 sum of x over the same inputs).
  *   x   device bfloat16 bits [M][K]
  *   y   device bfloat16 bits [M][N]
  *   workspace  device scratch of w4a16_linear_workspace_bytes(M, N, K, group)
  *     bytes (float split-K partials; may be NULL when that is 0)
- * Paths: SKINNY (M <= 16; each workgroup stages its K slice of the rows in
- * LDS, K split until it fits) and PREFILL (128-token tiles).
- * w4a16_linear_path forces one of the two (AUTO allowed), for tests.
+ * Paths: GEMV (M == 1, K <= 32768: the W4A8 GEMV's grid and weight stream,
+ * the bf16 token staged in LDS), SKINNY (M <= 16; each workgroup stages its
+ * K slice of the rows in LDS, K split until it fits) and PREFILL (128-token
+ * tiles).  w4a16_select_path names the path AUTO takes; w4a16_linear_path
+ * forces one (AUTO allowed), for tests, and returns
+ * W4A8_ERR_UNSUPPORTED_SHAPE when the forced path has no plan for the shape.
  */
 size_t w4a16_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 int w4a16_select_path(int64_t M, int64_t N, int64_t K);

@@ -256,7 +256,8 @@ def test_w4a16_rejections(lib):
     assert f(FAKE, FAKE2, pb - 16, 4, 256, 256, 128, y, None, 0, None) == -4
     assert f(FAKE, FAKE2, pb, 4, 256, 256, 128, FAKE2, None, 0, None) == -1   # y aliases packed
     g = lib.w4a16_linear_path
-    assert g(FAKE, FAKE2, pb, 4, 256, 256, 128, 1, y, None, 0, None) == -1    # no GEMV path
+    assert g(FAKE, FAKE2, pb, 4, 256, 256, 128, 1, y, None, 0, None) == -2    # GEMV needs M == 1
+    assert g(FAKE, FAKE2, pb, 1, 256, 256, 128, 9, y, None, 0, None) == -1    # no such path
     assert g(FAKE, FAKE2, pb, 17, 256, 256, 128, 2, y, None, 0, None) == -2   # SKINNY needs M <= 16
     pb2 = lib.w4a8_packed_weight_bytes(512, 18944, 128)
     need = lib.w4a16_linear_workspace_bytes(1, 512, 18944, 128)
@@ -264,3 +265,6 @@ def test_w4a16_rejections(lib):
     assert f(FAKE, FAKE2, pb2, 1, 512, 18944, 128, y, None, 0, None) == -4    # split K: workspace
     assert lib.w4a16_select_path(4, 3584, 18944) == 2
     assert lib.w4a16_select_path(17, 3584, 18944) == 3
+    assert lib.w4a16_select_path(1, 18944, 3584) == 1                         # GEMV
+    assert lib.w4a16_select_path(1, 3584, 18944) == 1
+    assert lib.w4a16_select_path(1, 256, 65536) == 2                          # K past the GEMV's LDS

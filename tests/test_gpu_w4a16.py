@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 REL = 4e-3
-SKINNY, PREFILL = 2, 3
+GEMV, SKINNY, PREFILL = 1, 2, 3
 
 
 @pytest.fixture(scope="module")
@@ -53,6 +53,10 @@ def _check(y, lin, rows):
 A16_SPECS = [
     synth.LinearSpec("a16_m1_up", 1, 3584, 18944, seed=110),
     synth.LinearSpec("a16_m1_k", 1, 3584, 512, seed=111),
+    synth.LinearSpec("a16_m1_down", 1, 18944, 3584, seed=123),
+    synth.LinearSpec("a16_m1_tiny", 1, 128, 16, seed=124),
+    synth.LinearSpec("a16_m1_kmax", 1, 32768, 256, seed=125),
+    synth.LinearSpec("a16_m1_ragged", 1, 1152, 4112, seed=126),
     synth.LinearSpec("a16_m2", 2, 640, 272, seed=112),
     synth.LinearSpec("a16_m3", 3, 1024, 512, seed=113),
     synth.LinearSpec("a16_m4_down", 4, 18944, 3584, seed=114),
@@ -80,6 +84,10 @@ def test_w4a16_linear(w4, spec):
     for rows in _rows(spec.M):
         _check(y, lin, rows)
     assert torch.equal(w4.w4a16_linear(x, W), y)          # deterministic
+    if spec.M == 1:
+        assert w4.w4a16_select_path(spec.M, spec.N, spec.K) == GEMV
+        ys = w4.w4a16_linear(x, W, path=SKINNY)           # the M <= 16 kernel, same row
+        _check(ys, lin, (0, 1))
     if spec.M <= 16:
         yp = w4.w4a16_linear(x, W, path=PREFILL)          # the other path, same rows
         _check(yp, lin, (0, spec.M))
@@ -95,3 +103,20 @@ def test_w4a16_symmetric_grid(w4):
     ref = oracle.w4a16_linear(lin["x"], lin["q"], z8, lin["s"])
     ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy(), ref, REL)
     assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+
+
+def test_w4a16_gemv_symmetric_and_zero_token(w4):
+    """M == 1 GEMV: symmetric grid (constant zero point 8), and an all-zero
+    token gives exactly zero."""
+    say("w4a16 gemv symmetric + zero token")
+    lin = synth.make_linear(synth.LinearSpec("a16_m1_sym", 1, 2048, 1024, seed=127))
+    W = w4.pack_weights(dev(lin["q"]), None, dev(lin["s"]))
+    x = dev(lin["x"].view(np.int16)).view(torch.bfloat16)
+    assert w4.w4a16_select_path(1, 1024, 2048) == GEMV
+    y = w4.w4a16_linear(x, W, path=GEMV)
+    z8 = np.full_like(lin["z"], 8)
+    ref = oracle.w4a16_linear(lin["x"], lin["q"], z8, lin["s"])
+    ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy(), ref, REL)
+    assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+    y0 = w4.w4a16_linear(torch.zeros_like(x), W, path=GEMV)
+    assert not torch.any(y0.float() != 0.0)
