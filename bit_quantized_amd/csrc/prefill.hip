@@ -274,34 +274,51 @@ prefill_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rqa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.qa), (short)0, (int)(a.M * a.K),
                                         kBufferWord3);
-  // activation tile of group g into buffer B (wave-uniform LDS address)
-#define PREFILL_DMA_A(B, g)                                                                 \
-  _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_)                                     \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rqa, &smem[B][kAOff + (kADma * wave + i_) * 1024], 16, \
-                                             off.a[i_], (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * kGroup)), 0, 0)
+  // W8: the weight halves are MFMA operands as stored, so they too go
+  // straight into LDS: block u = wave, half h to chunk 2u + h of the B area
+  const __amdgpu_buffer_rsrc_t rcw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w.codes), (short)0, W8 ? (int)(a.N * a.K) : 0, kBufferWord3);
+  // group g's LDS-direct operands into buffer B (wave-uniform LDS addresses)
+#define PREFILL_DMA(B, g)                                                                        \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_)                                        \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                  \
+          rqa, &smem[B][kAOff + (kADma * wave + i_) * 1024], 16, off.a[i_],                      \
+          (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * kGroup)), 0, 0);                  \
+    if constexpr (W8) {                                                                          \
+      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                          \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                \
+            rcw, &smem[B][kBOff + (2 * wave + h_) * kBlockBytes], 16, off.b + h_ * kBlockBytes, \
+            (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * 2 * kBlockBytes)), 0, 0);       \
+    }                                                                                            \
+  } while (0)
   Stage sb;
-  PREFILL_DMA_A(0, gb);
-  load_stage<W8>(a, off, gb, sb);
-  store_stage<W8>(smem[0], sb, off.zshift);
+  PREFILL_DMA(0, gb);
+  if constexpr (!W8) {
+    load_stage<W8>(a, off, gb, sb);
+    store_stage<W8>(smem[0], sb, off.zshift);
+  }
   __syncthreads();
   for (int64_t g = gb; g < ge; g += 2) {
     if (g + 1 < ge) {  // buffer 1 was last read before the previous barrier
-      PREFILL_DMA_A(1, g + 1);
-      load_stage<W8>(a, off, g + 1, sb);
+      PREFILL_DMA(1, g + 1);
+      if constexpr (!W8) load_stage<W8>(a, off, g + 1, sb);
     }
     compute(smem[0], g);
-    if (g + 1 < ge) store_stage<W8>(smem[1], sb, off.zshift);
+    if constexpr (!W8)
+      if (g + 1 < ge) store_stage<W8>(smem[1], sb, off.zshift);
     __syncthreads();
     if (g + 1 >= ge) break;
     if (g + 2 < ge) {
-      PREFILL_DMA_A(0, g + 2);
-      load_stage<W8>(a, off, g + 2, sb);
+      PREFILL_DMA(0, g + 2);
+      if constexpr (!W8) load_stage<W8>(a, off, g + 2, sb);
     }
     compute(smem[1], g + 1);
-    if (g + 2 < ge) store_stage<W8>(smem[0], sb, off.zshift);
+    if constexpr (!W8)
+      if (g + 2 < ge) store_stage<W8>(smem[0], sb, off.zshift);
     __syncthreads();
   }
-#undef PREFILL_DMA_A
+#undef PREFILL_DMA
 
   if constexpr (W8) {
     // int32 totals: to the workspace when K is split, else scaled to y (and
