@@ -240,9 +240,19 @@ size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
 }
 
+// The M <= 16 kernel copies each workgroup's K slice of the rows into LDS, so
+// long rows split K; past a 4-way split the 128-token prefill tiles are faster
+// (M = 16, K = 18944: a 16-way split takes 90 us, the prefill path 36 us;
+// M = 8 at a 4-way split: 31 us against 37 us).
+constexpr int kA16SkinnyMaxSplit = 4;
+
 int pick_a16_path(int64_t M, int64_t N, int64_t K) {
   if (a16_gemv_ok(M, N, K)) return W4A8_PATH_GEMV;
-  return M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL;
+  if (M > 16) return W4A8_PATH_PREFILL;
+  const int ks = skinny_a16_plan(M, N, K).ksplit;
+  const bool prefill_ok = 2 * M * K <= kPrefillMaxBytes && N * K / 2 <= kPrefillMaxBytes;
+  if (ks > 0 && (ks <= kA16SkinnyMaxSplit || !prefill_ok)) return W4A8_PATH_SKINNY;
+  return W4A8_PATH_PREFILL;
 }
 
 size_t a16_workspace_any(int64_t M, int64_t N, int64_t K) {

@@ -88,8 +88,11 @@ def test_w4a16_linear(w4, spec):
         assert w4.w4a16_select_path(spec.M, spec.N, spec.K) == GEMV
         ys = w4.w4a16_linear(x, W, path=SKINNY)           # the M <= 16 kernel, same row
         _check(ys, lin, (0, 1))
+    if 1 < spec.M <= 16:
+        ys = w4.w4a16_linear(x, W, path=SKINNY)           # both M <= 16 paths, same rows
+        _check(ys, lin, (0, spec.M))
     if spec.M <= 16:
-        yp = w4.w4a16_linear(x, W, path=PREFILL)          # the other path, same rows
+        yp = w4.w4a16_linear(x, W, path=PREFILL)
         _check(yp, lin, (0, spec.M))
 
 
