@@ -11,8 +11,8 @@
 // rounds over the compute units) splits into two roles that never meet at a
 // barrier before the last reduction:
 //   - kQ quantiser wavefronts load the token first (their requests lead the
-//     queue), take its absmax, quantise it into LDS (IEEE division, ties to
-//     even — the rule of w4a8_quant_act) with per-quarter code sums added by
+//     queue), take its absmax, quantise it into LDS (the rule of
+//     w4a8_quant_act bit for bit, ties to even) with per-quarter code sums added by
 //     integer LDS atomics (exact, so order-free), and raise an LDS flag; they
 //     synchronise among themselves through LDS counters;
 //   - the other wavefronts put D code blocks of their runs in flight at once,
@@ -297,6 +297,7 @@ gemv_kernel(GemmArgs a) {
       scale = __uint_as_float(
           __hip_atomic_load(&s_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) / 127.0f;
     }
+    const float inv = scale != 0.0f ? 1.0f / scale : 0.0f;  // correctly rounded
     for (int b = nbatch - 1; b >= 0; --b) {
       if (b != nbatch - 1) {
 #pragma unroll
@@ -311,17 +312,12 @@ gemv_kernel(GemmArgs a) {
           if constexpr (XT == X_QUANTISED) {
             pk = make_uint2(xr[i][0].x, xr[i][0].y);
           } else {
-            // an all-zero token has scale 0 and all-zero codes (no division)
-            const bool live = scale != 0.0f;
-            const float den = live ? scale : 1.0f;
-            uint32_t w[2] = {0u, 0u};
+            // the rule of w4a8_quant_act, bit for bit (quant8_codes); an
+            // all-zero token has scale 0 and all-zero codes
+            float v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float r = fminf(fmaxf(rintf(chunk_value<XT>(xr[i], e) / den), -127.0f), 127.0f);
-              r = live ? r : 0.0f;
-              w[e >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu) << (8 * (e & 3));
-            }
-            pk = make_uint2(w[0], w[1]);
+            for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
+            pk = scale != 0.0f ? quant8_codes(v, scale, inv) : make_uint2(0u, 0u);
           }
           *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
           // chunk ch covers elements 8(ch%16)..+7 of group ch/16: quarter

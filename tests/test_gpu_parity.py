@@ -396,6 +396,31 @@ def test_fused_skinny_zero_and_tie_rows(w4):
     assert not y_fused[1].float().abs().sum().item()
 
 
+@pytest.mark.parametrize("K", [3584, 18944])
+def test_fused_gemv_zero_and_tie_rows(w4, K):
+    """In-kernel quantisation of the M == 1 GEMV on an all-zero token (scale 0,
+    codes 0, y exactly 0) and on tokens of exact half-integer quotients (ties
+    to even): the codes (debug partials) equal the oracle's, and y is
+    bitwise that of the stand-alone quantiser + GEMV."""
+    say(f"fused gemv zero and tie rows K={K}")
+    spec = synth.LinearSpec("fg_rows", 3, K, 1024, seed=78, act="f32")
+    lin, W, _, _ = _setup(w4, spec)
+    x = lin["x"].copy()
+    x[1] = 0.0
+    rng = np.random.Generator(np.random.PCG64(79))
+    x[2] = (rng.integers(-127, 127, size=K) + 0.5).astype(np.float32)
+    x[2, 0] = 127.0
+    for m in range(3):
+        xd = dev(x[m:m + 1])
+        y_fused = w4.linear(xd, W)
+        qa, sa = w4.quant_act(xd)
+        qa_ref, sa_ref = oracle.quant_act(x[m:m + 1])
+        assert np.array_equal(qa.cpu().numpy(), qa_ref)
+        assert torch.equal(y_fused, w4.gemm(qa, sa, W))             # M == 1: the GEMV
+        if m == 1:
+            assert not y_fused.float().abs().sum().item()
+
+
 @pytest.mark.parametrize("M", [1, 4, 300])
 def test_symmetric_grid(w4, M):
     """Weights without zero points ("The 4-bit CPU path", section "W4A8": the
