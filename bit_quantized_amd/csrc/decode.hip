@@ -394,8 +394,7 @@ skinny_kernel(GemmArgs a) {
     // wavefronts through LDS
     // (the raw chunks stay packed in registers; they are widened twice)
     float amax = XChunk<T>::absmax(xr, NPT);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = wave_max64(amax);
     if (lane == 0) s_wmax[wave] = amax;
     __syncthreads();
     load_first();

@@ -64,11 +64,7 @@ __device__ __forceinline__ uint4 ntload16(const uint8_t* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_max64(v); }
 
 // Sum of the 8 signed bytes in a uint2.
 __device__ __forceinline__ int byte_sum8(uint2 v) {

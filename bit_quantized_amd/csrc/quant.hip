@@ -40,11 +40,7 @@ struct Chunk8<float> {
   }
 };
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave_max64(v); }
 
 // Codes of eight activations under one row scale (a zero row: codes 0).
 __device__ __forceinline__ uint2 quant8(const float* v, float amax, float scale) {

@@ -52,6 +52,27 @@ __device__ __forceinline__ uint32_t sub_zero_bytes(uint32_t nib4, uint32_t zz) {
   return ((nib4 | 0x80808080u) - zz) ^ 0x80808080u;
 }
 
+// Maximum of v over the 64 lanes of a wavefront, in every lane.  Max is
+// exact in any order, so the value is that of any reduction tree: DPP moves
+// take each 16-lane row to its maximum (quad swaps, half-row mirror, row
+// mirror), then the four row maxima are read into scalar registers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+  return fmaxf(v, o);
+}
+__device__ __forceinline__ float wave_max64(float v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = dpp_max_step<0x141>(v);  // row_half_mirror: the other quad of the half-row
+  v = dpp_max_step<0x140>(v);  // row_mirror: the other half of the row
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Codes of eight finite activations under a row scale s > 0 with inv the
 // correctly rounded 1 / s: rint(x / s) (IEEE quotient, ties to even) clamped
 // to [-127, 127], as bytes.  The quotient is taken as x * inv, which differs
