@@ -36,12 +36,10 @@ constexpr int kADma = BM / kADmaRows / (kThreads / 64);       // such loads per 
 // sits at chunk c ^ (r % 8) of the row's 128 bytes.
 __device__ __forceinline__ int a_chunk(int r, int c) { return c ^ (r & 7); }
 
-// One group's weight operands as they come from HBM, held in registers
-// while the previous group computes.
+// One group's W4 weight operands as they come from HBM, held in registers
+// while the previous group computes.  (W8 weights go straight into LDS.)
 struct Stage {
-  v4i b;          // W4: this thread's 16 packed bytes: block t/64, lane t%64
-                  // W8: half 0 of block t/64, lane t%64 (16 int8 weights)
-  v4i b8;         // W8: half 1 of the same block and lane
+  v4i b;          // this thread's 16 packed bytes: block t/64, lane t%64
   uint32_t zb;    // the byte holding that lane's zero point
   float s;        // scale of channel t%16 of block (t/16)%8
 };
@@ -78,37 +76,22 @@ __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, i
   return o;
 }
 
-template <bool W8>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
                                            Stage& st) {
-  if constexpr (W8) {
-    const uint8_t* codes = a.w.codes + g * 2 * kBlockBytes;
-    st.b = *reinterpret_cast<const v4i*>(codes + o.b);
-    st.b8 = *reinterpret_cast<const v4i*>(codes + o.b + kBlockBytes);
-  } else {
-    const uint8_t* codes = a.w.codes + g * kBlockBytes;
-    const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
-    const float* scales = a.w.scales + g * 16;
-    st.b = *reinterpret_cast<const v4i*>(codes + o.b);
-    st.zb = zeros[o.z];
-    st.s = scales[o.s];
-  }
+  const uint8_t* codes = a.w.codes + g * kBlockBytes;
+  const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
+  const float* scales = a.w.scales + g * 16;
+  st.b = *reinterpret_cast<const v4i*>(codes + o.b);
+  st.zb = zeros[o.z];
+  st.s = scales[o.s];
 }
 
 // Stage -> LDS.  The packed codes are unpacked here, once per workgroup, to
 // signed q - z bytes in exactly the order the MFMA B operand is read: block
 // u, half h (low nibbles = input channels 16j..16j+15 of the group, high =
 // 64+16j..), lane L.
-template <bool W8>
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
   const int tid = threadIdx.x;
-  if constexpr (W8) {
-    // the packed halves are already the MFMA B operand: copied as they are
-    const int u = tid >> 6, L = tid & 63;
-    *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + L * 16) = st.b;
-    *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + L * 16) = st.b8;
-    return;
-  }
   const uint32_t zz = ((st.zb >> zshift) & 0xFu) * 0x01010101u;
   v4i lo, hi;
 #pragma unroll
@@ -292,30 +275,30 @@ prefill_kernel(GemmArgs a) {
             (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * 2 * kBlockBytes)), 0, 0);       \
     }                                                                                            \
   } while (0)
-  Stage sb;
+  Stage sb;  // W4 only
   PREFILL_DMA(0, gb);
   if constexpr (!W8) {
-    load_stage<W8>(a, off, gb, sb);
-    store_stage<W8>(smem[0], sb, off.zshift);
+    load_stage(a, off, gb, sb);
+    store_stage(smem[0], sb, off.zshift);
   }
   __syncthreads();
   for (int64_t g = gb; g < ge; g += 2) {
     if (g + 1 < ge) {  // buffer 1 was last read before the previous barrier
       PREFILL_DMA(1, g + 1);
-      if constexpr (!W8) load_stage<W8>(a, off, g + 1, sb);
+      if constexpr (!W8) load_stage(a, off, g + 1, sb);
     }
     compute(smem[0], g);
     if constexpr (!W8)
-      if (g + 1 < ge) store_stage<W8>(smem[1], sb, off.zshift);
+      if (g + 1 < ge) store_stage(smem[1], sb, off.zshift);
     __syncthreads();
     if (g + 1 >= ge) break;
     if (g + 2 < ge) {
       PREFILL_DMA(0, g + 2);
-      if constexpr (!W8) load_stage<W8>(a, off, g + 2, sb);
+      if constexpr (!W8) load_stage(a, off, g + 2, sb);
     }
     compute(smem[1], g + 1);
     if constexpr (!W8)
-      if (g + 2 < ge) store_stage<W8>(smem[0], sb, off.zshift);
+      if (g + 2 < ge) store_stage(smem[0], sb, off.zshift);
     __syncthreads();
   }
 #undef PREFILL_DMA
