@@ -116,15 +116,15 @@ __device__ __forceinline__ void load_next(__amdgpu_buffer_rsrc_t rsrc, int oob, 
 // One 8-element chunk of the token (chunk ch), raw: bf16 -> one uint4, f32 ->
 // two, pre-quantised codes -> one uint2 (in .x, .y).
 template <int XT>
-__device__ __forceinline__ void load_chunk(const GemmArgs& a, int ch, uint4* r) {
+__device__ __forceinline__ void load_chunk(const void* x, int ch, uint4* r) {
   if constexpr (XT == X_BF16 || XT == X_A16) {
-    r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + 8 * ch);
+    r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + 8 * ch);
   } else if constexpr (XT == X_F32) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(a.x) + 8 * ch);
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(x) + 8 * ch);
     r[0] = p[0];
     r[1] = p[1];
   } else {
-    const uint2 c2 = *reinterpret_cast<const uint2*>(a.qa + 8 * ch);
+    const uint2 c2 = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(x) + 8 * ch);
     r[0] = make_uint4(c2.x, c2.y, 0u, 0u);
   }
 }
@@ -142,16 +142,22 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
 
 // kQChunks: token chunks (8 elements) a quantiser thread holds at once; the
 // whole token fits in one batch when K / 8 <= 256 * kQChunks.
+// The operands the first loads need lead the argument list as scalars, so
+// that they arrive preloaded in scalar registers (kernel-argument preload)
+// instead of behind a memory round trip; the rest stays in GemmArgs.
+// xin: the token (bf16 / f32) or, pre-quantised, its codes.
 template <int XT, bool DEBUG, bool KSPLIT, int kQChunks>
 __global__ void __launch_bounds__(kThreads)
-gemv_kernel(GemmArgs a) {
+gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+            const uint8_t* __restrict__ zeros, const void* __restrict__ xin, int K, int cb_q,
+            int cb_r, GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ __attribute__((aligned(16))) float s_scale[kWaves][kMaxRun][16];
   __shared__ __attribute__((aligned(16))) uint2 s_zero[kWaves][kMaxRun];
   __shared__ float part[kMaxCb][kWaves][16];
   // [0] token absmax bits, [1] quantisers past the absmax, [2] quantisers done
   __shared__ unsigned s_sync[4];
-  const int K = (int)a.K, G = K / kGroup, NB = (int)(a.N / kBlockCols);
+  const int G = K / kGroup, NB = (int)(a.N / kBlockCols);
   int8_t* qs = reinterpret_cast<int8_t*>(smem);               // [K] activation codes
   int* rs = reinterpret_cast<int*>(smem + K);                  // [4G] per-quarter code sums
   // W4A16 instead: the bf16 token [K] and its per-quarter float sums [4G]
@@ -166,8 +172,8 @@ gemv_kernel(GemmArgs a) {
   // everything up to the first loads is kept short, because those loads
   // start the memory pipe.
   const int bx = blockIdx.x;
-  const int nb0 = bx * a.cb_q + min(bx, a.cb_r);
-  const int nb1 = nb0 + a.cb_q + (bx < a.cb_r ? 1 : 0);
+  const int nb0 = bx * cb_q + min(bx, cb_r);
+  const int nb1 = nb0 + cb_q + (bx < cb_r ? 1 : 0);
   int g0 = 0, gk = G;
   if constexpr (KSPLIT) {
     g0 = split_point(G, gridDim.y, blockIdx.y);
@@ -183,13 +189,13 @@ gemv_kernel(GemmArgs a) {
   const int last = nrun > 0 ? nrun - 1 : 0;
   const int64_t bs = unit_block<KSPLIT>(u0 + min(lane >> 2, last), nb0, G, g0, gk);
   const int64_t bz = unit_block<KSPLIT>(u0 + min(lane & 15, last), nb0, G, g0, gk);
-  const float* hot_s = a.w.scales + bs * 16 + 4 * (lane & 3);
+  const float* hot_s = scales + bs * 16 + 4 * (lane & 3);
   // the run's blocks: [first, first + span) of the codes plane
   const int64_t first = unit_block<KSPLIT>(u0, nb0, G, g0, gk);
   const int span = nrun > 0 ? (int)(unit_block<KSPLIT>(u1 - 1, nb0, G, g0, gk) - first + 1) : 0;
   const int oob = span * kBlockBytes;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.w.codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
+      const_cast<uint8_t*>(codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
       kBufferWord3);
   uint4 wv[D];
   int lu = u0, lg = 0, rel = 0;  // next unit to load (lg: its group within the slice)
@@ -205,10 +211,10 @@ gemv_kernel(GemmArgs a) {
   // first loads: every wavefront's run metadata (two small loads), then the
   // quantisers' token chunks and the streamers' first D code blocks
   s4 = *reinterpret_cast<const uint4*>(hot_s);
-  z2 = *reinterpret_cast<const uint2*>(a.w.zeros + bz * kZeroBlockBytes);
+  z2 = *reinterpret_cast<const uint2*>(zeros + bz * kZeroBlockBytes);
   if (wave < kQ) {
 #pragma unroll
-    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(a, min(i * kQThreads + tid, nch - 1), xr[i]);
+    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(xin, min(i * kQThreads + tid, nch - 1), xr[i]);
   } else {
 #pragma unroll
     for (int i = 0; i < D; ++i) load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
@@ -231,7 +237,7 @@ gemv_kernel(GemmArgs a) {
       if (b > 0) {
 #pragma unroll
         for (int i = 0; i < kQChunks; ++i)
-          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + tid, nch - 1), xr[i]);
+          load_chunk<XT>(xin, min((b * kQChunks + i) * kQThreads + tid, nch - 1), xr[i]);
       }
 #pragma unroll
       for (int i = 0; i < kQChunks; ++i) {
@@ -266,7 +272,7 @@ gemv_kernel(GemmArgs a) {
       if (b > 0) {
 #pragma unroll
         for (int i = 0; i < kQChunks; ++i)
-          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
+          load_chunk<XT>(xin, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
       }
       if constexpr (XT != X_QUANTISED) {
 #pragma unroll
@@ -298,7 +304,7 @@ gemv_kernel(GemmArgs a) {
       if (b != nbatch - 1) {
 #pragma unroll
         for (int i = 0; i < kQChunks; ++i)
-          load_chunk<XT>(a, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
+          load_chunk<XT>(xin, min((b * kQChunks + i) * kQThreads + qt, nch - 1), xr[i]);
       }
 #pragma unroll
       for (int i = 0; i < kQChunks; ++i) {
@@ -450,10 +456,13 @@ hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (XT == X_A16 ? 2 : 1) * (size_t)a.K + 16 * (size_t)G;
+  const void* xin = XT == X_QUANTISED ? static_cast<const void*>(a.qa) : a.x;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a.w.codes,
+                       a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC>), grid, dim3(kThreads), lds, st,
+                       a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
   return hipGetLastError();
 }
 
