@@ -29,8 +29,8 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # the leading scalar kernel arguments (up to 7) arrive preloaded in SGPRs
-    "-mllvm", "-amdgpu-kernarg-preload-count=7",
+    # the leading scalar kernel arguments (up to 9) arrive preloaded in SGPRs
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     "-I", os.path.join(ROOT, "include"),
 ]
 

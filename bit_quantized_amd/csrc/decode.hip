@@ -156,9 +156,24 @@ template <> struct XChunk<float> {  // two 16-byte loads
 // by s into the accumulator.
 constexpr int kA16Slack = 1536;  // LDS past the staged rows that padded quads may read
 
+// The operands the first loads need also lead the argument list as scalars,
+// so that they arrive preloaded in scalar registers (kernel-argument preload)
+// rather than behind a memory round trip; they overwrite the same fields of
+// the by-value GemmArgs, which supplies everything else.
 template <bool DEBUG, int MP, int NPT, typename T, bool W8, bool A16 = false>
 __global__ void __launch_bounds__(kThreads)
-skinny_kernel(GemmArgs a) {
+skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+              const uint8_t* __restrict__ zeros, const int8_t* __restrict__ qa,
+              const void* __restrict__ x, int M, int K, int gq, int gr, GemmArgs a) {
+  a.w.codes = codes;
+  a.w.scales = scales;
+  a.w.zeros = zeros;
+  a.qa = qa;
+  a.x = x;
+  a.M = M;
+  a.K = K;
+  a.gq = gq;
+  a.gr = gr;
   constexpr bool STAGE = NPT > 0;            // activations staged in LDS
   constexpr bool FUSED = STAGE && !A16;      // ... as int8 codes quantised here
   constexpr int kUnitBytes = W8 ? 2 * kBlockBytes : kBlockBytes;  // codes per unit
@@ -525,6 +540,10 @@ w8_splitk_reduce_kernel(const int32_t* __restrict__ ws, int ksplit, const float*
 
 // Split K only while the channel blocks alone leave compute units idle, and
 // never below one group per wavefront.
+// Launch arguments of skinny_kernel: the preloaded scalars, then the struct.
+#define SKINNY_ARGS(a) \
+  (a).w.codes, (a).w.scales, (a).w.zeros, (a).qa, (a).x, (int)(a).M, (int)(a).K, (a).gq, (a).gr, (a)
+
 int pick_ksplit(int64_t N, int64_t K) {
   const int64_t nb = N / kBlockCols, G = K / kGroup;
   const int64_t cus = device_cus();
@@ -536,9 +555,9 @@ int pick_ksplit(int64_t N, int64_t K) {
 template <int MP, bool W8>
 void launch_mp(const GemmArgs& a, dim3 grid, hipStream_t st) {
   if (a.partials)
-    hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, SKINNY_ARGS(a));
   else
-    hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, SKINNY_ARGS(a));
 }
 
 // Chunks of eight activations per thread of the fused variant, or 0 when it
@@ -562,12 +581,12 @@ template <int MP, typename T, bool W8>
 void launch_fused_mp(const GemmArgs& a, dim3 grid, int npt, hipStream_t st) {
   const size_t lds = (size_t)(a.M * (a.K + 16) + 512);
   if (npt == 4)
-    hipLaunchKernelGGL((skinny_kernel<false, MP, 4, T, W8>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((skinny_kernel<false, MP, 4, T, W8>), grid, dim3(kThreads), lds, st, SKINNY_ARGS(a));
   else if constexpr (sizeof(T) == 2) {
     if (npt == 8)
-      hipLaunchKernelGGL((skinny_kernel<false, MP, 8, T, W8>), grid, dim3(kThreads), lds, st, a);
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 8, T, W8>), grid, dim3(kThreads), lds, st, SKINNY_ARGS(a));
     else
-      hipLaunchKernelGGL((skinny_kernel<false, MP, 10, T, W8>), grid, dim3(kThreads), lds, st, a);
+      hipLaunchKernelGGL((skinny_kernel<false, MP, 10, T, W8>), grid, dim3(kThreads), lds, st, SKINNY_ARGS(a));
   }
 }
 
@@ -639,7 +658,7 @@ hipError_t launch_skinny_a16(GemmArgs a, hipStream_t st) {
   const dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit), block(kThreads);
   const int mp = pow2_rows(a.M);
 #define W4A16_LAUNCH(MPV, NPTV) \
-  hipLaunchKernelGGL((skinny_kernel<false, MPV, NPTV, uint16_t, false, true>), grid, block, p.lds, st, a)
+  hipLaunchKernelGGL((skinny_kernel<false, MPV, NPTV, uint16_t, false, true>), grid, block, p.lds, st, SKINNY_ARGS(a))
   if (p.npt == 4) {
     if (mp == 2) W4A16_LAUNCH(2, 4); else if (mp == 4) W4A16_LAUNCH(4, 4);
     else if (mp == 8) W4A16_LAUNCH(8, 4); else W4A16_LAUNCH(16, 4);
