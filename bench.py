@@ -293,7 +293,7 @@ def bench_w8a8(torch, w4, args):
         gemm_ms = graph_launches_ms(torch, lambda i: w4.w8a8_gemm(qa, sa, Ws[i % R], out=y,
                                                                   workspace=gws), n)
         r = {"workload": f"{spec.name} M={M} K={K} N={N} (W8A8: quant + int8 GEMM)",
-             "path": {2: "skinny", 3: "prefill"}[w4.w8a8_select_path(M, N, K)],
+             "path": {1: "gemv", 2: "skinny", 3: "prefill"}[w4.w8a8_select_path(M, N, K)],
              "us_per_step": round(step_ms * 1e3, 3), "gemm_us": round(gemm_ms * 1e3, 3),
              "parity": {"rows": list(rows), "max_err": err, "bound": bound}}
         if M <= 16:

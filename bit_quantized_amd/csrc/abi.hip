@@ -356,22 +356,38 @@ int check_w8_shape(int64_t N, int64_t K) {
   return W4A8_OK;
 }
 
-int pick_w8_path(int64_t M) { return M <= 16 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL; }
+// The GEMV serves W8A8 at M == 1 when the token fits its LDS and the grid its
+// tables (the same rule as W4A8).
+bool w8_gemv_ok(int64_t M, int64_t N, int64_t K) {
+  return M == 1 && K <= kGemvMaxK && gemv_shape_ok(N, K, gemv_shape(N, K));
+}
+
+int pick_w8_path(int64_t M, int64_t N, int64_t K) {
+  if (w8_gemv_ok(M, N, K)) return W4A8_PATH_GEMV;
+  return M <= 16 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL;
+}
 
 int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
+  if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K) : prefill_ksplit(M, N, K);
 }
 
-// int32 split-K partials [ksplit][M][N].
+// int32 split-K partials [ksplit][M][N], then (GEMV only) one 256-byte slot
+// for the scale the fused quantiser computes.
 size_t w8_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = w8_ksplit(path, M, N, K);
-  return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
+  if (ks <= 1) return 0;
+  return round256((size_t)ks * (size_t)M * (size_t)N * 4) + (path == W4A8_PATH_GEMV ? 256 : 0);
 }
 
 size_t w8_gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
   size_t need = w8_workspace_for(W4A8_PATH_PREFILL, M, N, K);
   if (M <= 16) {
     const size_t w = w8_workspace_for(W4A8_PATH_SKINNY, M, N, K);
+    if (w > need) need = w;
+  }
+  if (w8_gemv_ok(M, N, K)) {
+    const size_t w = w8_workspace_for(W4A8_PATH_GEMV, M, N, K);
     if (w > need) need = w;
   }
   return need;
@@ -399,10 +415,13 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   const size_t need = (size_t)w8_packed_bytes(N, K);
   if (packed_bytes_ < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
-  if (path == W4A8_PATH_AUTO) path = pick_w8_path(M);
-  if (path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
-    return fail(W4A8_ERR_INVALID_ARG, "W8A8 paths are SKINNY (M <= 16) and PREFILL (got %d)",
-                (int)path);
+  if (path == W4A8_PATH_AUTO) path = pick_w8_path(M, N, K);
+  if (path != W4A8_PATH_GEMV && path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
+    return fail(W4A8_ERR_INVALID_ARG,
+                "W8A8 paths are GEMV (M == 1), SKINNY (M <= 16) and PREFILL (got %d)", (int)path);
+  if (path == W4A8_PATH_GEMV && !w8_gemv_ok(M, N, K))
+    return fail(W4A8_ERR_UNSUPPORTED_SHAPE, "no W8A8 GEMV plan for M=%lld N=%lld K=%lld",
+                (long long)M, (long long)N, (long long)K);
   if (path == W4A8_PATH_SKINNY && M > 16)
     return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
   if (path == W4A8_PATH_PREFILL && (M * K > kPrefillMaxBytes || N * K > kPrefillMaxBytes))
@@ -410,7 +429,8 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
                 "PREFILL path addresses activations and codes with 32-bit offsets "
                 "(M*K=%lld, N*K=%lld, limit %lld)",
                 (long long)(M * K), (long long)(N * K), (long long)kPrefillMaxBytes);
-  if (fused && !(path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype) && !debug))
+  if (fused && (debug || !(path == W4A8_PATH_GEMV ||
+                            (path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype)))))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
@@ -462,12 +482,24 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   a.ksplit = ks;
   a.cb = a.ks = 0;
   a.w8 = true;
+  const float* sa_for_reduce = act.sa;
+  if (path == W4A8_PATH_GEMV) {
+    const GemvShape gs = gemv_shape(N, K);
+    a.cb = gs.cb;
+    a.ks = gs.ks;
+    if (fused && ks > 1) {  // the in-kernel scale, for the reduction
+      a.sa_ws = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_need - 256);
+      sa_for_reduce = a.sa_ws;
+    }
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = path == W4A8_PATH_SKINNY ? launch_skinny(a, st) : launch_prefill(a, st);
+  hipError_t e = path == W4A8_PATH_GEMV     ? launch_gemv(a, st)
+                 : path == W4A8_PATH_SKINNY ? launch_skinny(a, st)
+                                            : launch_prefill(a, st);
   if (e == hipSuccess && ks > 1 && (y || a.partials))
-    e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, act.sa, a.w.scales,
-                                M, N, y, a.partials, a.m_begin, a.m_end, st);
+    e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, sa_for_reduce,
+                                a.w.scales, M, N, y, a.partials, a.m_begin, a.m_end, st);
   return device_status(e, "w8a8 gemm launch");
 }
 
@@ -741,7 +773,7 @@ size_t w8a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return w8_gemm_workspace_any(M, N, K);
 }
 
-int w8a8_select_path(int64_t M, int64_t, int64_t) { return M <= 0 ? 0 : pick_w8_path(M); }
+int w8a8_select_path(int64_t M, int64_t N, int64_t K) { return M <= 0 ? 0 : pick_w8_path(M, N, K); }
 
 int w8a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes_,
               int64_t M, int64_t N, int64_t K, uint16_t* y, void* workspace,
@@ -777,11 +809,13 @@ int w8a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (!workspace || workspace_bytes < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-  // One launch when the skinny kernel can quantise these rows itself.
-  if (pick_w8_path(M) == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, x_dtype))
-    return run_w8_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K,
-                       W4A8_PATH_SKINNY, 0, 0, nullptr, y, workspace, workspace_bytes, stream,
-                       false);
+  // One launch when the GEMV (M == 1) or the M <= 16 kernel can quantise
+  // these rows itself.
+  const int fpath = pick_w8_path(M, N, K);
+  if (fpath == W4A8_PATH_GEMV ||
+      (fpath == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, x_dtype)))
+    return run_w8_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, fpath,
+                       0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
   const size_t xbytes = (size_t)M * K * (x_dtype == W4A8_F32 ? 4 : 2);
   if (overlaps(workspace, need, x, xbytes) || overlaps(workspace, need, packed, packed_bytes_))
     return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");

@@ -99,13 +99,19 @@ __device__ __forceinline__ int64_t unit_block(int u, int nb0, int G, int g0, int
 // compile-time count of loads in flight and waits stay exact) but with an
 // offset beyond the descriptor's range, which the hardware answers with zeros
 // and no memory request.  Branch-free on purpose.
+// A unit is H KiB: H = 1 for the int4 codes, 2 for the W8A8 weights (two
+// 1 KiB halves, input channels 0-63 and 64-127 of the group).
+template <int H>
 __device__ __forceinline__ void load_next(__amdgpu_buffer_rsrc_t rsrc, int oob, int u1, int G,
                                           int gk, int lane, int& lu, int& lg, int& rel,
-                                          uint4& w) {
+                                          uint4 (&w)[H]) {
   const int live = lu < u1 ? 1 : 0;  // wave-uniform
-  const int off = live ? rel * kBlockBytes + 16 * lane : oob;
-  const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNontemporal);
-  w = make_uint4(t.x, t.y, t.z, t.w);
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int off = live ? (rel * H + h) * kBlockBytes + 16 * lane : oob;
+    const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kNontemporal);
+    w[h] = make_uint4(t.x, t.y, t.z, t.w);
+  }
   lu += live;
   lg += live;
   const int wrap = (lg == gk) ? 1 : 0;
@@ -146,7 +152,10 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
 // that they arrive preloaded in scalar registers (kernel-argument preload)
 // instead of behind a memory round trip; the rest stays in GemmArgs.
 // xin: the token (bf16 / f32) or, pre-quantised, its codes.
-template <int XT, bool DEBUG, bool KSPLIT, int kQChunks>
+// W8: the W8A8 weights (two 1 KiB halves per unit, already in operand order;
+// one scale per channel in `scales`, no zero points): raw int8 dots, int32
+// totals over the run, the scales applied once in the epilogue.
+template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint8_t* __restrict__ zeros, const void* __restrict__ xin, int K, int cb_q,
@@ -163,6 +172,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   // W4A16 instead: the bf16 token [K] and its per-quarter float sums [4G]
   constexpr bool A16 = XT == X_A16;
   float* xsum = reinterpret_cast<float*>(smem + 2 * K);
+  constexpr int H = W8 ? 2 : 1;  // KiB per unit
+  int (*part_i)[kWaves][16] = reinterpret_cast<int (*)[kWaves][16]>(part);  // W8: int32 pieces
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -193,11 +204,11 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   // the run's blocks: [first, first + span) of the codes plane
   const int64_t first = unit_block<KSPLIT>(u0, nb0, G, g0, gk);
   const int span = nrun > 0 ? (int)(unit_block<KSPLIT>(u1 - 1, nb0, G, g0, gk) - first + 1) : 0;
-  const int oob = span * kBlockBytes;
+  const int oob = span * H * kBlockBytes;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(codes + (nrun > 0 ? first : 0) * kBlockBytes), (short)0, oob,
+      const_cast<uint8_t*>(codes + (nrun > 0 ? first : 0) * H * kBlockBytes), (short)0, oob,
       kBufferWord3);
-  uint4 wv[D];
+  uint4 wv[D][H];
   int lu = u0, lg = 0, rel = 0;  // next unit to load (lg: its group within the slice)
   if constexpr (KSPLIT) lg = nrun > 0 ? u0 % gk : 0;
   uint4 s4;
@@ -210,19 +221,21 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
 
   // first loads: every wavefront's run metadata (two small loads), then the
   // quantisers' token chunks and the streamers' first D code blocks
-  s4 = *reinterpret_cast<const uint4*>(hot_s);
-  z2 = *reinterpret_cast<const uint2*>(zeros + bz * kZeroBlockBytes);
+  if constexpr (!W8) {  // (W8: one scale per channel, read in the epilogue)
+    s4 = *reinterpret_cast<const uint4*>(hot_s);
+    z2 = *reinterpret_cast<const uint2*>(zeros + bz * kZeroBlockBytes);
+  }
   if (wave < kQ) {
 #pragma unroll
     for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(xin, min(i * kQThreads + tid, nch - 1), xr[i]);
   } else {
 #pragma unroll
-    for (int i = 0; i < D; ++i) load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
 
   for (int t = tid; t < kMaxCb * kWaves * 16; t += kThreads) (&part[0][0][0])[t] = 0.0f;
-  if constexpr (!A16)
+  if constexpr (!A16 && !W8)
     for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
   if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
@@ -260,7 +273,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+      load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   } else if (wave < kQ) {
     // ---- quantiser: token chunks (8 elements) qt, qt + 256, ... in batches
     // of kQChunks (the first batch is in flight already); the last batch
@@ -324,7 +337,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;
           // chunk ch covers elements 8(ch%16)..+7 of group ch/16: quarter
           // ((ch % 16) % 8) / 2 of the lane layout (0..63 and 64..127 fold)
-          atomicAdd(&rs[4 * (ch >> 4) + ((ch & 7) >> 1)], byte_sum8(pk));
+          if constexpr (!W8) atomicAdd(&rs[4 * (ch >> 4) + ((ch & 7) >> 1)], byte_sum8(pk));
         }
       }
     }
@@ -335,7 +348,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     // then the quantiser streams its own (shorter) run
 #pragma unroll
     for (int i = 0; i < D; ++i)
-      load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+      load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   } else {
     // ---- streamer: metadata and D code blocks are in flight; the flag
     if constexpr (XT == X_QUANTISED) scale = a.sa[0];
@@ -348,12 +361,15 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
       scale = __uint_as_float(
           __hip_atomic_load(&s_sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) / 127.0f;
   }
-  if ((lane >> 2) < kMaxRun) *reinterpret_cast<uint4*>(&s_scale[wave][lane >> 2][4 * (lane & 3)]) = s4;
-  if (lane < kMaxRun) s_zero[wave][lane] = z2;
+  if constexpr (!W8) {
+    if ((lane >> 2) < kMaxRun) *reinterpret_cast<uint4*>(&s_scale[wave][lane >> 2][4 * (lane & 3)]) = s4;
+    if (lane < kMaxRun) s_zero[wave][lane] = z2;
+  }
 
   // the run, through the ring
   {
     float accf = 0.0f;
+    int acci = 0;  // W8: int32 total of the current channel block
     int ccb = nrun > 0 ? u0 / gk : 0, cg = nrun > 0 ? u0 % gk : 0;  // compute position
     int cur = ccb;
     const int zshift = (c & 1) * 4;
@@ -363,10 +379,17 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
         const int r = ub + i;  // position in the run
         if (r < nrun) {
           if (ccb != cur) {
-            accf += __shfl_xor(accf, 16);
-            accf += __shfl_xor(accf, 32);
-            if (j == 0) part[cur][wave][c] = accf;
-            accf = 0.0f;
+            if constexpr (W8) {
+              acci += __shfl_xor(acci, 16);
+              acci += __shfl_xor(acci, 32);
+              if (j == 0) part_i[cur][wave][c] = acci;
+              acci = 0;
+            } else {
+              accf += __shfl_xor(accf, 16);
+              accf += __shfl_xor(accf, 32);
+              if (j == 0) part[cur][wave][c] = accf;
+              accf = 0.0f;
+            }
             cur = ccb;
           }
           const int g = g0 + cg;
@@ -381,7 +404,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint4 xh1 = *reinterpret_cast<const uint4*>(xb + 144);
             const uint32_t xl[8] = {xl0.x, xl0.y, xl0.z, xl0.w, xl1.x, xl1.y, xl1.z, xl1.w};
             const uint32_t xh[8] = {xh0.x, xh0.y, xh0.z, xh0.w, xh1.x, xh1.y, xh1.z, xh1.w};
-            const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+            const uint32_t d[4] = {wv[i][0].x, wv[i][0].y, wv[i][0].z, wv[i][0].w};
             float acc = 0.0f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -396,10 +419,24 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint32_t zbyte = reinterpret_cast<const uint8_t*>(&s_zero[wave][r])[c >> 1];
             const float zf = (float)(int)(((zbyte >> zshift) & 0xFu) + 128u);
             accf += s_scale[wave][r][c] * fmaf(-zf, xsum[4 * g + j], acc);
+          } else if constexpr (W8) {
+            // the two halves' int8 weights against the codes of the same
+            // input channels: no unpacking, no zero point, no per-group scale
+            const uint4 al = *reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * j);
+            const uint4 ah = *reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * j);
+            const uint32_t w0[4] = {wv[i][0].x, wv[i][0].y, wv[i][0].z, wv[i][0].w};
+            const uint32_t w1[4] = {wv[i][1].x, wv[i][1].y, wv[i][1].z, wv[i][1].w};
+            const uint32_t l4[4] = {al.x, al.y, al.z, al.w};
+            const uint32_t h4[4] = {ah.x, ah.y, ah.z, ah.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              acci = __builtin_amdgcn_sdot4((int)w0[w], (int)l4[w], acci, false);
+              acci = __builtin_amdgcn_sdot4((int)w1[w], (int)h4[w], acci, false);
+            }
           } else {
           const uint4 al = *reinterpret_cast<const uint4*>(qs + kGroup * g + 16 * j);
           const uint4 ah = *reinterpret_cast<const uint4*>(qs + kGroup * g + 64 + 16 * j);
-          const uint32_t d[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+          const uint32_t d[4] = {wv[i][0].x, wv[i][0].y, wv[i][0].z, wv[i][0].w};
           const uint32_t l4[4] = {al.x, al.y, al.z, al.w};
           const uint32_t h4[4] = {ah.x, ah.y, ah.z, ah.w};
           int acc = 0;
@@ -426,12 +463,18 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           ccb += wrap;
         }
         // refill this slot with the unit D ahead
-        load_next(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+        load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
       }
     }
-    accf += __shfl_xor(accf, 16);
-    accf += __shfl_xor(accf, 32);
-    if (nrun > 0 && j == 0) part[cur][wave][c] = accf;
+    if constexpr (W8) {
+      acci += __shfl_xor(acci, 16);
+      acci += __shfl_xor(acci, 32);
+      if (nrun > 0 && j == 0) part_i[cur][wave][c] = acci;
+    } else {
+      accf += __shfl_xor(accf, 16);
+      accf += __shfl_xor(accf, 32);
+      if (nrun > 0 && j == 0) part[cur][wave][c] = accf;
+    }
   }
   __syncthreads();
 
@@ -439,6 +482,21 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   const int ncb = nb1 - nb0;
   for (int t = tid; t < ncb * 16; t += kThreads) {
     const int cbl = t >> 4, cc = t & 15;
+    if constexpr (W8) {
+      // exact int32 total (order-free), then y = sa * (sw * P) as on every
+      // W8A8 path; split K: the slice's total to the int32 workspace
+      int total = part_i[cbl][0][cc];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) total += part_i[cbl][w][cc];
+      const int64_t n = (int64_t)16 * (nb0 + cbl) + cc;
+      if (gridDim.y == 1) {
+        if (DEBUG && a.partials && a.m_begin == 0 && a.m_end > 0) a.partials[n] = total;
+        if (a.y) a.y[n] = f32_to_bf16_rne(scale * (scales[n] * (float)total));
+      } else {
+        reinterpret_cast<int32_t*>(a.workspace)[(int64_t)blockIdx.y * a.N + n] = total;
+      }
+      continue;
+    }
     float total = part[cbl][0][cc];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) total += part[cbl][w][cc];
@@ -451,17 +509,17 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   }
 }
 
-template <int XT, bool KSPLIT, int QC>
+template <int XT, bool KSPLIT, int QC, bool W8>
 hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (XT == X_A16 ? 2 : 1) * (size_t)a.K + 16 * (size_t)G;
   const void* xin = XT == X_QUANTISED ? static_cast<const void*>(a.qa) : a.x;
   if (a.partials)
-    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC>), grid, dim3(kThreads), lds, st, a.w.codes,
+    hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st, a.w.codes,
                        a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC>), grid, dim3(kThreads), lds, st,
+    hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st,
                        a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
   return hipGetLastError();
 }
@@ -469,21 +527,21 @@ hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
 // Token chunks per quantiser thread: as few as hold the token in one batch
 // (fewer, shorter loads on the critical path); past 20480 inputs (float
 // tokens: past 8192) the token is quantised in batches of 4 chunks.
-template <int XT, bool KSPLIT>
+template <int XT, bool KSPLIT, bool W8>
 hipError_t launch_qc(const GemmArgs& a, hipStream_t st) {
   const int64_t nch = a.K / 8, per = 64 * kQ;
-  if (nch <= 2 * per) return launch_ks<XT, KSPLIT, 2>(a, st);
-  if (nch <= 4 * per || XT == X_F32) return launch_ks<XT, KSPLIT, 4>(a, st);
-  if (nch <= 10 * per) return launch_ks<XT, KSPLIT, 10>(a, st);
-  return launch_ks<XT, KSPLIT, 4>(a, st);
+  if (nch <= 2 * per) return launch_ks<XT, KSPLIT, 2, W8>(a, st);
+  if (nch <= 4 * per || XT == X_F32) return launch_ks<XT, KSPLIT, 4, W8>(a, st);
+  if (nch <= 10 * per) return launch_ks<XT, KSPLIT, 10, W8>(a, st);
+  return launch_ks<XT, KSPLIT, 4, W8>(a, st);
 }
 
-template <int XT>
+template <int XT, bool W8 = false>
 hipError_t launch_xt(GemmArgs a, hipStream_t st) {
   const int NB = (int)(a.N / kBlockCols);
   a.cb_q = NB / a.cb;  // workgroup b holds cb_q blocks, plus one if b < cb_r
   a.cb_r = NB % a.cb;
-  return a.ksplit > 1 ? launch_qc<XT, true>(a, st) : launch_qc<XT, false>(a, st);
+  return a.ksplit > 1 ? launch_qc<XT, true, W8>(a, st) : launch_qc<XT, false, W8>(a, st);
 }
 
 }  // namespace
@@ -553,6 +611,11 @@ bool gemv_shape_ok(int64_t N, int64_t K, const GemvShape& s) {
 hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st) { return launch_xt<X_A16>(a, st); }
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st) {
+  if (a.w8) {  // W8A8 weights (a.w.scales: one per channel)
+    if (!a.x) return launch_xt<X_QUANTISED, true>(a, st);
+    if (a.x_dtype == 0) return launch_xt<X_BF16, true>(a, st);
+    return launch_xt<X_F32, true>(a, st);
+  }
   if (!a.x) return launch_xt<X_QUANTISED>(a, st);
   if (a.x_dtype == 0) return launch_xt<X_BF16>(a, st);
   return launch_xt<X_F32>(a, st);

@@ -317,8 +317,9 @@ int w8a8_pack_weights(const int8_t* qw, const float* sw, int64_t N, int64_t K, v
 int w8a8_unpack_weights(const void* packed, size_t packed_bytes, int64_t N, int64_t K, int8_t* qw,
                         float* sw, void* stream);
 
-/* Path for an M x N x K W8A8 product: W4A8_PATH_SKINNY for M <= 16 (M == 1
- * included), W4A8_PATH_PREFILL otherwise. */
+/* Path for an M x N x K W8A8 product: W4A8_PATH_GEMV for M == 1 when the
+ * token fits the GEMV (K <= 32768, as for W4A8), W4A8_PATH_SKINNY for
+ * M <= 16, W4A8_PATH_PREFILL otherwise. */
 int w8a8_select_path(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -335,8 +336,8 @@ int w8a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t pack
               size_t workspace_bytes, void* stream);
 
 /*
- * w8a8_gemm_debug — the same kernels with a forced path (AUTO, SKINNY for
- * M <= 16, or PREFILL) and the exact int32 totals written for rows
+ * w8a8_gemm_debug — the same kernels with a forced path (AUTO, GEMV for
+ * M == 1, SKINNY for M <= 16, or PREFILL) and the exact int32 totals written for rows
  * [m_begin, m_end):  totals device int32 [m_end - m_begin][N] (may be NULL);
  * y_or_null as in w4a8_gemm_debug.
  */
@@ -348,8 +349,9 @@ int w8a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
 /*
  * w8a8_linear — quantisation (the rule of w4a8_quant_act) and the W8A8 GEMM
  * from raw activations; bitwise identical to w4a8_quant_act + w8a8_gemm.
- * For M <= 16 whose rows fit (the same limits as w4a8_linear) it is one
- * launch: the kernel quantises the rows into LDS itself.
+ * At M == 1 (the GEMV) and for M <= 16 whose rows fit (the same limits as
+ * w4a8_linear) it is one launch: the kernel quantises the rows into LDS
+ * itself.
  *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
  *   workspace  device scratch of w8a8_linear_workspace_bytes(M, N, K) bytes,
  *     required on every path

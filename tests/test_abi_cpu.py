@@ -206,12 +206,14 @@ def test_w8_debug_and_path_rejections(lib):
     f = lib.w8a8_gemm_debug
     pb = lib.w8a8_packed_weight_bytes(256, 256)
     y = ctypes.c_void_p(1 << 28)
-    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 1, 0, 4, None, y, None, 0, None) == -1   # no GEMV
+    assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 1, 0, 4, None, y, None, 0, None) == -2   # GEMV: M == 1
+    assert f(FAKE, FAKE, FAKE2, pb, 1, 256, 256, 9, 0, 1, None, y, None, 0, None) == -1   # no such path
     assert f(FAKE, FAKE, FAKE2, pb, 17, 256, 256, 2, 0, 17, None, y, None, 0, None) == -1  # SKINNY M
     assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 0, 2, 5, None, y, None, 0, None) == -1   # window
     assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 7, 0, 4, None, y, None, 0, None) == -1   # enum
     assert f(FAKE, FAKE, FAKE2, pb, 4, 256, 256, 0, 0, 4, MIS, y, None, 0, None) == -3
-    assert lib.w8a8_select_path(1, 18944, 3584) == 2
+    assert lib.w8a8_select_path(1, 18944, 3584) == 1                           # GEMV
+    assert lib.w8a8_select_path(1, 256, 65536) == 2                            # K past the GEMV
     assert lib.w8a8_select_path(16, 3584, 18944) == 2
     assert lib.w8a8_select_path(17, 3584, 18944) == 3
 

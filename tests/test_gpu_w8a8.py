@@ -23,7 +23,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 REL = 4e-3
-SKINNY, PREFILL = 2, 3
+GEMV, SKINNY, PREFILL = 1, 2, 3
 
 
 @pytest.fixture(scope="module")
@@ -82,6 +82,8 @@ def test_w8_pack_bytes_and_round_trip(w4, N, K):
 W8_SPECS = [
     synth.LinearSpec("w8_m1_decode_up", 1, 3584, 18944, seed=80),
     synth.LinearSpec("w8_m1_ksplit", 1, 18944, 512, seed=81),
+    synth.LinearSpec("w8_m1_ragged", 1, 1152, 4112, seed=97),
+    synth.LinearSpec("w8_m1_down", 1, 18944, 3584, seed=98),
     synth.LinearSpec("w8_m2", 2, 256, 256, seed=82, act="f32"),
     synth.LinearSpec("w8_m3", 3, 640, 272, seed=83),
     synth.LinearSpec("w8_m4", 4, 1024, 512, seed=84),
@@ -103,7 +105,7 @@ def test_w8_totals_and_output(w4, spec):
     qa_ref, sa_ref = oracle.quant_act(lin["x"])
     assert np.array_equal(qa.cpu().numpy(), qa_ref)
     assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_ref.view(np.uint32))
-    paths = ([SKINNY] if spec.M <= 16 else []) + [PREFILL]
+    paths = ([GEMV] if spec.M == 1 else []) + ([SKINNY] if spec.M <= 16 else []) + [PREFILL]
     ys = {}
     for path in paths:
         for (m0, m1) in _windows(spec.M):
@@ -122,6 +124,7 @@ def test_w8_totals_and_output(w4, spec):
 
 W8_LINEAR_SPECS = [
     synth.LinearSpec("w8l_m1", 1, 3584, 3584, seed=92),
+    synth.LinearSpec("w8l_m1_ksplit_f32", 1, 18944, 512, seed=99, act="f32"),
     synth.LinearSpec("w8l_m4_fused", 4, 18944, 3584, seed=93),
     synth.LinearSpec("w8l_m16_fused_f32", 16, 2048, 2048, seed=94, act="f32"),
     synth.LinearSpec("w8l_m16_two_launch", 16, 18944, 512, seed=95),
@@ -163,3 +166,6 @@ def test_w8_extreme_values(w4):
     for path in (SKINNY, PREFILL):
         P, _ = w4.w8a8_gemm_debug(qa, sa, W, path=path)
         assert np.array_equal(P.cpu().numpy(), P_ref), path
+    for m in (0, 1):  # one row at a time through the GEMV
+        P, _ = w4.w8a8_gemm_debug(qa[m:m + 1].clone(), sa[m:m + 1].clone(), W, path=GEMV)
+        assert np.array_equal(P.cpu().numpy(), P_ref[m:m + 1]), ("gemv", m)
