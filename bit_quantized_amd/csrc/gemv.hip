@@ -32,6 +32,11 @@
 // summed with cross-lane shuffles and the pieces of a channel block (several
 // wavefronts may share one) in fixed wavefront order through LDS, so the
 // result never depends on timing.
+// The same grid and stream serve two more weight/activation pairs:
+//   - W4A16 (X_A16): the quantisers become stagers that copy the bf16 token
+//     into LDS with its per-quarter float sums; lanes take bf16 pair dots;
+//   - W8A8 (W8): 2 KiB units of int8 weights in operand order, raw dot4,
+//     exact int32 totals and one per-channel scale in the epilogue.
 #include <atomic>
 
 #include "w4a8_internal.h"
