@@ -68,6 +68,28 @@ int pick_path(int64_t M, int64_t K) {
   return W4A8_PATH_PREFILL;
 }
 
+// The prefill kernels address the activation plane with 32-bit offsets.
+// Taller matrices run as consecutive row chunks on the stream, each chunk at
+// most kPrefillMaxBytes of activations (whole 256-row tiles where a tile
+// fits); 0 when a single row is already too long.
+int64_t prefill_chunk_rows(int64_t K, int64_t bytes_per_value) {
+  const int64_t rows = kPrefillMaxBytes / (K * bytes_per_value);
+  return rows >= 256 ? rows / 256 * 256 : rows;
+}
+
+// Row window [m_begin, m_end) of a debug call, restricted to the chunk of
+// rows [m0, m0 + mc): the chunk-local window and the row offset of its first
+// row in the caller's partials (empty window: begin == end == 0).
+struct ChunkWindow {
+  int64_t begin, end, out_row;
+};
+ChunkWindow chunk_window(int64_t m_begin, int64_t m_end, int64_t m0, int64_t mc) {
+  const int64_t b = m_begin > m0 ? m_begin : m0;
+  const int64_t e = m_end < m0 + mc ? m_end : m0 + mc;
+  if (b >= e) return ChunkWindow{0, 0, 0};
+  return ChunkWindow{b - m0, e - m0, b - m_begin};
+}
+
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
@@ -135,11 +157,11 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
                 (long long)kGemvMaxK, (long long)K);
   if (path == W4A8_PATH_SKINNY && M > 16)
     return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
-  if (path == W4A8_PATH_PREFILL && (M * K > kPrefillMaxBytes || N * K / 2 > kPrefillMaxBytes))
+  if (path == W4A8_PATH_PREFILL && (prefill_chunk_rows(K, 1) == 0 || N * K / 2 > kPrefillMaxBytes))
     return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
-                "PREFILL path addresses activations and codes with 32-bit offsets "
-                "(M*K=%lld, N*K/2=%lld, limit %lld)",
-                (long long)(M * K), (long long)(N * K / 2), (long long)kPrefillMaxBytes);
+                "PREFILL path addresses a row of activations and the codes with 32-bit offsets "
+                "(K=%lld, N*K/2=%lld, limit %lld)",
+                (long long)K, (long long)(N * K / 2), (long long)kPrefillMaxBytes);
   if (fused && path != W4A8_PATH_GEMV &&
       !(path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype) && !debug))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
@@ -204,12 +226,35 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // start from a clean error state
   hipError_t e;
+  if (path == W4A8_PATH_PREFILL) {
+    // row chunks (one chunk unless M*K exceeds the 32-bit offsets); a split
+    // K reuses the front of the workspace, chunk after chunk on the stream
+    const int64_t rows = prefill_chunk_rows(K, 1);
+    const int64_t G = K / kGroup;
+    e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
+      const int64_t mc = M - m0 < rows ? M - m0 : rows;
+      GemmArgs c = a;
+      c.qa = a.qa + m0 * K;
+      c.sa = a.sa + m0;
+      c.M = mc;
+      c.y = y ? y + m0 * N : nullptr;
+      if (a.partials) {
+        const ChunkWindow w = chunk_window(a.m_begin, a.m_end, m0, mc);
+        c.m_begin = w.begin;
+        c.m_end = w.end;
+        c.partials = w.begin < w.end ? a.partials + w.out_row * N * G : nullptr;
+      }
+      e = launch_prefill(c, st);
+      if (e == hipSuccess && ks > 1 && c.y)
+        e = launch_splitk_reduce(c.workspace, ks, c.sa, mc, N, c.y, st);
+    }
+    return device_status(e, "gemm launch");
+  }
   if (path == W4A8_PATH_GEMV)
     e = launch_gemv(a, st);
-  else if (path == W4A8_PATH_SKINNY)
-    e = launch_skinny(a, st);
   else
-    e = launch_prefill(a, st);
+    e = launch_skinny(a, st);
   if (e == hipSuccess && ks > 1 && y)
     e = launch_splitk_reduce(a.workspace, ks, sa_for_reduce, M, N, y, st);
   return device_status(e, "gemm launch");
@@ -250,7 +295,7 @@ int pick_a16_path(int64_t M, int64_t N, int64_t K) {
   if (a16_gemv_ok(M, N, K)) return W4A8_PATH_GEMV;
   if (M > 16) return W4A8_PATH_PREFILL;
   const int ks = skinny_a16_plan(M, N, K).ksplit;
-  const bool prefill_ok = 2 * M * K <= kPrefillMaxBytes && N * K / 2 <= kPrefillMaxBytes;
+  const bool prefill_ok = prefill_chunk_rows(K, 2) > 0 && N * K / 2 <= kPrefillMaxBytes;
   if (ks > 0 && (ks <= kA16SkinnyMaxSplit || !prefill_ok)) return W4A8_PATH_SKINNY;
   return W4A8_PATH_PREFILL;
 }
@@ -291,9 +336,9 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
   if (path != W4A8_PATH_GEMV && path != W4A8_PATH_SKINNY && path != W4A8_PATH_PREFILL)
     return fail(W4A8_ERR_INVALID_ARG, "W4A16 paths are GEMV, SKINNY and PREFILL (got %d)",
                 (int)path);
-  if (path == W4A8_PATH_PREFILL && (2 * M * K > kPrefillMaxBytes || N * K / 2 > kPrefillMaxBytes))
+  if (path == W4A8_PATH_PREFILL && (prefill_chunk_rows(K, 2) == 0 || N * K / 2 > kPrefillMaxBytes))
     return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
-                "PREFILL path addresses activations and codes with 32-bit offsets");
+                "PREFILL path addresses a row of activations and the codes with 32-bit offsets");
   const int ks = a16_ksplit(path, M, N, K);
   const size_t ws_need = a16_workspace_for(path, M, N, K);
   if (ws_need && (!workspace || workspace_bytes < ws_need))
@@ -334,9 +379,22 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = path == W4A8_PATH_GEMV     ? launch_gemv_a16(a, st)
-                 : path == W4A8_PATH_SKINNY ? launch_skinny_a16(a, st)
-                                            : launch_prefill_a16(a, st);
+  if (path == W4A8_PATH_PREFILL) {
+    // row chunks, as for W4A8 (bf16 rows: two bytes per value)
+    const int64_t rows = prefill_chunk_rows(K, 2);
+    hipError_t e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
+      const int64_t mc = M - m0 < rows ? M - m0 : rows;
+      GemmArgs c = a;
+      c.x = x + m0 * K;
+      c.M = mc;
+      c.y = y + m0 * N;
+      e = launch_prefill_a16(c, st);
+      if (e == hipSuccess && ks > 1) e = launch_splitk_reduce(c.workspace, ks, nullptr, mc, N, c.y, st);
+    }
+    return device_status(e, "w4a16 launch");
+  }
+  hipError_t e = path == W4A8_PATH_GEMV ? launch_gemv_a16(a, st) : launch_skinny_a16(a, st);
   if (e == hipSuccess && ks > 1) e = launch_splitk_reduce(a.workspace, ks, nullptr, M, N, y, st);
   return device_status(e, "w4a16 launch");
 }
@@ -424,11 +482,11 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
                 (long long)M, (long long)N, (long long)K);
   if (path == W4A8_PATH_SKINNY && M > 16)
     return fail(W4A8_ERR_INVALID_ARG, "SKINNY path needs M <= 16 (M=%lld)", (long long)M);
-  if (path == W4A8_PATH_PREFILL && (M * K > kPrefillMaxBytes || N * K > kPrefillMaxBytes))
+  if (path == W4A8_PATH_PREFILL && (prefill_chunk_rows(K, 1) == 0 || N * K > kPrefillMaxBytes))
     return fail(W4A8_ERR_UNSUPPORTED_SHAPE,
-                "PREFILL path addresses activations and codes with 32-bit offsets "
-                "(M*K=%lld, N*K=%lld, limit %lld)",
-                (long long)(M * K), (long long)(N * K), (long long)kPrefillMaxBytes);
+                "PREFILL path addresses a row of activations and the codes with 32-bit offsets "
+                "(K=%lld, N*K=%lld, limit %lld)",
+                (long long)K, (long long)(N * K), (long long)kPrefillMaxBytes);
   if (fused && (debug || !(path == W4A8_PATH_GEMV ||
                             (path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype)))))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
@@ -494,9 +552,31 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t e = path == W4A8_PATH_GEMV     ? launch_gemv(a, st)
-                 : path == W4A8_PATH_SKINNY ? launch_skinny(a, st)
-                                            : launch_prefill(a, st);
+  if (path == W4A8_PATH_PREFILL) {
+    // row chunks, as for W4A8; the totals of the debug window per chunk
+    const int64_t rows = prefill_chunk_rows(K, 1);
+    hipError_t e = hipSuccess;
+    for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
+      const int64_t mc = M - m0 < rows ? M - m0 : rows;
+      GemmArgs c = a;
+      c.qa = a.qa + m0 * K;
+      c.sa = a.sa + m0;
+      c.M = mc;
+      c.y = y ? y + m0 * N : nullptr;
+      if (a.partials) {
+        const ChunkWindow w = chunk_window(a.m_begin, a.m_end, m0, mc);
+        c.m_begin = w.begin;
+        c.m_end = w.end;
+        c.partials = w.begin < w.end ? a.partials + w.out_row * N : nullptr;
+      }
+      e = launch_prefill(c, st);
+      if (e == hipSuccess && ks > 1 && (c.y || c.partials))
+        e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, c.sa,
+                                    a.w.scales, mc, N, c.y, c.partials, c.m_begin, c.m_end, st);
+    }
+    return device_status(e, "w8a8 gemm launch");
+  }
+  hipError_t e = path == W4A8_PATH_GEMV ? launch_gemv(a, st) : launch_skinny(a, st);
   if (e == hipSuccess && ks > 1 && (y || a.partials))
     e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, sa_for_reduce,
                                 a.w.scales, M, N, y, a.partials, a.m_begin, a.m_end, st);

@@ -61,8 +61,11 @@ extern "C" {
 
 /* GEMM paths (M buckets).  AUTO picks GEMV for M == 1 (K <= 32768, else
  * SKINNY), SKINNY for 2 <= M <= 16, PREFILL for M > 16; the choice depends on
- * (M, N, K) only.  PREFILL needs M*K < 2^31 and N*K/2 < 2^31 (32-bit operand
- * offsets); larger shapes return W4A8_ERR_UNSUPPORTED_SHAPE. */
+ * (M, N, K) only.  PREFILL addresses the codes and each launch's activations
+ * with 32-bit offsets: an activation matrix of 2^31 bytes or more runs as
+ * consecutive row chunks (one launch each, in order on the stream, with the
+ * same results as one launch); N*K/2 >= 2^31 (N*K for W8A8 weights) or a
+ * single row of 2^31 bytes returns W4A8_ERR_UNSUPPORTED_SHAPE. */
 #define W4A8_PATH_AUTO 0
 #define W4A8_PATH_GEMV 1
 #define W4A8_PATH_SKINNY 2
