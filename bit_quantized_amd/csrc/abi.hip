@@ -285,18 +285,12 @@ size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
 }
 
-// The M <= 16 kernel copies each workgroup's K slice of the rows into LDS, so
-// long rows split K; past a 4-way split the 128-token prefill tiles are faster
-// (M = 16, K = 18944: a 16-way split takes 90 us, the prefill path 36 us;
-// M = 8 at a 4-way split: 31 us against 37 us).
-constexpr int kA16SkinnyMaxSplit = 4;
-
+// M <= 16 takes the M <= 16 kernel whenever it has a plan (it beat the
+// 128-token prefill tiles at every shape measured: M = 16, K = 18944 -> N =
+// 3584 23 us against 34 us; K = 3584 -> N = 18944 34 us against 42 us).
 int pick_a16_path(int64_t M, int64_t N, int64_t K) {
   if (a16_gemv_ok(M, N, K)) return W4A8_PATH_GEMV;
-  if (M > 16) return W4A8_PATH_PREFILL;
-  const int ks = skinny_a16_plan(M, N, K).ksplit;
-  const bool prefill_ok = prefill_chunk_rows(K, 2) > 0 && N * K / 2 <= kPrefillMaxBytes;
-  if (ks > 0 && (ks <= kA16SkinnyMaxSplit || !prefill_ok)) return W4A8_PATH_SKINNY;
+  if (M <= 16 && skinny_a16_plan(M, N, K).ksplit > 0) return W4A8_PATH_SKINNY;
   return W4A8_PATH_PREFILL;
 }
 

@@ -155,6 +155,11 @@ template <> struct XChunk<float> {  // two 16-byte loads
 // of the group, the same slots in A and B), and the fp32 group sum is scaled
 // by s into the accumulator.
 constexpr int kA16Slack = 1536;  // LDS past the staged rows that padded quads may read
+//
+// A16 with NPT == 0 instead reads each unit's A operands straight from the
+// row-major bf16 rows, four 16-byte loads per lane per unit (step t's eight
+// values, exactly the MFMA layout), so the rows need no LDS and K no split.
+// Units past a wavefront's run and rows >= M read as zeros.
 
 // The operands the first loads need also lead the argument list as scalars,
 // so that they arrive preloaded in scalar registers (kernel-argument preload)
@@ -176,11 +181,12 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
   a.gr = gr;
   constexpr bool STAGE = NPT > 0;            // activations staged in LDS
   constexpr bool FUSED = STAGE && !A16;      // ... as int8 codes quantised here
+  constexpr bool DIRECT16 = A16 && !STAGE;   // bf16 A operands loaded per unit
   constexpr int kUnitBytes = W8 ? 2 * kBlockBytes : kBlockBytes;  // codes per unit
   constexpr int CW = W8 ? 2 : 1;                                  // code loads per unit
   using S = ActShape<MP>;
-  constexpr int kQuadLoads = STAGE ? 0 : S::kQuadLoads;
-  constexpr int kSlotLoads = STAGE ? 0 : S::kSlotLoads;
+  constexpr int kQuadLoads = STAGE || DIRECT16 ? 0 : S::kQuadLoads;
+  constexpr int kSlotLoads = STAGE ? 0 : (DIRECT16 ? 4 : S::kSlotLoads);
   constexpr int QL = kQuadLoads > 0 ? kQuadLoads : 1;
   constexpr int SL = kSlotLoads > 0 ? kSlotLoads : 1;
   __shared__ float red[kWaves][4][64];
@@ -237,7 +243,8 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
   const __amdgpu_buffer_rsrc_t rz =
       W8 ? rsrc_of(a.w.scales, 0)
          : rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
-  const __amdgpu_buffer_rsrc_t ra = rsrc_of(a.qa, FUSED ? 0 : a.M * a.K);
+  const __amdgpu_buffer_rsrc_t ra =
+      DIRECT16 ? rsrc_of(a.x, a.M * a.K * 2) : rsrc_of(a.qa, FUSED ? 0 : a.M * a.K);
   const int oob = 0x7FFFFFF0;  // beyond every descriptor
 
   // activation row segment this lane fetches (row >= M: none)
@@ -268,8 +275,17 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
     }
   };
   // per-unit operands of unit u: codes and (MP >= 8) the activations
+  // DIRECT16: byte offset of this lane's step-0 operand in unit u (row r16,
+  // input channels 16j.. of the group; step t adds 128 (t / 2) + 16 (t % 2))
+  const int a16_lane = r16 < a.M ? r16 * (int)a.K * 2 + gb * 2 * kGroup + 32 * j : oob;
   auto load_unit = [&](int u, v4u* w, v4i* act) __attribute__((always_inline)) {
-    if constexpr (kSlotLoads > 0) {
+    if constexpr (DIRECT16) {
+      const int o = u < nrun && a16_lane != oob ? a16_lane + u * 2 * kGroup : oob;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        act[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ra, o == oob ? oob : o + 128 * (t >> 1) + 16 * (t & 1), 0, 0));
+    } else if constexpr (kSlotLoads > 0) {
 #pragma unroll
       for (int h = 0; h < kSlotLoads; ++h)
         act[h] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
@@ -306,7 +322,11 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {  // step t: nibble half t / 2, code bytes 8 (t % 2) ..
-        const v4i av = *reinterpret_cast<const v4i*>(qs + off + (t >> 1) * kGroup + (t & 1) * 16);
+        v4i av;
+        if constexpr (DIRECT16)
+          av = au[t];
+        else
+          av = *reinterpret_cast<const v4i*>(qs + off + (t >> 1) * kGroup + (t & 1) * 16);
         const int sh = (t >> 1) * 4;
         int b0, b1, b2, b3;
         codes_to_bf16x2((w[0][2 * (t & 1)] >> sh) & 0x0F0F0F0Fu, zz, b0, b1);
@@ -386,7 +406,7 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       __builtin_amdgcn_sched_barrier(0);  // slot order = issue order, so waits stay exact
     }
   };
-  if constexpr (A16) {
+  if constexpr (A16 && STAGE) {
     // copy the slice's rows to LDS as they are, then the first weight loads.
     // The units that pad a run's last quad multiply zero weights by whatever
     // lies past the run (row pads, the slack after the rows): zeroed here,
@@ -632,20 +652,28 @@ int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 // W4A16 on the M <= 16 kernel: K is split at least as much as filling the
 // machine asks, and further until one workgroup's slice of the rows fits the
 // LDS budget and takes at most 8 chunks of eight per thread.
+// The K split is the one that fills the machine (as for W4A8).  The rows are
+// staged in LDS when the workgroup's slice of them fits (read once, with
+// coalesced loads); otherwise each wavefront loads its A operands per unit
+// straight from memory (npt 0).  Measured at K = 18944 -> N = 3584: staging
+// that needed a further K split took 21.4 / 29.2 / 85.7 us at M = 4 / 8 / 16,
+// direct loads 16.5 / 18.0 / 23.1 us; where the rows fit, staging is as fast
+// or faster (M = 4, K = 3584 -> N = 18944: 23.8 us against 30.3 us).
 A16Plan skinny_a16_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t G = K / kGroup;
+  const int ks = pick_ksplit(N, K);
+  // the first workgroup's slice is the longest: 16 runs of gq groups, plus
+  // one more group for each of the first gr runs
+  const int64_t parts = (int64_t)ks * kWaves, gq = G / parts, gr = G % parts;
+  const int64_t slice = kWaves * gq + (gr < kWaves ? gr : kWaves);
+  // (slack: a wavefront's padded last quad reads up to three units, 3 x 256
+  // bytes, plus one operand span past its run)
+  const int64_t lds = M * (2 * kGroup * slice + 16) + kA16Slack;
   const int64_t mp = pow2_rows(M);
-  for (int ks = pick_ksplit(N, K); ks <= G && ks <= 64; ks *= 2) {
-    // the first workgroup's slice is the longest: 16 runs of gq groups, plus
-    // one more group for each of the first gr runs
-    const int64_t parts = (int64_t)ks * kWaves, gq = G / parts, gr = G % parts;
-    const int64_t slice = kWaves * gq + (gr < kWaves ? gr : kWaves);
-    // (slack: a wavefront's padded last quad reads up to three units, 3 x 256
-    // bytes, plus one operand span past its run)
-    const int64_t lds = M * (2 * kGroup * slice + 16) + kA16Slack;
-    const int64_t npt = (kGroup / 8 * slice + kThreads / mp - 1) / (kThreads / mp);
-    if (lds <= kFusedLdsBytes && npt <= 8) return A16Plan{ks, npt <= 4 ? 4 : 8, (size_t)lds};
-  }
+  const int64_t npt = (kGroup / 8 * slice + kThreads / mp - 1) / (kThreads / mp);
+  if (lds <= kFusedLdsBytes && npt <= 8) return A16Plan{ks, npt <= 4 ? 4 : 8, (size_t)lds};
+  // direct loads address the rows with 32-bit offsets
+  if (M * K * 2 <= kPrefillMaxBytes) return A16Plan{ks, 0, 0};
   return A16Plan{0, 0, 0};
 }
 
@@ -656,6 +684,11 @@ hipError_t launch_skinny_a16(GemmArgs a, hipStream_t st) {
   a.gq = (int)(G / parts);
   a.gr = (int)(G % parts);
   const dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit), block(kThreads);
+  if (p.npt == 0) {
+    hipLaunchKernelGGL((skinny_kernel<false, 16, 0, uint16_t, false, true>), grid, block, 0, st,
+                       SKINNY_ARGS(a));
+    return hipGetLastError();
+  }
   const int mp = pow2_rows(a.M);
 #define W4A16_LAUNCH(MPV, NPTV) \
   hipLaunchKernelGGL((skinny_kernel<false, MPV, NPTV, uint16_t, false, true>), grid, block, p.lds, st, SKINNY_ARGS(a))

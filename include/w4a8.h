@@ -262,9 +262,10 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed, siz
  *     bytes (float split-K partials; may be NULL when that is 0)
  * Paths: GEMV (M == 1, K <= 32768: the W4A8 GEMV's grid and weight stream,
  * the bf16 token staged in LDS), SKINNY (M <= 16; each workgroup stages its
- * K slice of the rows in LDS, K split until it fits) and PREFILL (128-token
- * tiles).  AUTO takes the GEMV at M == 1 when it fits, else SKINNY when it
- * splits K at most 4 ways, else PREFILL (faster than a deeper split).
+ * K slice of the rows in LDS when it fits, else loads the A operands straight
+ * from the rows, which needs 2*M*K < 2^31) and PREFILL (128-token tiles).
+ * AUTO takes the GEMV at M == 1 when it fits, else SKINNY at M <= 16, else
+ * PREFILL.
  * w4a16_select_path names the path AUTO takes; w4a16_linear_path
  * forces one (AUTO allowed), for tests, and returns
  * W4A8_ERR_UNSUPPORTED_SHAPE when the forced path has no plan for the shape.

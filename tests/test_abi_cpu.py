@@ -266,8 +266,8 @@ def test_w4a16_rejections(lib):
     assert need > 0
     assert f(FAKE, FAKE2, pb2, 1, 512, 18944, 128, y, None, 0, None) == -4    # split K: workspace
     assert lib.w4a16_select_path(4, 3584, 18944) == 2
-    assert lib.w4a16_select_path(8, 3584, 18944) == 2                          # K split 4 ways
-    assert lib.w4a16_select_path(16, 3584, 18944) == 3                         # 16 ways: prefill tiles
+    assert lib.w4a16_select_path(8, 3584, 18944) == 2                          # direct operand loads
+    assert lib.w4a16_select_path(16, 3584, 18944) == 2
     assert lib.w4a16_select_path(17, 3584, 18944) == 3
     assert lib.w4a16_select_path(1, 18944, 3584) == 1                         # GEMV
     assert lib.w4a16_select_path(1, 3584, 18944) == 1

@@ -47,9 +47,10 @@ def _check(y, lin, rows):
     assert ok, f"rows {m0}:{m1}: max|y - y_ref| = {err:.3e} > {bound:.3e}"
 
 
-# M <= 16: every row bucket, K split for the LDS budget (and runs of no group
-# when the split exceeds the groups), ragged and small N; M > 16: prefill
-# tiles of 128 tokens with ragged M and N, split K, full size
+# M <= 16: every row bucket, rows staged in LDS where they fit and A operands
+# loaded straight from memory where they do not (m4/m16 down, m6, m13: the
+# last with a K split to fill the machine), ragged and small N; M > 16:
+# prefill tiles of 128 tokens with ragged M and N, split K, full size
 A16_SPECS = [
     synth.LinearSpec("a16_m1_up", 1, 3584, 18944, seed=110),
     synth.LinearSpec("a16_m1_k", 1, 3584, 512, seed=111),
@@ -63,6 +64,8 @@ A16_SPECS = [
     synth.LinearSpec("a16_m8", 8, 4096, 1024, seed=115),
     synth.LinearSpec("a16_m16_down", 16, 18944, 3584, seed=116),
     synth.LinearSpec("a16_m16_small_k", 16, 256, 2048, seed=117),
+    synth.LinearSpec("a16_m6_direct", 6, 24576, 4096, seed=128),
+    synth.LinearSpec("a16_m13_direct_ksplit", 13, 18944, 400, seed=129),
     synth.LinearSpec("a16_m17", 17, 512, 272, seed=118),
     synth.LinearSpec("a16_m300", 300, 1024, 528, seed=119),
     synth.LinearSpec("a16_m512_ksplit", 512, 3584, 512, seed=120),
