@@ -90,6 +90,17 @@ ChunkWindow chunk_window(int64_t m_begin, int64_t m_end, int64_t m0, int64_t mc)
   return ChunkWindow{b - m0, e - m0, b - m_begin};
 }
 
+// The prefill's tail split (none when the rows run as several chunks) and
+// the workspace bytes its slices take ([split][M][N - n0], 4 bytes each).
+PrefillTail prefill_tail_for(int64_t M, int64_t N, int64_t K) {
+  if (M > prefill_chunk_rows(K, 1)) return PrefillTail{0, 0, 0};
+  return prefill_tail(M, N, K);
+}
+size_t tail_workspace(const PrefillTail& t, int64_t M, int64_t N) {
+  if (t.split < 2) return 0;
+  return ((size_t)t.split * (size_t)M * (size_t)(N - t.n0) * 4 + 255) / 256 * 256;
+}
+
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
@@ -101,7 +112,7 @@ int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
 // slot for the scale the fused quantiser computes.
 size_t workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = ksplit_for(path, M, N, K);
-  if (ks <= 1) return 0;
+  if (ks <= 1) return path == W4A8_PATH_PREFILL ? tail_workspace(prefill_tail_for(M, N, K), M, N) : 0;
   size_t b = (size_t)ks * (size_t)M * (size_t)N * sizeof(float);
   b = (b + 255) / 256 * 256;
   return path == W4A8_PATH_GEMV ? b + 256 : b;
@@ -231,6 +242,10 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
     // K reuses the front of the workspace, chunk after chunk on the stream
     const int64_t rows = prefill_chunk_rows(K, 1);
     const int64_t G = K / kGroup;
+    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K);
+    a.tail_split = tail.split;
+    a.tail_tiles = tail.tiles;
+    a.tail_n0 = tail.n0;
     e = hipSuccess;
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
       const int64_t mc = M - m0 < rows ? M - m0 : rows;
@@ -248,6 +263,8 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
       e = launch_prefill(c, st);
       if (e == hipSuccess && ks > 1 && c.y)
         e = launch_splitk_reduce(c.workspace, ks, c.sa, mc, N, c.y, st);
+      if (e == hipSuccess && tail.split > 1 && c.y)
+        e = launch_splitk_reduce(c.workspace, tail.split, c.sa, mc, N, c.y, st, tail.n0);
     }
     return device_status(e, "gemm launch");
   }
@@ -428,7 +445,7 @@ int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
 // for the scale the fused quantiser computes.
 size_t w8_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = w8_ksplit(path, M, N, K);
-  if (ks <= 1) return 0;
+  if (ks <= 1) return path == W4A8_PATH_PREFILL ? tail_workspace(prefill_tail_for(M, N, K), M, N) : 0;
   return round256((size_t)ks * (size_t)M * (size_t)N * 4) + (path == W4A8_PATH_GEMV ? 256 : 0);
 }
 
@@ -549,6 +566,10 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   if (path == W4A8_PATH_PREFILL) {
     // row chunks, as for W4A8; the totals of the debug window per chunk
     const int64_t rows = prefill_chunk_rows(K, 1);
+    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K);
+    a.tail_split = tail.split;
+    a.tail_tiles = tail.tiles;
+    a.tail_n0 = tail.n0;
     hipError_t e = hipSuccess;
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
       const int64_t mc = M - m0 < rows ? M - m0 : rows;
@@ -567,6 +588,10 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
       if (e == hipSuccess && ks > 1 && (c.y || c.partials))
         e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), ks, c.sa,
                                     a.w.scales, mc, N, c.y, c.partials, c.m_begin, c.m_end, st);
+      if (e == hipSuccess && tail.split > 1 && (c.y || c.partials))
+        e = launch_w8_splitk_reduce(reinterpret_cast<const int32_t*>(workspace), tail.split, c.sa,
+                                    a.w.scales, mc, N, c.y, c.partials, c.m_begin, c.m_end, st,
+                                    tail.n0);
     }
     return device_status(e, "w8a8 gemm launch");
   }

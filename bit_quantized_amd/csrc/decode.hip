@@ -532,14 +532,16 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
 // per-token scale comes from `sa` (a device array written before this kernel
 // runs: by the caller, or by the fused-quant GEMV).
 __global__ void __launch_bounds__(256)
+// The slices cover columns [n0, N) of y: ws is [ksplit][M][N - n0].
 splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __restrict__ sa,
-                     int64_t M, int64_t N, uint16_t* __restrict__ y) {
+                     int64_t M, int64_t N, uint16_t* __restrict__ y, int64_t n0) {
+  const int64_t W = N - n0;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= M * N) return;
-  const int64_t m = t / N;
+  if (t >= M * W) return;
+  const int64_t m = t / W;
   float v = ws[t];
-  for (int k = 1; k < ksplit; ++k) v += ws[k * M * N + t];
-  y[t] = f32_to_bf16_rne(sa ? sa[m] * v : v);
+  for (int k = 1; k < ksplit; ++k) v += ws[k * M * W + t];
+  y[m * N + n0 + t % W] = f32_to_bf16_rne(sa ? sa[m] * v : v);
 }
 
 // W8A8 split-K: the exact int32 totals summed over the slices (order-free),
@@ -548,14 +550,15 @@ splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __re
 __global__ void __launch_bounds__(256)
 w8_splitk_reduce_kernel(const int32_t* __restrict__ ws, int ksplit, const float* __restrict__ sa,
                         const float* __restrict__ sw, int64_t M, int64_t N, uint16_t* __restrict__ y,
-                        int32_t* __restrict__ totals, int64_t m_begin, int64_t m_end) {
+                        int32_t* __restrict__ totals, int64_t m_begin, int64_t m_end, int64_t n0) {
+  const int64_t W = N - n0;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= M * N) return;
-  const int64_t m = t / N, n = t % N;
+  if (t >= M * W) return;
+  const int64_t m = t / W, n = n0 + t % W;
   int p = ws[t];
-  for (int k = 1; k < ksplit; ++k) p += ws[k * M * N + t];
+  for (int k = 1; k < ksplit; ++k) p += ws[k * M * W + t];
   if (totals && m >= m_begin && m < m_end) totals[(m - m_begin) * N + n] = p;
-  if (y) y[t] = f32_to_bf16_rne(sa[m] * (sw[n] * (float)p));
+  if (y) y[m * N + n] = f32_to_bf16_rne(sa[m] * (sw[n] * (float)p));
 }
 
 // Split K only while the channel blocks alone leave compute units idle, and
@@ -719,18 +722,18 @@ hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
 
 hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,
                                    int64_t M, int64_t N, uint16_t* y, int32_t* totals,
-                                   int64_t m_begin, int64_t m_end, hipStream_t st) {
-  const int64_t total = M * N;
+                                   int64_t m_begin, int64_t m_end, hipStream_t st, int64_t n0) {
+  const int64_t total = M * (N - n0);
   hipLaunchKernelGGL(w8_splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     st, ws, ksplit, sa, sw, M, N, y, totals, m_begin, m_end);
+                     st, ws, ksplit, sa, sw, M, N, y, totals, m_begin, m_end, n0);
   return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
-                                int64_t N, uint16_t* y, hipStream_t st) {
-  const int64_t total = M * N;
+                                int64_t N, uint16_t* y, hipStream_t st, int64_t n0) {
+  const int64_t total = M * (N - n0);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     st, ws, ksplit, sa, M, N, y);
+                     st, ws, ksplit, sa, M, N, y, n0);
   return hipGetLastError();
 }
 

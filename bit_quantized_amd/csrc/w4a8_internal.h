@@ -156,6 +156,10 @@ struct GemmArgs {
   int gq, gr;             // skinny: G = gq * (ksplit * 16) + gr (set by the launcher)
   bool w8;                // W8A8 weights (codes [N/16][G][2][1024], scales [N]); partials
                           // are then the int32 totals [m_end-m_begin][N]
+  // prefill: the last tail_tiles tiles (channels >= tail_n0) each run as
+  // tail_split K slices into workspace [tail_split][M][N - tail_n0]
+  int tail_split = 0;
+  int64_t tail_tiles = 0, tail_n0 = 0;
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).
@@ -175,6 +179,15 @@ int skinny_ksplit(int64_t M, int64_t N, int64_t K);
 // itself (GemmArgs::x set); x_dtype as in GemmArgs.
 bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype);
 int prefill_ksplit(int64_t M, int64_t N, int64_t K);
+// Prefill grid beyond prefill_ksplit: when the tiles fill R whole rounds of
+// the compute units plus a partial one, the partial round's tiles (rounded up
+// to whole column tiles) run as `split` K slices each, so the last round is
+// 1/split as long.  split 0: no tail split.
+struct PrefillTail {
+  int split;
+  int64_t tiles, n0;
+};
+PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 // W4A16 (bf16 token in GemmArgs::x, M == 1) on the GEMV kernel; same grid rules.
 hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st);
@@ -192,10 +205,12 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
 // W4A16 prefill (bf16 activations in GemmArgs::x): K split and launch.
 int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K);
 hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st);
+// ws is [ksplit][M][N - n0]: the columns [n0, N) of y (n0 = 0: all).
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
-                                int64_t N, uint16_t* y, hipStream_t st);
+                                int64_t N, uint16_t* y, hipStream_t st, int64_t n0 = 0);
 hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,
                                    int64_t M, int64_t N, uint16_t* y, int32_t* totals,
-                                   int64_t m_begin, int64_t m_end, hipStream_t st);
+                                   int64_t m_begin, int64_t m_end, hipStream_t st,
+                                   int64_t n0 = 0);
 
 }  // namespace w4a8

@@ -317,6 +317,27 @@ def test_errors_leave_outputs_untouched(w4):
     assert torch.all(y.float() == 7.0)
 
 
+@pytest.mark.parametrize("M,K,N", [(512, 3584, 18944), (300, 1024, 18992)])
+def test_prefill_tail_split(w4, M, K, N):
+    """Tiles that fill one round and part of another: the partial round's
+    tiles (whole column tiles, the last channels) run as K slices whose float
+    sums a second kernel reduces.  Bit-exact partials over a row window for
+    every channel, y on rows of both row tiles, and the debug call's y equal
+    to the plain call's (N = 18992 makes the last column tile ragged)."""
+    say(f"prefill tail split M={M} K={K} N={N}")
+    assert w4.workspace_bytes(M, N, K) > 0               # the tail slices' sums
+    spec = synth.LinearSpec(f"tail_{M}_{K}_{N}", M, K, N, seed=M + N)
+    lin, W, qa_ref, sa_ref = _setup(w4, spec)
+    qa, sa = dev(qa_ref), dev(sa_ref)
+    y = w4.gemm(qa, sa, W)
+    for rows in [(0, 8), (M - 8, M)]:
+        _check_y(y, lin, qa_ref, sa_ref, rows)
+    P, y2 = w4.gemm_debug(qa, sa, W, path=w4.PATH_PREFILL, rows=(250, 262))
+    assert np.array_equal(P.cpu().numpy(),
+                          oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=250, m1=262))
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+
+
 @pytest.mark.parametrize("name,K,N", [("k", 3584, 512), ("o", 3584, 3584), ("down", 18944, 3584)])
 @pytest.mark.parametrize("M", [1, 512])
 def test_layer_linears(w4, name, K, N, M):

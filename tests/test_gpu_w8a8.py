@@ -94,6 +94,9 @@ W8_SPECS = [
     synth.LinearSpec("w8_m300", 300, 1024, 528, seed=89, act="f32"),
     synth.LinearSpec("w8_m512_ksplit", 512, 3584, 512, seed=90),
     synth.LinearSpec("w8_m2048_up", 2048, 3584, 18944, seed=91),
+    # one round of tiles plus a partial one: the partial round runs as K slices
+    synth.LinearSpec("w8_m512_tail", 512, 3584, 18944, seed=99),
+    synth.LinearSpec("w8_m300_tail_ragged", 300, 1024, 18992, seed=100),
 ]
 
 
