@@ -341,6 +341,31 @@ def bench_hadamard(torch, w4, args):
         res["timing"].append({"M": M, "K": K, "quant_us": round(plain * 1e3, 3),
                               "hadamard_quant_us": round(rot * 1e3, 3),
                               "bytes": M * K * 3 + 4 * M})
+    # the layer with the rotation against the plain layer: one launch each
+    # where the GEMV or the M <= 16 kernel quantises the rows itself
+    import oracle
+    res["linear"] = []
+    for spec in (synth.DECODE_UP, synth.SKINNY_DOWN_4):
+        lin, x, Ws = setup_linear(torch, w4, spec, 16)
+        M, K, N = spec.M, spec.K, spec.N
+        y = w4.linear_hadamard(x, Ws[0])
+        qa_ref, sa_ref = oracle.hadamard_quant_act(lin["x"])
+        ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(0, M))
+        ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy(), ref)
+        if not ok:
+            raise SystemExit(f"parity check failed (hadamard {spec.name}): {err:.3e} > {bound:.3e}")
+        R = len(Ws)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(w4.linear_workspace_bytes(M, N, K),
+                             int(w4.load().w4a8_linear_hadamard_workspace_bytes(M, N, K, 128)), 16),
+                         dtype=torch.uint8, device="cuda")
+        plain = graph_launches_ms(torch, lambda i: w4.linear(x, Ws[i % R], out, ws), 64)
+        rot = graph_launches_ms(torch, lambda i: w4.linear_hadamard(x, Ws[i % R], out, ws), 64)
+        res["linear"].append({"workload": f"{spec.name} M={M} K={K} N={N}",
+                              "linear_us": round(plain * 1e3, 3),
+                              "linear_hadamard_us": round(rot * 1e3, 3),
+                              "parity": {"rows": [0, M], "max_err": err, "bound": bound}})
+        del Ws
     # accuracy: 7B-shaped down projection input with 0.5 % of channels x 20
     M, K, N = 16, 3584, 2048
     lin = synth.make_linear(synth.LinearSpec("had_acc", M, K, N, seed=6))

@@ -143,7 +143,7 @@ struct ActIn {
 int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
              int64_t K, int32_t group, int32_t path, int64_t m_begin, int64_t m_end,
              int32_t* partials, uint16_t* y, void* workspace, size_t workspace_bytes,
-             void* stream, bool debug, bool validate_only = false) {
+             void* stream, bool debug, bool validate_only = false, bool hadamard = false) {
   int rc = check_weight_shape(N, K, group);
   if (rc) return rc;
   if (M <= 0 || M > ((int64_t)1 << 24))
@@ -220,6 +220,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   a.ksplit = ks;
   a.cb = a.ks = 0;
   a.w8 = false;
+  a.hadamard = fused && hadamard;
   const float* sa_for_reduce = act.sa;
   if (path == W4A8_PATH_GEMV) {
     const GemvShape gs = gemv_shape(N, K);
@@ -807,6 +808,14 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed,
     return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
   if (overlaps(y, (size_t)M * N * 2, x, xbytes))
     return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  // At M == 1 one launch: the GEMV's quantiser rotates the token first.  (In
+  // the M <= 16 kernel every workgroup would rotate all rows again; measured
+  // slower than the two launches at every shape tried, e.g. M = 4, K = 18944
+  // -> N = 3584: 26.5 against 15.8 us.)
+  if (pick_path(M, K) == W4A8_PATH_GEMV)
+    return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
+                    W4A8_PATH_GEMV, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false,
+                    false, /*hadamard=*/true);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qa = reinterpret_cast<int8_t*>(ws);
   float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));

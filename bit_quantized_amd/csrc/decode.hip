@@ -591,8 +591,13 @@ constexpr int64_t kFusedLdsBytes = 128 * 1024;
 
 int pow2_rows(int64_t M) { return M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
+// Every workgroup quantises all M rows again, so the fused form also needs
+// the channel blocks to fit one round of workgroups: past that, the separate
+// quantiser and the GEMM on its codes are faster (M = 4, K = 3584 -> N =
+// 18944, 1184 blocks: 22.3 us fused against about 20 us; M = 16 there: 32.4
+// against about 22 us).
 int fused_chunks(int64_t M, int64_t N, int64_t K, int x_dtype) {
-  if (M < 1 || M > 16 || pick_ksplit(N, K) != 1) return 0;
+  if (M < 1 || M > 16 || pick_ksplit(N, K) != 1 || N / kBlockCols > device_cus()) return 0;
   if (M * (K + 16) + 512 > kFusedLdsBytes) return 0;
   const int64_t per_thread = (K / 8 + kThreads / pow2_rows(M) - 1) / (kThreads / pow2_rows(M));
   const int64_t limit = x_dtype == 0 ? 10 : 4;
@@ -652,9 +657,6 @@ bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype) {
 
 int skinny_ksplit(int64_t, int64_t N, int64_t K) { return pick_ksplit(N, K); }
 
-// W4A16 on the M <= 16 kernel: K is split at least as much as filling the
-// machine asks, and further until one workgroup's slice of the rows fits the
-// LDS budget and takes at most 8 chunks of eight per thread.
 // The K split is the one that fills the machine (as for W4A8).  The rows are
 // staged in LDS when the workgroup's slice of them fits (read once, with
 // coalesced loads); otherwise each wavefront loads its A operands per unit

@@ -294,10 +294,22 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
       }
       if constexpr (XT != X_QUANTISED) {
 #pragma unroll
-        for (int i = 0; i < kQChunks; ++i)
-          if ((b * kQChunks + i) * kQThreads + qt < nch)
+        for (int i = 0; i < kQChunks; ++i) {
+          // (liveness is the same for the 16 lanes of a row: nch % 16 == 0)
+          const bool live = (b * kQChunks + i) * kQThreads + qt < nch;
+          if (a.hadamard) {  // the rotated values set the scale
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
+            hadamard_chunk(v);
+            if (live)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+          } else if (live) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(chunk_value<XT>(xr[i], e)));
+          }
+        }
       }
     }
     if constexpr (XT == X_QUANTISED) {
@@ -327,16 +339,22 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
 #pragma unroll
       for (int i = 0; i < kQChunks; ++i) {
         const int ch = (b * kQChunks + i) * kQThreads + qt;
+        float v[8];
+        if constexpr (XT != X_QUANTISED) {
+          // (rotated, when asked, outside the branch: the rotation exchanges
+          // values across the 16 lanes of a row)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
+          if (a.hadamard) hadamard_chunk(v);
+        }
         if (ch < nch) {
           uint2 pk;
           if constexpr (XT == X_QUANTISED) {
             pk = make_uint2(xr[i][0].x, xr[i][0].y);
           } else {
-            // the rule of w4a8_quant_act, bit for bit (quant8_codes); an
-            // all-zero token has scale 0 and all-zero codes
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
+            // the rule of w4a8_quant_act (or w4a8_quant_act_hadamard), bit
+            // for bit (quant8_codes); an all-zero token has scale 0 and
+            // all-zero codes
             pk = scale != 0.0f ? quant8_codes(v, scale, inv) : make_uint2(0u, 0u);
           }
           *reinterpret_cast<uint2*>(qs + 8 * ch) = pk;

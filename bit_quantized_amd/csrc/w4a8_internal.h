@@ -112,6 +112,61 @@ __device__ __forceinline__ uint2 quant8_codes(const float* v, float s, float inv
   return make_uint2(w[0], w[1]);
 }
 
+// v of lane (lane ^ d) for d = 1, 2, 4, 8, within each 16-lane row, by DPP
+// moves (no LDS traffic).  Only symmetric lane maps are used, so the result
+// does not depend on the direction conventions of shifts: quad permutations
+// [1,0,3,2] and [2,3,0,1] for d = 1, 2; for d = 4 a mirror of each 8-lane
+// half (p -> 7 - p) and then a reversal of each quad: position p of a half
+// reads mirror position 7 - q(p), q(p) = (p & 4) | (3 - (p & 3)), which is
+// p ^ 4; for d = 8 a rotation of the 16-lane row by half its length.
+__device__ __forceinline__ float lane_xor_in_row(float v, int d) {
+  constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kQuadReverse = 0x1B;
+  constexpr int kRowHalfMirror = 0x141, kRowRotate8 = 0x128;
+  int x = __float_as_int(v);
+  if (d == 1) {
+    x = __builtin_amdgcn_mov_dpp(x, kQuadSwap1, 0xF, 0xF, true);
+  } else if (d == 2) {
+    x = __builtin_amdgcn_mov_dpp(x, kQuadSwap2, 0xF, 0xF, true);
+  } else if (d == 4) {
+    x = __builtin_amdgcn_mov_dpp(x, kRowHalfMirror, 0xF, 0xF, true);
+    x = __builtin_amdgcn_mov_dpp(x, kQuadReverse, 0xF, 0xF, true);
+  } else {
+    x = __builtin_amdgcn_mov_dpp(x, kRowRotate8, 0xF, 0xF, true);
+  }
+  return __int_as_float(x);
+}
+
+// Online Hadamard rotation of one chunk of eight, in place: this thread's
+// chunk is chunk (threadIdx.x & 15) of a group of 128 input channels whose
+// other 15 chunks sit in the neighbouring threads of the same 16-lane row.
+// The group is multiplied by the unnormalised 128 x 128 Walsh-Hadamard
+// matrix (Sylvester order) by radix-2 butterflies of increasing stride
+// h = 1, ..., 64, each pair (i, i + h) becoming (a + b, a - b): strides below
+// 8 inside the chunk, the rest across lanes.  Every element sees the same
+// float32 operations in the same order as the straightforward in-place
+// transform, so the rotated values are exact reproductions of it.
+__device__ __forceinline__ void hadamard_chunk(float* v) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  const int pos = threadIdx.x & 15;
+#pragma unroll
+  for (int d = 1; d < 16; d *= 2) {  // stride 8 d: the partner chunk is lane ^ d
+    const bool upper = (pos & d) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float u = lane_xor_in_row(v[i], d);
+      v[i] = upper ? u - v[i] : v[i] + u;
+    }
+  }
+}
+
 // Zero point of column c in a zeros block.
 __device__ __forceinline__ uint32_t zero_of(const uint8_t* zblk, int c) {
   uint32_t b = zblk[c >> 1];
@@ -160,6 +215,9 @@ struct GemmArgs {
   // tail_split K slices into workspace [tail_split][M][N - tail_n0]
   int tail_split = 0;
   int64_t tail_tiles = 0, tail_n0 = 0;
+  // the GEMV's in-kernel quantisation: rotate each group of 128 by the
+  // Walsh-Hadamard matrix first (hadamard_chunk), as w4a8_quant_act_hadamard
+  bool hadamard = false;
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).

@@ -200,8 +200,10 @@ int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
  * GEMV quantises the token in its prologue, so a decode step has no separate
  * quantisation kernel.  For 2 <= M <= 16 it is also one launch when the rows
  * fit: M*(K+16) <= 128 KiB, at most 10240*8/MP bf16 (4096*8/MP float) values
- * per row with MP = M rounded up to a power of two >= 2, and N large enough
- * that K is not split; the SKINNY kernel then quantises the rows into LDS.
+ * per row with MP = M rounded up to a power of two >= 2, N large enough that
+ * K is not split and small enough that its 16-channel blocks fit one round
+ * of workgroups (N/16 <= the compute units; every workgroup quantises all
+ * rows again); the SKINNY kernel then quantises the rows into LDS.
  * Otherwise the codes are written to the workspace and the GEMM of the
  * selected path follows (two launches).  The result is bitwise identical to
  * w4a8_quant_act followed by w4a8_gemm.
@@ -235,10 +237,13 @@ int w4a8_quant_act_hadamard(const void* x, int32_t x_dtype, int64_t M, int64_t K
                             float* sa, void* stream);
 
 /*
- * w4a8_linear_hadamard — w4a8_quant_act_hadamard into the workspace, then
- * w4a8_gemm with weights packed from the rotated W' (two launches on every
- * path).  Arguments as w4a8_linear; workspace of
- * w4a8_linear_hadamard_workspace_bytes(M, N, K, group) bytes.
+ * w4a8_linear_hadamard — w4a8_quant_act_hadamard, then w4a8_gemm with
+ * weights packed from the rotated W'.  At M == 1 (the GEMV path) one launch:
+ * the GEMV's quantiser rotates the token first, with the same codes and
+ * scale; otherwise two launches through the workspace.  The result is bitwise that
+ * of the two calls.  Arguments as w4a8_linear; workspace of
+ * w4a8_linear_hadamard_workspace_bytes(M, N, K, group) bytes (required on
+ * every path).
  */
 size_t w4a8_linear_hadamard_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes,

@@ -86,8 +86,16 @@ def test_hadamard_special_rows(w4):
     assert np.all(np.abs(q[1, 128:256].astype(int)) == 127) and not q[1, :128].any()
 
 
+# M = 1 and the M <= 16 kernels quantise (and rotate) in the kernel: bf16 and
+# f32, one and two token batches (K = 32768), every row bucket; M = 16 at
+# K = 18944 and M = 300 take the two-launch path.
 LIN_CASES = [synth.LinearSpec("hadl_m1", 1, 3584, 18944, seed=97),
+             synth.LinearSpec("hadl_m1_k32768_f32", 1, 32768, 256, seed=101, act="f32"),
+             synth.LinearSpec("hadl_m2_f32", 2, 4096, 1024, seed=102, act="f32"),
              synth.LinearSpec("hadl_m4", 4, 18944, 3584, seed=98),
+             synth.LinearSpec("hadl_m9", 9, 2048, 512, seed=103),
+             synth.LinearSpec("hadl_m16_k3584", 16, 3584, 512, seed=104),
+             synth.LinearSpec("hadl_m16_two_launch", 16, 18944, 256, seed=105),
              synth.LinearSpec("hadl_m300", 300, 1024, 528, seed=99, act="f32")]
 
 
