@@ -160,7 +160,7 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
 // W8: the W8A8 weights (two 1 KiB halves per unit, already in operand order;
 // one scale per channel in `scales`, no zero points): raw int8 dots, int32
 // totals over the run, the scales applied once in the epilogue.
-template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false>
+template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false, bool HAD = false>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint8_t* __restrict__ zeros, const void* __restrict__ xin, int K, int cb_q,
@@ -297,7 +297,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
         for (int i = 0; i < kQChunks; ++i) {
           // (liveness is the same for the 16 lanes of a row: nch % 16 == 0)
           const bool live = (b * kQChunks + i) * kQThreads + qt < nch;
-          if (a.hadamard) {  // the rotated values set the scale
+          if constexpr (HAD) {  // the rotated values set the scale
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
@@ -345,7 +345,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           // values across the 16 lanes of a row)
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = chunk_value<XT>(xr[i], e);
-          if (a.hadamard) hadamard_chunk(v);
+          if constexpr (HAD) hadamard_chunk(v);
         }
         if (ch < nch) {
           uint2 pk;
@@ -538,6 +538,17 @@ hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
   dim3 grid((unsigned)a.cb, (unsigned)a.ksplit);
   const size_t lds = (XT == X_A16 ? 2 : 1) * (size_t)a.K + 16 * (size_t)G;
   const void* xin = XT == X_QUANTISED ? static_cast<const void*>(a.qa) : a.x;
+  if constexpr ((XT == X_BF16 || XT == X_F32) && !W8) {
+    // the rotated token (w4a8_linear_hadamard): its own instantiation, so the
+    // plain kernel carries none of the rotation's code
+    if (a.hadamard) {
+      if (a.partials) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC, false, true>), grid, dim3(kThreads), lds,
+                         st, a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.hadamard) return hipErrorInvalidValue;
   if (a.partials)
     hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st, a.w.codes,
                        a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);

@@ -215,8 +215,9 @@ struct GemmArgs {
   // tail_split K slices into workspace [tail_split][M][N - tail_n0]
   int tail_split = 0;
   int64_t tail_tiles = 0, tail_n0 = 0;
-  // the GEMV's in-kernel quantisation: rotate each group of 128 by the
-  // Walsh-Hadamard matrix first (hadamard_chunk), as w4a8_quant_act_hadamard
+  // the GEMV's in-kernel quantisation (bf16 / f32 token, not debug): rotate
+  // each group of 128 by the Walsh-Hadamard matrix first (hadamard_chunk), as
+  // w4a8_quant_act_hadamard
   bool hadamard = false;
 };
 
