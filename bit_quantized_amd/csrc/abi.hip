@@ -298,9 +298,16 @@ int a16_ksplit(int path, int64_t M, int64_t N, int64_t K) {
   return path == W4A8_PATH_SKINNY ? skinny_a16_plan(M, N, K).ksplit : prefill_a16_ksplit(M, N, K);
 }
 
+// The W4A16 prefill's tail split (none when the rows run as several chunks).
+PrefillTail a16_tail_for(int64_t M, int64_t N, int64_t K) {
+  if (M > prefill_chunk_rows(K, 2)) return PrefillTail{0, 0, 0};
+  return prefill_tail(M, N, K, /*a16=*/true);
+}
+
 size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = a16_ksplit(path, M, N, K);
-  return ks <= 1 ? 0 : round256((size_t)ks * (size_t)M * (size_t)N * 4);
+  if (ks <= 1) return path == W4A8_PATH_PREFILL ? tail_workspace(a16_tail_for(M, N, K), M, N) : 0;
+  return round256((size_t)ks * (size_t)M * (size_t)N * 4);
 }
 
 // M <= 16 takes the M <= 16 kernel whenever it has a plan (it beat the
@@ -394,6 +401,10 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
   if (path == W4A8_PATH_PREFILL) {
     // row chunks, as for W4A8 (bf16 rows: two bytes per value)
     const int64_t rows = prefill_chunk_rows(K, 2);
+    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : a16_tail_for(M, N, K);
+    a.tail_split = tail.split;
+    a.tail_tiles = tail.tiles;
+    a.tail_n0 = tail.n0;
     hipError_t e = hipSuccess;
     for (int64_t m0 = 0; m0 < M && e == hipSuccess; m0 += rows) {
       const int64_t mc = M - m0 < rows ? M - m0 : rows;
@@ -403,6 +414,8 @@ int run_a16(const uint16_t* x, const void* packed, size_t packed_bytes_, int64_t
       c.y = y + m0 * N;
       e = launch_prefill_a16(c, st);
       if (e == hipSuccess && ks > 1) e = launch_splitk_reduce(c.workspace, ks, nullptr, mc, N, c.y, st);
+      if (e == hipSuccess && tail.split > 1)
+        e = launch_splitk_reduce(c.workspace, tail.split, nullptr, mc, N, c.y, st, tail.n0);
     }
     return device_status(e, "w4a16 launch");
   }

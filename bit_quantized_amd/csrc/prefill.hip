@@ -537,10 +537,25 @@ prefill_a16_kernel(GemmArgs a) {
   const int64_t NB = a.N / kBlockCols;
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles_n = (NB + NCB - 1) / NCB;
-  const int64_t t = xcd_tile(blockIdx.x, tiles_m * tiles_n);
+  // tiles and tail slices as in the W4A8 kernel
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t main_tiles = a.tail_split > 1 ? tiles - a.tail_tiles : tiles;
+  int64_t t;
+  int slice = blockIdx.y, nslices = gridDim.y;
+  int64_t wn0 = 0;
+  if ((int64_t)blockIdx.x < main_tiles) {
+    t = xcd_tile(blockIdx.x, main_tiles);
+  } else {
+    const int64_t r = blockIdx.x - main_tiles;
+    t = main_tiles + r % a.tail_tiles;
+    slice = (int)(r / a.tail_tiles);
+    nslices = a.tail_split;
+    wn0 = a.tail_n0;
+  }
+  const int64_t ldw = a.N - wn0;
   const int64_t tm = t % tiles_m, tn = t / tiles_m;
   const int64_t m0 = tm * BM, cb0 = tn * NCB;
-  const int64_t gb = G * blockIdx.y / gridDim.y, ge = G * (blockIdx.y + 1) / gridDim.y;
+  const int64_t gb = G * slice / nslices, ge = G * (slice + 1) / nslices;
 
   float accf[2][4][4];
 #pragma unroll
@@ -579,8 +594,8 @@ prefill_a16_kernel(GemmArgs a) {
         const int64_t nb = cb0 + wn * 4 + u;
         if (nb >= NB) continue;
         const int64_t n = nb * 16 + r16;
-        if (gridDim.y > 1)
-          a.workspace[((int64_t)blockIdx.y * a.M + m) * a.N + n] = accf[i][u][r];
+        if (nslices > 1)
+          a.workspace[((int64_t)slice * a.M + m) * ldw + n - wn0] = accf[i][u][r];
         else
           a.y[m * a.N + n] = f32_to_bf16_rne(accf[i][u][r]);
       }
@@ -604,8 +619,9 @@ int prefill_ksplit(int64_t M, int64_t N, int64_t K) {
 // Measured at M = 512, K = 3584 -> N = 18944 (296 tiles: one round and 40
 // tiles): with the last 40 tiles as 6 K slices each, quantisation + GEMM
 // takes 68.6 us instead of 87 us.
-PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N / kBlockCols + NCB - 1) / NCB;
+PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, bool a16) {
+  const int64_t bm = a16 ? a16::BM : BM;
+  const int64_t tiles_m = (M + bm - 1) / bm, tiles_n = (N / kBlockCols + NCB - 1) / NCB;
   const int64_t tiles = tiles_m * tiles_n, cus = device_cus(), G = K / kGroup;
   const PrefillTail none{0, 0, 0};
   if (tiles <= cus || tiles % cus == 0) return none;
@@ -650,7 +666,10 @@ int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st) {
   const int64_t NB = a.N / kBlockCols;
   const int64_t tiles = ((a.M + a16::BM - 1) / a16::BM) * ((NB + NCB - 1) / NCB);
-  hipLaunchKernelGGL(a16::prefill_a16_kernel, dim3((unsigned)tiles, (unsigned)a.ksplit),
+  if (a.tail_split > 1 && (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
+    return hipErrorInvalidValue;
+  const int64_t wgs = a.tail_split > 1 ? tiles - a.tail_tiles + a.tail_tiles * a.tail_split : tiles;
+  hipLaunchKernelGGL(a16::prefill_a16_kernel, dim3((unsigned)wgs, (unsigned)a.ksplit),
                      dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }

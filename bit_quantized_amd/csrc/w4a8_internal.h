@@ -246,7 +246,7 @@ struct PrefillTail {
   int split;
   int64_t tiles, n0;
 };
-PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K);
+PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, bool a16 = false);  // a16: W4A16 tiles
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 // W4A16 (bf16 token in GemmArgs::x, M == 1) on the GEMV kernel; same grid rules.
 hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st);
