@@ -70,6 +70,9 @@ A16_SPECS = [
     synth.LinearSpec("a16_m300", 300, 1024, 528, seed=119),
     synth.LinearSpec("a16_m512_ksplit", 512, 3584, 512, seed=120),
     synth.LinearSpec("a16_m2048_up", 2048, 3584, 18944, seed=121),
+    # 2384 tiles: 9 rounds and 80 tiles, the last column tile ragged; the
+    # partial round runs as K slices
+    synth.LinearSpec("a16_m2048_tail_ragged", 2048, 3584, 18960, seed=130),
 ]
 
 
