@@ -272,3 +272,23 @@ def test_w4a16_rejections(lib):
     assert lib.w4a16_select_path(1, 18944, 3584) == 1                         # GEMV
     assert lib.w4a16_select_path(1, 3584, 18944) == 1
     assert lib.w4a16_select_path(1, 256, 65536) in (2, 3)                     # K past the GEMV's LDS
+
+
+def test_prefill_workspace_plans(lib):
+    """Host planning of the prefill grid, visible through the workspace sizes
+    (no GPU here: the planner assumes 256 compute units, as on MI355X).
+    - A partial last round of tiles runs as K slices whose float (int32 for
+      W8A8) sums cover only the tail's channels: M = 512, K = 3584 -> N =
+      18944 has 296 tiles (one round and 40), 6 slices of 512 x 2560.
+    - W4A16 tiles hold 128 tokens: M = 2048 there has 2368 tiles (9 rounds
+      and 64), 4 slices of 2048 x 512.
+    - Whole rounds, or a partial round too large to split (M = 2048 W4A8:
+      160 tiles), need no workspace; nor do rows that run as several chunks
+      (M * K >= 2^31)."""
+    slices = 6 * 512 * 2560 * 4
+    assert lib.w4a8_gemm_workspace_bytes(512, 18944, 3584, 128) == slices
+    assert lib.w8a8_gemm_workspace_bytes(512, 18944, 3584) == slices
+    assert lib.w4a16_linear_workspace_bytes(2048, 18944, 3584, 128) == 4 * 2048 * 512 * 4
+    assert lib.w4a8_gemm_workspace_bytes(2048, 18944, 3584, 128) == 0
+    assert lib.w4a8_gemm_workspace_bytes(1024, 32768, 3584, 128) == 0      # 4 x 256 tiles
+    assert lib.w4a8_gemm_workspace_bytes(1 << 24, 16, 128, 128) == 0       # row chunks
