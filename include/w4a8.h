@@ -159,7 +159,9 @@ int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K,
                    int8_t* qa, float* sa, void* stream);
 
 /* Workspace bytes any path of w4a8_gemm / w4a8_gemm_debug may need for these
- * shapes (split-K partial sums); 0 if none. */
+ * shapes (split-K partial sums: K split over all tiles when they leave
+ * compute units idle, or over the tiles of a partial last round); 0 if none.
+ * The plan depends on the device's compute-unit count (256 on MI355X). */
 size_t w4a8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group);
 
 /* The path W4A8_PATH_AUTO takes for these shapes. */
