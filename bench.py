@@ -47,13 +47,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--copies", type=int, default=16, help="packed weight copies rotated per step")
     p.add_argument("--prefill-steps", type=int, default=32)
+    p.add_argument("--replays", type=int, default=9,
+                   help="extra graph replays after the timed one, for the p10/p50/p90 spread")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline sample budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the skinny and layer legs")
     p.add_argument("--only", choices=["all", "decode", "prefill", "skinny", "layer", "w8a8", "hadamard",
-                                      "w4a16", "copy"],
+                                      "w4a16", "copy", "peaks"],
                    default="all", help="run one part only (for hardware-counter passes)")
     return p.parse_args()
 
@@ -95,9 +97,11 @@ def graph_launches_ms(torch, launch, n):
     return graph_steps_ms(torch, launch, min(n, 8), n) / n
 
 
-def graph_steps_ms(torch, step, warmup, steps):
+def graph_steps_ms(torch, step, warmup, steps, spread=None):
     """Capture `steps` calls of step(i) in one HIP graph, replay it, and time
-    the replay between a synchronize and events on the replay stream."""
+    the replay between a synchronize and events on the replay stream.  With
+    spread=R the graph is replayed R more times after the timed replay, and
+    those replay times are kept for replay_spread(step, steps)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):                 # eager warmup outside capture
@@ -120,7 +124,30 @@ def graph_steps_ms(torch, step, warmup, steps):
     gt.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1)
+    first = e0.elapsed_time(e1)
+    if spread:
+        times = []
+        for _ in range(spread):
+            e0.record()
+            gt.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        _SPREAD[id(step)] = times
+    return first
+
+
+_SPREAD = {}
+
+
+def replay_spread(step, steps):
+    """p10/p50/p90 (microseconds per step) of the extra replays recorded by
+    graph_steps_ms(..., spread=R) for this step function."""
+    t = np.array(_SPREAD.pop(id(step)), dtype=np.float64) * 1e3 / steps
+    return {"replays": int(t.size), "steps_per_replay": steps,
+            "p10_us": round(float(np.percentile(t, 10)), 3),
+            "p50_us": round(float(np.percentile(t, 50)), 3),
+            "p90_us": round(float(np.percentile(t, 90)), 3)}
 
 
 def to_dev(torch, a):
@@ -144,24 +171,43 @@ def setup_linear(torch, w4, spec, copies):
     return lin, x, Ws
 
 
-def parity_check(w4, lin, x, W, rows=None, cols=None):
-    """The benchmarked path against the oracle before timing (on a window of
-    rows and columns for the large shapes)."""
+def parity_check(w4, lin, x, W, rows=None, cols=None, windows=None):
+    """The benchmarked path against the oracle before timing (on windows of
+    rows and columns for the large shapes: `windows` is a list of
+    ((m0, m1), (c0, c1)); by default one window of `rows` x `cols`)."""
     import oracle
     y = w4.linear(x, W).float().cpu().numpy()
     qa_ref, sa_ref = oracle.quant_act(lin["x"])
-    m0, m1 = rows or (0, lin["spec"].M)
-    c0, c1 = cols or (0, lin["spec"].N)
-    ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1),
-                        cols=(c0, c1))
-    ok, err, bound = oracle.tolerance_ok(y[m0:m1, c0:c1], ref)
-    if not ok:
-        raise SystemExit(f"parity check failed ({lin['spec'].name}): max err {err:.3e} > "
-                         f"{bound:.3e}")
-    out = {"rows": [m0, m1], "max_err": err, "bound": bound}
-    if cols:
-        out["cols"] = [c0, c1]
+    M, N = lin["spec"].M, lin["spec"].N
+    if windows is None:
+        windows = [(rows or (0, M), cols or (0, N))]
+    worst, out = None, {"windows": []}
+    for (m0, m1), (c0, c1) in windows:
+        ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(m0, m1),
+                            cols=(c0, c1))
+        ok, err, bound = oracle.tolerance_ok(y[m0:m1, c0:c1], ref)
+        if not ok:
+            raise SystemExit(f"parity check failed ({lin['spec'].name}, rows {m0}:{m1}, cols "
+                             f"{c0}:{c1}): max err {err:.3e} > {bound:.3e}")
+        out["windows"].append({"rows": [m0, m1], "cols": [c0, c1], "max_err": err,
+                               "bound": bound})
+        if worst is None or err / bound > worst[0] / worst[1]:
+            worst = (err, bound)
+    out["max_err"], out["bound"] = worst
+    if len(windows) == 1:
+        w = out.pop("windows")[0]
+        out["rows"] = w["rows"]
+        if cols:
+            out["cols"] = w["cols"]
     return out
+
+
+def layer_windows(M, N):
+    """Parity windows for the layer legs: the first row and (M > 1) a middle
+    row from the second row tile, each over the first and the last 64
+    columns (the last column tiles are the ones a tail split slices)."""
+    rows = [(0, 1)] + ([(M // 2, M // 2 + 1)] if M > 1 else [])
+    return [(r, c) for r in rows for c in ((0, 64), (N - 64, N))]
 
 
 def bench_decode(torch, w4, args):
@@ -181,7 +227,8 @@ def bench_decode(torch, w4, args):
     def step(i):
         w4.linear(x, Ws[i % R], out=y, workspace=ws)
 
-    total_ms = graph_steps_ms(torch, step, args.warmup, args.steps)
+    total_ms = graph_steps_ms(torch, step, args.warmup, args.steps, spread=args.replays)
+    spread = replay_spread(step, args.steps)
     kern_ms = graph_launches_ms(torch, step, args.steps)
 
     # for reference: the same step as two launches (quantise, then GEMV)
@@ -200,7 +247,7 @@ def bench_decode(torch, w4, args):
     path = {1: "gemv", 2: "skinny", 3: "prefill"}[w4.select_path(M, N, K)]
     return {
         "spec": spec, "lin": lin, "value": value, "ms_per_step": ms_per_step,
-        "step_bytes": step_bytes, "parity": parity, "path": path,
+        "step_bytes": step_bytes, "parity": parity, "path": path, "spread": spread,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("w4a8_gemv_decode_up_M1_K3584_N18944_traffic.txt"),
@@ -232,9 +279,15 @@ def bench_prefill(torch, w4, args):
         w4.gemm(qa, sa, Ws[i % R], out=y)
 
     n = args.prefill_steps
-    total_ms = graph_steps_ms(torch, step, max(2, n // 4), n)
+    total_ms = graph_steps_ms(torch, step, max(2, n // 4), n, spread=args.replays)
+    spread = replay_spread(step, n)
     w4.quant_act(x, qa, sa)
-    kern_ms = graph_launches_ms(torch, lambda i: w4.gemm(qa, sa, Ws[i % R], out=y), n)
+
+    def gemm_only(i):
+        w4.gemm(qa, sa, Ws[i % R], out=y)
+
+    kern_ms = graph_steps_ms(torch, gemm_only, min(n, 8), n, spread=args.replays) / n
+    kspread = replay_spread(gemm_only, n)
     ops = 2.0 * M * N * K
     tops_kernel = ops / (kern_ms * 1e-3) / 1e12
     tops_step = ops / (total_ms / n * 1e-3) / 1e12
@@ -242,6 +295,7 @@ def bench_prefill(torch, w4, args):
         "spec": spec, "lin": lin, "parity": parity,
         "workload": f"prefill_up M={M} K={K} N={N} group=128 (quant + GEMM)",
         "value": round(tops_step, 1), "unit": "TOPS", "ms_per_step": total_ms / n,
+        "spread": spread, "gemm_spread": kspread,
         "roofline": {"bound": "mfma", "achieved": round(tops_kernel, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TOPS", "frac": round(tops_kernel / INT8_PEAK_TOPS, 4),
                      "traffic": measured_traffic("w4a8_prefill_up_M2048_K3584_N18944_traffic.txt"),
@@ -474,7 +528,7 @@ def bench_layer(torch, w4, args):
         for spec in specs:
             lin, x, Ws = setup_linear(torch, w4, spec, 2)
             K, N = spec.K, spec.N
-            parity = parity_check(w4, lin, x, Ws[0], rows=(0, 1), cols=(0, 64))
+            parity = parity_check(w4, lin, x, Ws[0], windows=layer_windows(M, N))
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             ws = torch.zeros(max(w4.linear_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
                              device="cuda")
@@ -519,18 +573,21 @@ def bench_layer(torch, w4, args):
             del parts
             x0 = sib[group_names[0]][1]
             Nf = Ws[0].packed.N
-            # parity: every sibling's first 64 columns of row 0 against the
-            # oracle, on the shared input
+            # parity: every sibling's first and last 64 columns of row 0 and
+            # a middle row against the oracle, on the shared input
             import oracle
             lin0 = sib[group_names[0]][0]
             qa_ref, sa_ref = oracle.quant_act(lin0["x"])
             for nm, yv in zip(group_names, w4.linear_siblings(x0, Ws[0])):
                 ln = sib[nm][0]
-                ref = oracle.linear(qa_ref, sa_ref, ln["q"], ln["z"], ln["s"], rows=(0, 1),
-                                    cols=(0, 64))
-                ok, err, bound = oracle.tolerance_ok(yv.float().cpu().numpy()[0:1, 0:64], ref)
-                if not ok:
-                    raise SystemExit(f"fused sibling parity failed ({nm}, M={M})")
+                yn = yv.float().cpu().numpy()
+                for (m0, m1), (c0, c1) in layer_windows(M, yn.shape[1]):
+                    ref = oracle.linear(qa_ref, sa_ref, ln["q"], ln["z"], ln["s"], rows=(m0, m1),
+                                        cols=(c0, c1))
+                    ok, err, bound = oracle.tolerance_ok(yn[m0:m1, c0:c1], ref)
+                    if not ok:
+                        raise SystemExit(f"fused sibling parity failed ({nm}, M={M}, rows "
+                                         f"{m0}:{m1}, cols {c0}:{c1})")
             yf = torch.empty((M, Nf), dtype=torch.bfloat16, device="cuda")
             wsf = torch.zeros(max(w4.linear_workspace_bytes(M, Nf, x0.shape[1]), 16),
                               dtype=torch.uint8, device="cuda")
@@ -619,6 +676,87 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_each_way": n, "launches": 8}))
 
 
+def bench_peaks(torch, w4):
+    """On-device peaks beside the datasheet ones: one read of a 1 GiB buffer
+    (four times the 256 MB Infinity Cache) by the streaming probe, and chains
+    of v_mfma_i32_16x16x64_i8 on every SIMD with the engine clock they ran
+    at (shader cycles over 100 MHz constant-clock ticks)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 1 << 30
+    buf = torch.empty(n // 4, dtype=torch.int32, device="cuda")
+    buf.copy_(torch.arange(n // 4, dtype=torch.int32, device="cuda") * 0x01000193)
+    res = {"stream_read": [], "mfma_i8": []}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_gbs = 0.0
+    for blocks in (4 * cus, 8 * cus, 16 * cus):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        w4.peak_stream_read(buf, blocks, sink)
+        times = []
+        for _ in range(7):
+            e0.record()
+            w4.peak_stream_read(buf, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        gbs = [n / (t * 1e-3) / 1e9 for t in times]
+        best_gbs = max(best_gbs, float(np.median(gbs)))
+        res["stream_read"].append({"blocks": blocks, "bytes": n,
+                                   "p10_GBps": round(float(np.percentile(gbs, 10)), 1),
+                                   "p50_GBps": round(float(np.median(gbs)), 1),
+                                   "p90_GBps": round(float(np.percentile(gbs, 90)), 1)})
+    del buf
+    best_tops, clk = 0.0, None
+    iters = 4096
+    for waves_per_simd in (1, 2):
+        blocks = cus * waves_per_simd
+        sink, clocks = w4.peak_mfma_i8(16, blocks)
+        tops, ghz = [], []
+        for _ in range(5):
+            e0.record()
+            w4.peak_mfma_i8(iters, blocks, sink, clocks)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            tops.append(iters * 8 * 32768.0 * blocks * 4 / (ms * 1e-3) / 1e12)
+            c = clocks.cpu().numpy().astype(np.float64)
+            ghz.append(float(np.median(c[:, 0] / (c[:, 1] / 100e6))) / 1e9)
+        med = float(np.median(tops))
+        if med > best_tops:
+            best_tops, clk = med, float(np.median(ghz))
+        res["mfma_i8"].append({"waves_per_simd": waves_per_simd, "blocks": blocks, "iters": iters,
+                               "p10_TOPS": round(float(np.percentile(tops, 10)), 1),
+                               "p50_TOPS": round(med, 1),
+                               "p90_TOPS": round(float(np.percentile(tops, 90)), 1),
+                               "sclk_GHz_p50": round(float(np.median(ghz)), 3)})
+    res["hbm_GBps"] = round(best_gbs, 1)
+    res["int8_TOPS"] = round(best_tops, 1)
+    res["sclk_GHz_under_mfma"] = round(clk, 3) if clk else None
+    res["note"] = ("on-device peaks measured in this run; the datasheet peaks are 8000 GB/s and "
+                   "5000 TOPS (int8 dense, 2.4 GHz)")
+    return res
+
+
+def source_digest():
+    """sha256 over the library sources and headers (names and bytes, sorted),
+    so a result can be tied to the code it ran."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "bit_quantized_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _read(path):
+    try:
+        return open(path).read().strip()
+    except OSError:
+        return None
+
+
 def gpu_info(torch):
     info = {"device": torch.cuda.get_device_name(0)}
     try:
@@ -632,6 +770,27 @@ def gpu_info(torch):
                                      capture_output=True, text=True).stdout.strip() or None
     except Exception:
         info["git"] = None
+    info["source_sha256"] = source_digest()
+    info["rocm"] = _read("/opt/rocm/.info/version")
+    info["torch"] = torch.__version__
+    info["hip"] = getattr(torch.version, "hip", None)
+    cpu = _read("/proc/cpuinfo") or ""
+    info["cpu_model"] = next((ln.split(":", 1)[1].strip() for ln in cpu.splitlines()
+                              if ln.startswith("model name")), None)
+    info["host_threads"] = len(os.sched_getaffinity(0))
+    import bit_quantized_amd as w4
+    lib = w4.load()
+    info["abi_version"] = lib.w4a8_abi_version()
+    info["layout_version"] = lib.w4a8_layout_version()
+    info["w8a8_layout_version"] = lib.w8a8_layout_version()
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        info["clocks"] = [ln.strip() for ln in r.stdout.splitlines()
+                          if "clk" in ln.lower() and "level" in ln.lower()][:8] or None
+    except Exception:
+        info["clocks"] = None
+    info["flags"] = {"env": {k: os.environ[k] for k in ("HIP_VISIBLE_DEVICES", "GPU_MAX_HW_QUEUES",
+                                                         "OMP_NUM_THREADS") if k in os.environ}}
     return info
 
 
@@ -652,7 +811,9 @@ def main():
         copy_calibration(torch)
         return
 
-    dec = pre = skinny = layer = w8 = had = a16 = None
+    dec = pre = skinny = layer = w8 = had = a16 = peaks = None
+    if args.only in ("all", "peaks"):
+        peaks = bench_peaks(torch, w4)
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
@@ -675,8 +836,17 @@ def main():
             cpu_pre = cpu_baseline_prefill(pre, max(2.0, args.cpu_seconds / 3))
 
     from bit_quantized_amd import synth
+    if peaks:
+        # the same kernels against what this device reached in this run
+        for leg, key in ((dec, "hbm_GBps"), (pre, "int8_TOPS")):
+            if leg and peaks.get(key):
+                rf = leg["roofline"]
+                rf["peak_onbox"] = peaks[key]
+                rf["frac_onbox"] = round(rf["achieved"] / peaks[key], 4)
     if dec is None:
         out = {"metric": METRIC}
+        if peaks:
+            out["peaks"] = peaks
         if pre:
             out["prefill"] = {k: v for k, v in pre.items() if k not in ("spec", "lin")}
         if skinny:
@@ -717,6 +887,10 @@ def main():
         "two_launch": dec["two_launch"],
         "parity": dec["parity"],
     }
+    if dec.get("spread"):
+        line["spread"] = dec["spread"]
+    if peaks:
+        line["peaks"] = peaks
     if pre:
         p = {k: v for k, v in pre.items() if k not in ("spec", "lin")}
         p["cpu_baseline"] = cpu_pre

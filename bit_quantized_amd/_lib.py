@@ -73,6 +73,9 @@ SIGNATURES = {
                                        _vp, _vp, _vp, _sz, _vp]),
     "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    # include/w4a8_peaks.h
+    "w4a8_peak_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "w4a8_peak_mfma_i8": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp]),
 }
 
 _lib = None
@@ -503,3 +506,28 @@ def w4a16_linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None,
     _check(lib.w4a16_linear_path(_p(x), _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, path,
                                  _p(out), _p(workspace), wsb, _stream(x.device)))
     return out
+
+
+# ------------------------------------------------------------ peak probes
+
+def peak_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor | None = None):
+    """One read of `buf` (16-byte multiple) by the streaming probe."""
+    _need_cuda(buf)
+    if sink is None:
+        sink = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    _check(load().w4a8_peak_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                        blocks, _stream(buf.device)))
+    return sink
+
+
+def peak_mfma_i8(iters: int, blocks: int, sink: torch.Tensor | None = None,
+                 clocks: torch.Tensor | None = None):
+    """Chains of int8 matrix-core instructions; returns (sink, clocks) where
+    clocks[b] = (shader cycles, 100 MHz ticks) of workgroup b."""
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    if clocks is None:
+        clocks = torch.zeros((blocks, 2), dtype=torch.int64, device="cuda")
+    _check(load().w4a8_peak_mfma_i8(iters, _p(sink), _p(clocks), blocks, _stream(sink.device)))
+    return sink, clocks
+

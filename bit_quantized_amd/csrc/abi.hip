@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "../../include/w4a8.h"
+#include "../../include/w4a8_peaks.h"
 #include "w4a8_internal.h"
 
 using namespace w4a8;
@@ -980,6 +981,33 @@ int w4a16_linear_path(const uint16_t* x, const void* packed, size_t packed_bytes
                       void* workspace, size_t workspace_bytes, void* stream) {
   return run_a16(x, packed, packed_bytes_, M, N, K, group, path, y, workspace, workspace_bytes,
                  stream);
+}
+
+// ------------------------------------------------------------ peak probes
+
+int w4a8_peak_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks,
+                          void* stream) {
+  if (!buf || !sink) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (bytes == 0 || bytes % 16) return fail(W4A8_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (blocks < 1 || blocks > 65536) return fail(W4A8_ERR_INVALID_ARG, "blocks=%d out of [1, 65536]", (int)blocks);
+  if (!aligned16(buf) || !aligned16(sink)) return fail(W4A8_ERR_MISALIGNED, "buffers must be 16-byte aligned");
+  if (overlaps(buf, bytes, sink, (size_t)blocks * 4)) return fail(W4A8_ERR_INVALID_ARG, "sink aliases the buffer");
+  (void)hipGetLastError();
+  return device_status(launch_peak_stream_read(buf, bytes, sink, blocks, static_cast<hipStream_t>(stream)),
+                       "stream probe launch");
+}
+
+int w4a8_peak_mfma_i8(int32_t iters, int32_t* sink, uint64_t* clocks, int32_t blocks, void* stream) {
+  if (!sink) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
+  if (iters < 1 || iters > (1 << 20)) return fail(W4A8_ERR_INVALID_ARG, "iters=%d out of [1, 2^20]", (int)iters);
+  if (blocks < 1 || blocks > 65536) return fail(W4A8_ERR_INVALID_ARG, "blocks=%d out of [1, 65536]", (int)blocks);
+  if (!aligned16(sink) || (clocks && !aligned16(clocks)))
+    return fail(W4A8_ERR_MISALIGNED, "buffers must be 16-byte aligned");
+  if (clocks && overlaps(sink, (size_t)blocks * 256 * 4, clocks, (size_t)blocks * 16))
+    return fail(W4A8_ERR_INVALID_ARG, "sink aliases clocks");
+  (void)hipGetLastError();
+  return device_status(launch_peak_mfma_i8(iters, sink, clocks, blocks, static_cast<hipStream_t>(stream)),
+                       "mfma probe launch");
 }
 
 }  // extern "C"

@@ -267,6 +267,11 @@ hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st);
 // ws is [ksplit][M][N - n0]: the columns [n0, N) of y (n0 = 0: all).
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st, int64_t n0 = 0);
+// on-device peak probes (include/w4a8_peaks.h)
+hipError_t launch_peak_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
+                                   hipStream_t st);
+hipError_t launch_peak_mfma_i8(int iters, int32_t* sink, uint64_t* clocks, int blocks,
+                               hipStream_t st);
 hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* sa, const float* sw,
                                    int64_t M, int64_t N, uint16_t* y, int32_t* totals,
                                    int64_t m_begin, int64_t m_end, hipStream_t st,

@@ -2,6 +2,7 @@
 header declares, and rejects bad arguments on the host (no GPU needed: a
 rejected call returns before anything is enqueued)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,13 +11,15 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "w4a8.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:w4a8|w8a8)_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b((?:w4a8|w8a8|w4a16)_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -292,3 +295,21 @@ def test_prefill_workspace_plans(lib):
     assert lib.w4a8_gemm_workspace_bytes(2048, 18944, 3584, 128) == 0
     assert lib.w4a8_gemm_workspace_bytes(1024, 32768, 3584, 128) == 0      # 4 x 256 tiles
     assert lib.w4a8_gemm_workspace_bytes(1 << 24, 16, 128, 128) == 0       # row chunks
+
+
+def test_peak_probe_rejections(lib):
+    f = lib.w4a8_peak_stream_read
+    assert f(None, 1 << 20, FAKE2, 64, None) == -1
+    assert f(FAKE, 0, FAKE2, 64, None) == -1
+    assert f(FAKE, 100, FAKE2, 64, None) == -1                           # not a 16-byte multiple
+    assert f(FAKE, 1 << 20, FAKE2, 0, None) == -1
+    assert f(FAKE, 1 << 20, FAKE2, 70000, None) == -1
+    assert f(MIS, 1 << 20, FAKE2, 64, None) == -3
+    assert f(FAKE, 1 << 20, ctypes.c_void_p((1 << 20) + 4096), 64, None) == -1  # sink in buf
+    g = lib.w4a8_peak_mfma_i8
+    assert g(0, FAKE, None, 256, None) == -1
+    assert g(1 << 21, FAKE, None, 256, None) == -1
+    assert g(16, None, None, 256, None) == -1
+    assert g(16, FAKE, None, 0, None) == -1
+    assert g(16, MIS, None, 256, None) == -3
+    assert g(16, FAKE, FAKE, 256, None) == -1                            # clocks alias sink
