@@ -143,6 +143,8 @@ _SPREAD = {}
 def replay_spread(step, steps):
     """p10/p50/p90 (microseconds per step) of the extra replays recorded by
     graph_steps_ms(..., spread=R) for this step function."""
+    if id(step) not in _SPREAD:
+        return None
     t = np.array(_SPREAD.pop(id(step)), dtype=np.float64) * 1e3 / steps
     return {"replays": int(t.size), "steps_per_replay": steps,
             "p10_us": round(float(np.percentile(t, 10)), 3),

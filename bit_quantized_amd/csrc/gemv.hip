@@ -16,8 +16,13 @@
 //     integer LDS atomics (exact, so order-free), and raise an LDS flag; they
 //     synchronise among themselves through LDS counters;
 //   - the other wavefronts put D code blocks of their runs in flight at once,
-//     wait for the flag (a bounded spin: the quantisers set it
-//     unconditionally), and stream.
+//     wait for the flag, and stream.
+// Both waits on the LDS counters are unbounded spins (with s_sleep): they end
+// only because each of the kQ quantiser (or, for W4A16, stager) wavefronts
+// increments each counter it owns exactly once, on a path with no branch
+// around the increment.  Any edit that lets one of those wavefronts skip an
+// increment would leave the others spinning for ever; the increments are
+// marked "kQ increments" below.
 // The workgroup's (16-channel block, group) units are dealt out as contiguous
 // runs of the codes plane (1 KiB per wavefront per unit, nontemporal loads:
 // every byte is read once), the quantisers taking a smaller share since they
@@ -274,6 +279,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     }
     scale = 1.0f;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
+    // kQ increments: every stager reaches this line exactly once; the
+    // streamers' unbounded wait for s_sync[2] == kQ depends on it
     if (lane == 0)
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
@@ -318,6 +325,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
       // row absmax: every quantiser publishes its wavefront max (non-negative
       // floats order as their bit patterns), then waits for the others
       amax = wave_max(amax);
+      // kQ increments: every quantiser reaches this line exactly once; the
+      // unbounded wait just below (all quantisers) depends on it
       if (lane == 0) {
         __hip_atomic_fetch_max(&s_sync[0], __float_as_uint(amax), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -366,6 +375,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     }
     if (a.sa_ws && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.sa_ws[0] = scale;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
+    // kQ increments: every quantiser reaches this line exactly once; the
+    // streamers' unbounded wait for s_sync[2] == kQ depends on it
     if (lane == 0)
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     // then the quantiser streams its own (shorter) run
@@ -374,6 +385,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
       load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   } else {
     // ---- streamer: metadata and D code blocks are in flight; the flag
+    // (an unbounded spin that ends once all kQ quantisers or stagers have
+    // made their one increment of s_sync[2])
     if constexpr (XT == X_QUANTISED) scale = a.sa[0];
     while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
            (unsigned)kQ)

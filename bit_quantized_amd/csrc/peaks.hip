@@ -11,17 +11,26 @@ constexpr int kPeakThreads = 256;
 // every load alive while (in practice) nothing is written.
 constexpr uint32_t kNever = 0x9E3779B9u;
 
-// Grid-stride read of n16 16-byte pieces, four loads in flight per thread.
+// Each workgroup reads one contiguous share of the n16 16-byte pieces,
+// eight 1 KiB wavefront loads in flight per wavefront (whole HBM pages per
+// workgroup rather than a grid-wide stride).
+constexpr int kStreamUnroll = 8;
 __global__ void __launch_bounds__(kPeakThreads)
 stream_read_kernel(const v4i* __restrict__ p, int64_t n16, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * kPeakThreads;
-  int64_t i = (int64_t)blockIdx.x * kPeakThreads + threadIdx.x;
+  const int64_t share = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * share;
+  const int64_t b1 = b0 + share < n16 ? b0 + share : n16;
+  constexpr int kStep = kPeakThreads * kStreamUnroll;
   v4i acc = {0, 0, 0, 0};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const v4i a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+  int64_t i = b0 + threadIdx.x;
+  for (; i + (kStreamUnroll - 1) * kPeakThreads < b1; i += kStep) {
+    v4i r[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) r[u] = __builtin_nontemporal_load(&p[i + u * kPeakThreads]);
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) acc ^= r[u];
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (; i < b1; i += kPeakThreads) acc ^= p[i];
   const uint32_t v = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
   if (v == kNever) sink[blockIdx.x] = v;
 }
