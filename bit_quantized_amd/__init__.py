@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     workspace_bytes, PackedW8, quant_act_hadamard, linear_hadamard, w4a16_linear,
     w4a16_select_path, w4a16_workspace_bytes, w8a8_gemm, w8a8_gemm_debug, w8a8_linear, w8a8_linear_workspace_bytes,
     w8a8_pack_weights, w8a8_select_path, w8a8_unpack_weights, w8a8_workspace_bytes,
-    peak_mfma_i8, peak_stream_read,
+    peak_mfma_i8, peak_stream_read, NOALLOC_SCRATCH_BYTES, linear_noalloc,
 )

@@ -73,6 +73,7 @@ SIGNATURES = {
                                        _vp, _vp, _vp, _sz, _vp]),
     "w8a8_linear_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "w8a8_linear": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "w4a8_linear_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _sz, _i64, _i64, _i64, _i32, _vp, _vp]),
     # include/w4a8_peaks.h
     "w4a8_peak_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "w4a8_peak_mfma_i8": (ctypes.c_int, [_i32, _vp, _vp, _i32, _vp]),
@@ -353,6 +354,26 @@ def linear(x: torch.Tensor, w: PackedWeight, out=None, workspace=None) -> torch.
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.w4a8_linear(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group, _p(out),
                            _p(workspace), wsb, _stream(x.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_noalloc(x: torch.Tensor, w: PackedWeight, out: torch.Tensor) -> torch.Tensor:
+    """w4a8_linear without a workspace (the library's static device scratch);
+    `out` must be given, so nothing is allocated."""
+    lib = load()
+    w.check()
+    _need_cuda(x, out)
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError(f"activations have K={K}, weight has K={w.K}")
+    dt = BF16 if x.dtype == torch.bfloat16 else F32 if x.dtype == torch.float32 else None
+    if dt is None:
+        raise TypeError(x.dtype)
+    _check(lib.w4a8_linear_noalloc(_p(x), dt, _p(w.buf), w.buf.numel(), M, w.N, w.K, w.group,
+                                   _p(out), _stream(x.device)))
     return out
 
 

@@ -34,6 +34,14 @@ int ok() {
   return W4A8_OK;
 }
 
+}  // namespace
+
+// Records the message w4a8_last_error() returns for a failing call made from
+// another translation unit of the library; returns status.
+int w4a8::report_error(int status, const char* msg) { return fail(status, "%s", msg); }
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_weight_shape(int64_t N, int64_t K, int32_t group) {

@@ -267,6 +267,9 @@ hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st);
 // ws is [ksplit][M][N - n0]: the columns [n0, N) of y (n0 = 0: all).
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st, int64_t n0 = 0);
+// Sets the thread's w4a8_last_error() message (abi.hip); returns status.
+int report_error(int status, const char* msg);
+
 // on-device peak probes (include/w4a8_peaks.h)
 hipError_t launch_peak_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks,
                                    hipStream_t st);

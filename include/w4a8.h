@@ -219,6 +219,29 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
                 int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * w4a8_linear_noalloc — w4a8_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments and result are those of w4a8_linear (bitwise
+ * the same output), without the workspace: the quantised activations, their
+ * scales and any split-K partial sums live in a static device array of
+ * W4A8_NOALLOC_SCRATCH_BYTES bytes that each GPU the library runs on holds
+ * from the library's first use on it until the process ends.  Its address is
+ * looked up once per device, on the first call with that device current.
+ * The call allocates and frees nothing.
+ *   - Shapes whose w4a8_linear_workspace_bytes(M, N, K, group) exceeds the
+ *     scratch return W4A8_ERR_BUFFER_TOO_SMALL before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's single scratch, which keeps the
+ *     last call's contents (nothing in it has to start at zero: each call
+ *     writes what it reads).  Calls that overlap in time on one GPU — on two
+ *     streams, or from two host threads without ordering between them — race
+ *     on it; the caller must serialise them (e.g. one stream).
+ */
+#define W4A8_NOALLOC_SCRATCH_BYTES (64u << 20)
+int w4a8_linear_noalloc(const void* x, int32_t x_dtype, const void* packed, size_t packed_bytes,
+                        int64_t M, int64_t N, int64_t K, int32_t group, uint16_t* y,
+                        void* stream);
+
 /* ------------------------------------------------------- online rotation
  *
  * The per-token quantisation preceded by an online Hadamard rotation, as in

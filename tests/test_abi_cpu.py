@@ -313,3 +313,16 @@ def test_peak_probe_rejections(lib):
     assert g(16, FAKE, None, 0, None) == -1
     assert g(16, MIS, None, 256, None) == -3
     assert g(16, FAKE, FAKE, 256, None) == -1                            # clocks alias sink
+
+
+def test_noalloc_rejections(lib):
+    """The allocation-free entry point refuses bad shapes and shapes whose
+    workspace exceeds its static scratch before touching the device."""
+    f = lib.w4a8_linear_noalloc
+    y = ctypes.c_void_p(1 << 28)
+    pb = lib.w4a8_packed_weight_bytes(256, 8192, 128)
+    assert f(FAKE, 0, FAKE2, pb, 8192, 256, 8192, 128, y, None) == -4   # 64 MiB of codes + more
+    assert b"static scratch" in lib.w4a8_last_error()
+    assert f(FAKE, 0, FAKE2, pb, 4, 250, 8192, 128, y, None) == -2      # N tail
+    assert f(FAKE, 0, FAKE2, pb, 0, 256, 8192, 128, y, None) == -1      # M
+    assert f(None, 0, FAKE2, pb, 4, 256, 8192, 128, y, None) == -1
