@@ -238,6 +238,25 @@ def bench_decode(torch, w4, args):
         w4.quant_act(x, qa, sa)
         w4.gemm(qa, sa, Ws[i % R], out=y, workspace=ws)
 
+    # the floor under the decode step, each from a graph of back-to-back
+    # launches like the step itself: a near-empty launch of as many threads
+    # as the GEMV (1024 workgroups of 256 threads reading 16 bytes), and the
+    # streaming probe reading each packed copy once (the same 36.6 MB per
+    # step the GEMV streams, rotated so the Infinity Cache cannot serve it)
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    tiny = torch.zeros(4, dtype=torch.int32, device="cuda")
+    empty_ms = graph_launches_ms(torch, lambda i: w4.peak_stream_read(tiny, 1024, sink), args.steps)
+    stream = {}
+    for blocks in (256, 1024, 2048):
+        ms = graph_launches_ms(torch, lambda i, b=blocks: w4.peak_stream_read(Ws[i % R].buf, b, sink),
+                               args.steps)
+        stream[str(blocks)] = round(ms * 1e3, 3)
+    floor = {"empty_launch_us": round(empty_ms * 1e3, 3),
+             "stream_packed_copy_us_by_blocks": stream,
+             "packed_copy_bytes": int(Ws[0].buf.numel()),
+             "gemv_us": round(kern_ms * 1e3, 3),
+             "note": "graph-replayed back-to-back launches; a 256-thread workgroup per block"}
+
     two_ms = graph_steps_ms(torch, two_launch, args.warmup, args.steps) / args.steps
     quant_ms = graph_launches_ms(torch, lambda i: w4.quant_act(x, qa, sa), args.steps)
     gemm_ms = graph_launches_ms(torch, lambda i: w4.gemm(qa, sa, Ws[i % R], out=y, workspace=ws),
@@ -257,6 +276,7 @@ def bench_decode(torch, w4, args):
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(kern_ms * 1e3, 3),
                      "timing": f"{args.steps} launches replayed from one HIP graph"},
+        "floor": floor,
         "two_launch": {"us_per_step": round(two_ms * 1e3, 3),
                        "quant_kernel_us": round(quant_ms * 1e3, 3),
                        "gemv_kernel_us": round(gemm_ms * 1e3, 3),
@@ -887,6 +907,7 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu_dec,
         "two_launch": dec["two_launch"],
+        "decode_floor": dec["floor"],
         "parity": dec["parity"],
     }
     if dec.get("spread"):

@@ -5,7 +5,7 @@ The public API is the C ABI in include/w4a8.h; this package is its thin
 Python binding (torch for device memory and streams only).
 """
 from ._lib import (  # noqa: F401
-    BF16, F32, GROUP, PATH_AUTO, PATH_GEMV, PATH_PREFILL, PATH_SKINNY, PackedWeight, SiblingWeight,
+    BF16, F32, GROUP, PATH_AUTO, PATH_GEMV, PATH_PREFILL, PATH_PREFILL_N128, PATH_PREFILL_N256, PATH_SKINNY, PackedWeight, SiblingWeight,
     W4A8Error, gemm, gemm_debug, linear, linear_siblings, linear_workspace_bytes, load,
     pack_siblings, pack_weights, packed_weight_bytes, quant_act, select_path, unpack_weights,
     workspace_bytes, PackedW8, quant_act_hadamard, linear_hadamard, w4a16_linear,

@@ -29,6 +29,8 @@ PATH_AUTO = 0
 PATH_GEMV = 1
 PATH_SKINNY = 2
 PATH_PREFILL = 3
+PATH_PREFILL_N128 = 4      # w4a8_gemm_debug only: prefill with 256 x 128 tiles forced
+PATH_PREFILL_N256 = 5      # w4a8_gemm_debug only: prefill with 256 x 256 tiles forced
 
 GROUP = 128
 

@@ -99,41 +99,48 @@ ChunkWindow chunk_window(int64_t m_begin, int64_t m_end, int64_t m0, int64_t mc)
   return ChunkWindow{b - m0, e - m0, b - m_begin};
 }
 
-// The prefill's tail split (none when the rows run as several chunks) and
-// the workspace bytes its slices take ([split][M][N - n0], 4 bytes each).
-PrefillTail prefill_tail_for(int64_t M, int64_t N, int64_t K) {
+// The prefill's tail split for a tile width (none when the rows run as
+// several chunks) and the workspace bytes its slices take ([split][M][N -
+// n0], 4 bytes each).
+PrefillTail prefill_tail_for(int64_t M, int64_t N, int64_t K, int tile) {
   if (M > prefill_chunk_rows(K, 1)) return PrefillTail{0, 0, 0};
-  return prefill_tail(M, N, K);
+  return prefill_tail(M, N, K, tile);
 }
 size_t tail_workspace(const PrefillTail& t, int64_t M, int64_t N) {
   if (t.split < 2) return 0;
   return ((size_t)t.split * (size_t)M * (size_t)(N - t.n0) * 4 + 255) / 256 * 256;
 }
 
-int ksplit_for(int path, int64_t M, int64_t N, int64_t K) {
+// `tile` (PrefillTile) matters for the PREFILL path only.
+int ksplit_for(int path, int64_t M, int64_t N, int64_t K, int tile) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
-  if (path == W4A8_PATH_PREFILL) return prefill_ksplit(M, N, K);
+  if (path == W4A8_PATH_PREFILL) return prefill_ksplit(M, N, K, tile);
   return 1;
 }
 
 // Split-K partial sums [ksplit][M][N] float, then (GEMV only) one 256-byte
 // slot for the scale the fused quantiser computes.
-size_t workspace_for(int path, int64_t M, int64_t N, int64_t K) {
-  const int ks = ksplit_for(path, M, N, K);
-  if (ks <= 1) return path == W4A8_PATH_PREFILL ? tail_workspace(prefill_tail_for(M, N, K), M, N) : 0;
+size_t workspace_for(int path, int64_t M, int64_t N, int64_t K, int tile) {
+  const int ks = ksplit_for(path, M, N, K, tile);
+  if (ks <= 1)
+    return path == W4A8_PATH_PREFILL ? tail_workspace(prefill_tail_for(M, N, K, tile), M, N) : 0;
   size_t b = (size_t)ks * (size_t)M * (size_t)N * sizeof(float);
   b = (b + 255) / 256 * 256;
   return path == W4A8_PATH_GEMV ? b + 256 : b;
 }
 
+// The most any path (and either prefill tile width, which the debug entry
+// point can force) needs.
 size_t gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
   size_t need = 0;
   for (int p = W4A8_PATH_GEMV; p <= W4A8_PATH_PREFILL; ++p) {
     if (p == W4A8_PATH_GEMV && (M != 1 || K > kGemvMaxK)) continue;
     if (p == W4A8_PATH_SKINNY && M > 16) continue;
-    const size_t w = workspace_for(p, M, N, K);
-    if (w > need) need = w;
+    for (int tile : {kTile256x128, kTile256x256}) {
+      const size_t w = workspace_for(p, M, N, K, tile);
+      if (w > need) need = w;
+    }
   }
   return need;
 }
@@ -168,8 +175,16 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   if (packed_bytes_ < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "packed buffer %zu bytes, need %zu", packed_bytes_, need);
   if (path == W4A8_PATH_AUTO) path = pick_path(M, K);
+  int tile = -1;  // prefill tile width: forced by the debug-only paths, else by shape
+  if (path == W4A8_PATH_PREFILL_N128 || path == W4A8_PATH_PREFILL_N256) {
+    if (!debug)
+      return fail(W4A8_ERR_INVALID_ARG, "path %d is accepted by w4a8_gemm_debug only", (int)path);
+    tile = path == W4A8_PATH_PREFILL_N256 ? kTile256x256 : kTile256x128;
+    path = W4A8_PATH_PREFILL;
+  }
   if (path < W4A8_PATH_GEMV || path > W4A8_PATH_PREFILL)
     return fail(W4A8_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (path == W4A8_PATH_PREFILL && tile < 0) tile = prefill_auto_tile(M, N, K);
   if (path == W4A8_PATH_GEMV && M != 1)
     return fail(W4A8_ERR_INVALID_ARG, "GEMV path needs M == 1 (M=%lld)", (long long)M);
   if (path == W4A8_PATH_GEMV && K > kGemvMaxK)
@@ -192,8 +207,8 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
     if (partials && !aligned16(partials))
       return fail(W4A8_ERR_MISALIGNED, "partials must be 16-byte aligned");
   }
-  const int ks = ksplit_for(path, M, N, K);
-  const size_t ws_need = workspace_for(path, M, N, K);
+  const int ks = ksplit_for(path, M, N, K, tile);
+  const size_t ws_need = workspace_for(path, M, N, K, tile);
   if (ws_need && (!workspace || workspace_bytes < ws_need))
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
                 ws_need);
@@ -229,6 +244,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   a.ksplit = ks;
   a.cb = a.ks = 0;
   a.w8 = false;
+  a.wide = path == W4A8_PATH_PREFILL && tile == kTile256x256;
   a.hadamard = fused && hadamard;
   const float* sa_for_reduce = act.sa;
   if (path == W4A8_PATH_GEMV) {
@@ -252,7 +268,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
     // K reuses the front of the workspace, chunk after chunk on the stream
     const int64_t rows = prefill_chunk_rows(K, 1);
     const int64_t G = K / kGroup;
-    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K);
+    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K, tile);
     a.tail_split = tail.split;
     a.tail_tiles = tail.tiles;
     a.tail_n0 = tail.n0;
@@ -290,7 +306,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
 // Workspace of w4a8_linear: the fused GEMV's own, or quantised activations
 // (qa, sa) followed by the GEMM's workspace.
 size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
-  if (pick_path(M, K) == W4A8_PATH_GEMV) return workspace_for(W4A8_PATH_GEMV, M, N, K);
+  if (pick_path(M, K) == W4A8_PATH_GEMV) return workspace_for(W4A8_PATH_GEMV, M, N, K, 0);
   return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
 }
 
@@ -310,7 +326,7 @@ int a16_ksplit(int path, int64_t M, int64_t N, int64_t K) {
 // The W4A16 prefill's tail split (none when the rows run as several chunks).
 PrefillTail a16_tail_for(int64_t M, int64_t N, int64_t K) {
   if (M > prefill_chunk_rows(K, 2)) return PrefillTail{0, 0, 0};
-  return prefill_tail(M, N, K, /*a16=*/true);
+  return prefill_tail(M, N, K, kTileA16);
 }
 
 size_t a16_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
@@ -461,14 +477,17 @@ int pick_w8_path(int64_t M, int64_t N, int64_t K) {
 
 int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
-  return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K) : prefill_ksplit(M, N, K);
+  return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K) : prefill_ksplit(M, N, K, kTile256x128);
 }
 
 // int32 split-K partials [ksplit][M][N], then (GEMV only) one 256-byte slot
 // for the scale the fused quantiser computes.
 size_t w8_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = w8_ksplit(path, M, N, K);
-  if (ks <= 1) return path == W4A8_PATH_PREFILL ? tail_workspace(prefill_tail_for(M, N, K), M, N) : 0;
+  if (ks <= 1)
+    return path == W4A8_PATH_PREFILL
+               ? tail_workspace(prefill_tail_for(M, N, K, kTile256x128), M, N)
+               : 0;
   return round256((size_t)ks * (size_t)M * (size_t)N * 4) + (path == W4A8_PATH_GEMV ? 256 : 0);
 }
 
@@ -589,7 +608,8 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   if (path == W4A8_PATH_PREFILL) {
     // row chunks, as for W4A8; the totals of the debug window per chunk
     const int64_t rows = prefill_chunk_rows(K, 1);
-    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K);
+    const PrefillTail tail =
+        ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K, kTile256x128);
     a.tail_split = tail.split;
     a.tail_tiles = tail.tiles;
     a.tail_n0 = tail.n0;

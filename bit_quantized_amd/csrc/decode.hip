@@ -531,17 +531,35 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
 // y[m][n] = bf16(sa[m] * sum_k ws[k][m][n]), summed in split order.  The
 // per-token scale comes from `sa` (a device array written before this kernel
 // runs: by the caller, or by the fused-quant GEMV).
+// The slices cover columns [n0, N) of y: ws is [ksplit][M][N - n0].  Each
+// thread takes eight consecutive outputs of one row (N - n0 is a multiple of
+// 16): 16-byte loads of every slice, one 16-byte store.
 __global__ void __launch_bounds__(256)
-// The slices cover columns [n0, N) of y: ws is [ksplit][M][N - n0].
 splitk_reduce_kernel(const float* __restrict__ ws, int ksplit, const float* __restrict__ sa,
                      int64_t M, int64_t N, uint16_t* __restrict__ y, int64_t n0) {
   const int64_t W = N - n0;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (t >= M * W) return;
   const int64_t m = t / W;
-  float v = ws[t];
-  for (int k = 1; k < ksplit; ++k) v += ws[k * M * W + t];
-  y[m * N + n0 + t % W] = f32_to_bf16_rne(sa ? sa[m] * v : v);
+  float v[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(ws + t);
+    const float4 b = *reinterpret_cast<const float4*>(ws + t + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  for (int k = 1; k < ksplit; ++k) {
+    const float4 a = *reinterpret_cast<const float4*>(ws + k * M * W + t);
+    const float4 b = *reinterpret_cast<const float4*>(ws + k * M * W + t + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  const float s = sa ? sa[m] : 1.0f;  // 1 * v == v exactly
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)f32_to_bf16_rne(s * v[2 * i]) | ((uint32_t)f32_to_bf16_rne(s * v[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(y + m * N + n0 + t % W) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // W8A8 split-K: the exact int32 totals summed over the slices (order-free),
@@ -733,7 +751,8 @@ hipError_t launch_w8_splitk_reduce(const int32_t* ws, int ksplit, const float* s
 
 hipError_t launch_splitk_reduce(const float* ws, int ksplit, const float* sa, int64_t M,
                                 int64_t N, uint16_t* y, hipStream_t st, int64_t n0) {
-  const int64_t total = M * (N - n0);
+  if ((N - n0) % 16 || n0 % 16) return hipErrorInvalidValue;
+  const int64_t total = M * (N - n0) / 8;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
                      st, ws, ksplit, sa, M, N, y, n0);
   return hipGetLastError();

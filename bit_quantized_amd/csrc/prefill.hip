@@ -393,6 +393,295 @@ prefill_kernel(GemmArgs a) {
   }
 }
 
+// --------------------------------------------------------------- wide tiles
+//
+// The same product on 256 x 256 output tiles: eight wavefronts of 64 tokens x
+// 128 channels (4 x 8 tiles of 16 x 16), still two per SIMD.  Per group of
+// 128 input channels the workgroup moves the activation tile (32 KiB, straight
+// into LDS) and the 16 code blocks (16 KiB, unpacked once to 32 KiB of q - z
+// bytes in LDS) for twice the products of the 256 x 128 tile: half the
+// activation bytes per product, and a quarter fewer fragment reads per product
+// (64 x 128 wave tiles read 24 KiB per 1 MiB products instead of 16 KiB per
+// 0.5 MiB).  Both the LDS and the path from L2 into the compute unit bound the
+// 256 x 128 tile well before its matrix cores do.
+namespace wide {
+
+constexpr int BN = 256;                       // output channels per tile
+constexpr int NCB = BN / kBlockCols;          // packed blocks per tile (16)
+constexpr int kAOff = 0;                      // activation tile [BM][128], chunks swizzled
+constexpr int kBOff = kAOff + BM * kGroup;    // unpacked q - z, [NCB][2][64 lanes][16 B]
+constexpr int kSOff = kBOff + NCB * 2 * kBlockBytes;  // scales [16 channels][NCB]
+constexpr int kBufBytes = kSOff + NCB * 16 * 4;
+
+// One group's weight operands in registers: thread t holds lane t % 64 of
+// code blocks t / 64 and t / 64 + 8 of the tile, their zero-point bytes, and
+// the scale of scale-table entry t % 256.
+struct Stage {
+  v4i b[2];
+  uint32_t zb[2];
+  float s;
+};
+
+struct Offsets {
+  uint32_t a[kADma];
+  uint32_t b[2], z[2], s;
+  int zshift;
+};
+
+__device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
+                                                int64_t NB, int64_t G) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Offsets o;
+#pragma unroll
+  for (int i = 0; i < kADma; ++i) {
+    const int r = kADmaRows * (kADma * wave + i) + (lane >> 3);
+    o.a[i] = (uint32_t)(min(m0 + r, a.M - 1) * a.K + 16 * a_chunk(r, lane & 7));
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int64_t nb = min(cb0 + wave + 8 * k, NB - 1);
+    o.b[k] = (uint32_t)(nb * G * kBlockBytes + lane * 16);
+    o.z[k] = (uint32_t)(nb * G * kZeroBlockBytes + ((lane & 15) >> 1));
+  }
+  o.zshift = (lane & 1) * 4;
+  const int64_t nbs = min(cb0 + ((tid >> 4) & (NCB - 1)), NB - 1);
+  o.s = (uint32_t)(nbs * G * 16 + (tid & 15));
+  return o;
+}
+
+__device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
+                                           Stage& st) {
+  const uint8_t* codes = a.w.codes + g * kBlockBytes;
+  const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    st.b[k] = *reinterpret_cast<const v4i*>(codes + o.b[k]);
+    st.zb[k] = zeros[o.z[k]];
+  }
+  st.s = (a.w.scales + g * 16)[o.s];
+}
+
+// Stage -> LDS: code block k (of the thread's two) unpacked to q - z bytes in
+// MFMA operand order (block u, half h, lane L) ...
+__device__ __forceinline__ void store_block(uint8_t* buf, const Stage& st, int zshift, int k) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t zz = ((st.zb[k] >> zshift) & 0xFu) * 0x01010101u;
+  v4i lo, hi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t d = (uint32_t)st.b[k][w];
+    lo[w] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
+    hi[w] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
+  }
+  const int u = wave + 8 * k;
+  *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 0) * kBlockBytes + lane * 16) = lo;
+  *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + lane * 16) = hi;
+}
+// ... and the scale table, transposed to [channel][block] so that a lane's
+// eight scales are contiguous.
+__device__ __forceinline__ void store_scale(uint8_t* buf, const Stage& st) {
+  const int e = threadIdx.x & (NCB * 16 - 1);  // entry (block e / 16, channel e % 16); two writers
+  reinterpret_cast<float*>(buf + kSOff)[(e & 15) * NCB + (e >> 4)] = st.s;
+}
+__device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
+  store_block(buf, st, zshift, 0);
+  store_block(buf, st, zshift, 1);
+  store_scale(buf, st);
+}
+
+// One group: the wavefront's 4 x 8 tiles, an MFMA pair each, and the rescale
+// of the tile two steps behind into the float accumulators.  A fragments are
+// read once; B fragments column tile by column tile, one ahead.
+// With `next` set, the next group's weights (already loaded into `st`) are
+// unpacked into `next` between the MFMA pairs of this group, where the
+// other wavefront of the SIMD keeps the matrix core busy, rather than in a
+// burst after them.
+template <bool DEBUG>
+__device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* buf, int64_t g,
+                                              int64_t m0, int64_t cb0, int64_t NB, int64_t G,
+                                              float (&accf)[4][8][4], uint8_t* next,
+                                              const Stage& st, int zshift) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  v4i a0[4], a1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // rows wm*64 + 16i + r16: the swizzle is r16 % 8
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kGroup;
+    a0[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, j));
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, 4 + j));
+  }
+  const float* srow = reinterpret_cast<const float*>(buf + kSOff) + r16 * NCB + wn * 8;
+  const v4i s0 = *reinterpret_cast<const v4i*>(srow), s1 = *reinterpret_cast<const v4i*>(srow + 4);
+  float sv[8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    sv[u] = __int_as_float(s0[u]);
+    sv[u + 4] = __int_as_float(s1[u]);
+  }
+  v4i b0[8], b1[8];
+  auto load_b = [&](int u) __attribute__((always_inline)) {
+    const int cb = wn * 8 + u;
+    b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
+    b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
+  };
+  load_b(0);
+  v4i acc[32];
+#pragma unroll
+  for (int t = 0; t < 34; ++t) {
+    if (t < 32) {
+      const int u = t >> 2, i = t & 3;
+      if (i == 0 && u + 1 < 8) load_b(u + 1);  // one column tile ahead
+      if (next && t == 16) store_block(next, st, zshift, 0);
+      if (next && t == 22) store_block(next, st, zshift, 1);
+      if (next && t == 28) store_scale(next, st);
+      const v4i zero = {0, 0, 0, 0};
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
+    }
+    if (t >= 2) {
+      const int e = t - 2, u = e >> 2, i = e & 3;
+      if (DEBUG && a.partials) {
+        const int64_t nb = cb0 + wn * 8 + u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+          if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
+            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
+      // The next MFMA pair takes its A operand through this empty statement,
+      // which reads the tile just rescaled: the compiler cannot run the
+      // pairs ahead of the rescales (which would keep every tile's int32
+      // results live at once) nor delay the rescales behind them.
+      if (t + 1 < 32) {
+        const int in = (t + 1) & 3;
+        asm volatile("" : "+v"(a0[in]) : "v"(accf[i][u][0]), "v"(accf[i][u][1]), "v"(accf[i][u][2]),
+                     "v"(accf[i][u][3]));
+      }
+    }
+  }
+}
+
+template <bool DEBUG>
+__global__ void __launch_bounds__(kThreads)
+prefill_wide_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 wavefronts of 64 x 128
+  const int r16 = lane & 15, j = lane >> 4;
+  const int64_t G = a.K / kGroup;
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (NB + NCB - 1) / NCB;
+  // whole tiles, then (with a tail split) the tail tiles' K slices, as in
+  // the 256 x 128 kernel
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t main_tiles = a.tail_split > 1 ? tiles - a.tail_tiles : tiles;
+  int64_t t;
+  int slice = blockIdx.y, nslices = gridDim.y;
+  int64_t wn0 = 0;
+  if ((int64_t)blockIdx.x < main_tiles) {
+    t = xcd_tile(blockIdx.x, main_tiles);
+  } else {
+    const int64_t r = blockIdx.x - main_tiles;
+    t = main_tiles + r % a.tail_tiles;
+    slice = (int)(r / a.tail_tiles);
+    nslices = a.tail_split;
+    wn0 = a.tail_n0;
+  }
+  const bool split = nslices > 1;
+  const int64_t ldw = a.N - wn0;
+  const int64_t tm = t % tiles_m, tn = t / tiles_m;
+  const int64_t m0 = tm * BM, cb0 = tn * NCB;
+  const int64_t gb = G * slice / nslices, ge = G * (slice + 1) / nslices;
+
+  float accf[4][8][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
+
+  const Offsets off = make_offsets(a, m0, cb0, NB, G);
+  const __amdgpu_buffer_rsrc_t rqa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.qa), (short)0, (int)(a.M * a.K),
+                                        kBufferWord3);
+#define WIDE_DMA(B, g)                                                                        \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_)                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
+          rqa, &smem[B][kAOff + (kADma * wave + i_) * 1024], 16, off.a[i_],                   \
+          (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * kGroup)), 0, 0);               \
+  } while (0)
+  Stage sb;
+  WIDE_DMA(0, gb);
+  load_stage(a, off, gb, sb);
+  store_stage(smem[0], sb, off.zshift);
+  __syncthreads();
+  for (int64_t g = gb; g < ge; g += 2) {
+    if (g + 1 < ge) {  // buffer 1 was last read before the previous barrier
+      WIDE_DMA(1, g + 1);
+      load_stage(a, off, g + 1, sb);
+    }
+    compute_group<DEBUG>(a, smem[0], g, m0, cb0, NB, G, accf, g + 1 < ge ? smem[1] : nullptr, sb,
+                         off.zshift);
+    __syncthreads();
+    if (g + 1 >= ge) break;
+    if (g + 2 < ge) {
+      WIDE_DMA(0, g + 2);
+      load_stage(a, off, g + 2, sb);
+    }
+    compute_group<DEBUG>(a, smem[1], g + 1, m0, cb0, NB, G, accf, g + 2 < ge ? smem[0] : nullptr,
+                         sb, off.zshift);
+    __syncthreads();
+  }
+#undef WIDE_DMA
+
+  if (split) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t nb = cb0 + wn * 8 + u;
+          if (nb < NB)
+            a.workspace[((int64_t)slice * a.M + m) * ldw + nb * 16 + r16 - wn0] = accf[i][u][r];
+        }
+      }
+    return;
+  }
+  if (!a.y) return;
+  float sam[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sam[i][r] = a.sa[min(m0 + wm * 64 + i * 16 + 4 * j + r, a.M - 1)];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t nb = cb0 + wn * 8 + u;
+        if (nb < NB) a.y[m * a.N + nb * 16 + r16] = f32_to_bf16_rne(sam[i][r] * accf[i][u][r]);
+      }
+    }
+  }
+}
+
+}  // namespace wide
+
 // --------------------------------------------------------------- W4A16
 //
 // "The 4-bit CPU path", section "W4A16": large batches of bf16 activations
@@ -606,22 +895,43 @@ prefill_a16_kernel(GemmArgs a) {
 
 }  // namespace
 
+namespace {
+// Output tile of a prefill kernel: rows (tokens) and 16-channel blocks.
+int64_t tile_rows(int tile) { return tile == kTileA16 ? a16::BM : BM; }
+int64_t tile_blocks(int tile) { return tile == kTile256x256 ? wide::NCB : NCB; }
+int64_t tile_count(int64_t M, int64_t N, int tile) {
+  const int64_t bm = tile_rows(tile), ncb = tile_blocks(tile);
+  return ((M + bm - 1) / bm) * ((N / kBlockCols + ncb - 1) / ncb);
+}
+}  // namespace
+
+// 256 x 256 tiles halve the activation bytes per product and cut the fragment
+// reads by a quarter, but fewer than one round of them leaves compute units
+// idle that 256 x 128 tiles (with their K split) would use.  Measured
+// (quantised GEMM, us, 256 x 128 against 256 x 256): M = 2048, K = 3584 ->
+// N = 18944 200 / 187; M = 512 -> N = 37888 119 / 107; M = 512 -> N = 18944
+// 63 / 73; M = 2048 -> N = 4608 62 / 71.
+int prefill_auto_tile(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  return tile_count(M, N, kTile256x256) >= (int64_t)device_cus() ? kTile256x256 : kTile256x128;
+}
+
 // Split K only while the output tiles leave compute units idle, keeping at
 // least two groups per slice.
-int prefill_ksplit(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N / kBlockCols + NCB - 1) / NCB);
+int prefill_ksplit(int64_t M, int64_t N, int64_t K, int tile) {
+  const int64_t tiles = tile_count(M, N, tile);
   const int64_t G = K / kGroup, cus = device_cus();
   int ks = 1;
   while (tiles * ks * 2 <= cus && G >= (int64_t)ks * 2 * 2) ks *= 2;
   return ks;
 }
 
-// Measured at M = 512, K = 3584 -> N = 18944 (296 tiles: one round and 40
-// tiles): with the last 40 tiles as 6 K slices each, quantisation + GEMM
-// takes 68.6 us instead of 87 us.
-PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, bool a16) {
-  const int64_t bm = a16 ? a16::BM : BM;
-  const int64_t tiles_m = (M + bm - 1) / bm, tiles_n = (N / kBlockCols + NCB - 1) / NCB;
+// Measured at M = 512, K = 3584 -> N = 18944 (296 tiles of 256 x 128: one
+// round and 40 tiles): with the last 40 tiles as 6 K slices each,
+// quantisation + GEMM takes 68.6 us instead of 87 us.
+PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, int tile) {
+  const int64_t bm = tile_rows(tile), ncb = tile_blocks(tile);
+  const int64_t tiles_m = (M + bm - 1) / bm, tiles_n = (N / kBlockCols + ncb - 1) / ncb;
   const int64_t tiles = tiles_m * tiles_n, cus = device_cus(), G = K / kGroup;
   const PrefillTail none{0, 0, 0};
   if (tiles <= cus || tiles % cus == 0) return none;
@@ -630,17 +940,22 @@ PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, bool a16) {
   int64_t s = cus / tail;
   if (s > G / 2) s = G / 2;  // at least two groups per slice
   if (s < 2) return none;
-  return PrefillTail{(int)s, tail, (tiles_n - cols) * NCB * kBlockCols};
+  return PrefillTail{(int)s, tail, (tiles_n - cols) * ncb * kBlockCols};
 }
 
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
-  const int64_t NB = a.N / kBlockCols;
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((NB + NCB - 1) / NCB);
+  if (a.wide && a.w8) return hipErrorInvalidValue;
+  const int64_t tiles = tile_count(a.M, a.N, a.wide ? kTile256x256 : kTile256x128);
   if (a.tail_split > 1 && (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
     return hipErrorInvalidValue;
   const int64_t wgs = a.tail_split > 1 ? tiles - a.tail_tiles + a.tail_tiles * a.tail_split : tiles;
   const dim3 grid((unsigned)wgs, (unsigned)a.ksplit);
-  if (a.w8) {
+  if (a.wide) {
+    if (a.partials)
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<true>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<false>), grid, dim3(kThreads), 0, st, a);
+  } else if (a.w8) {
     if (a.partials)
       hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
     else
@@ -655,17 +970,10 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
 
 // W4A16 prefill: K is split (float partials, deterministic reduce) only while
 // the output tiles leave compute units idle.
-int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + a16::BM - 1) / a16::BM) * ((N / kBlockCols + NCB - 1) / NCB);
-  const int64_t G = K / kGroup, cus = device_cus();
-  int ks = 1;
-  while (tiles * ks * 2 <= cus && G >= (int64_t)ks * 2 * 2) ks *= 2;
-  return ks;
-}
+int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K) { return prefill_ksplit(M, N, K, kTileA16); }
 
 hipError_t launch_prefill_a16(const GemmArgs& a, hipStream_t st) {
-  const int64_t NB = a.N / kBlockCols;
-  const int64_t tiles = ((a.M + a16::BM - 1) / a16::BM) * ((NB + NCB - 1) / NCB);
+  const int64_t tiles = tile_count(a.M, a.N, kTileA16);
   if (a.tail_split > 1 && (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
     return hipErrorInvalidValue;
   const int64_t wgs = a.tail_split > 1 ? tiles - a.tail_tiles + a.tail_tiles * a.tail_split : tiles;

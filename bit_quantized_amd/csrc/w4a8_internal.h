@@ -215,6 +215,8 @@ struct GemmArgs {
   // tail_split K slices into workspace [tail_split][M][N - tail_n0]
   int tail_split = 0;
   int64_t tail_tiles = 0, tail_n0 = 0;
+  // prefill (W4A8): 256 x 256 output tiles instead of 256 x 128
+  bool wide = false;
   // the GEMV's in-kernel quantisation (bf16 / f32 token, not debug): rotate
   // each group of 128 by the Walsh-Hadamard matrix first (hadamard_chunk), as
   // w4a8_quant_act_hadamard
@@ -237,7 +239,13 @@ int skinny_ksplit(int64_t M, int64_t N, int64_t K);
 // Whether the 2 <= M <= 16 kernel can quantise raw activations of this shape
 // itself (GemmArgs::x set); x_dtype as in GemmArgs.
 bool skinny_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype);
-int prefill_ksplit(int64_t M, int64_t N, int64_t K);
+// Output tiles of the prefill kernels: 256 tokens x 128 channels (W4A8 and
+// W8A8), 256 x 256 (W4A8, large grids), 128 x 128 (W4A16).
+enum PrefillTile { kTile256x128 = 0, kTile256x256 = 1, kTileA16 = 2 };
+// The W4A8 tile for an M x N x K product: 256 x 256 when its tiles fill at
+// least one round of the compute units, else 256 x 128.
+int prefill_auto_tile(int64_t M, int64_t N, int64_t K);
+int prefill_ksplit(int64_t M, int64_t N, int64_t K, int tile);
 // Prefill grid beyond prefill_ksplit: when the tiles fill R whole rounds of
 // the compute units plus a partial one, the partial round's tiles (rounded up
 // to whole column tiles) run as `split` K slices each, so the last round is
@@ -246,7 +254,7 @@ struct PrefillTail {
   int split;
   int64_t tiles, n0;
 };
-PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, bool a16 = false);  // a16: W4A16 tiles
+PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, int tile);
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t st);
 // W4A16 (bf16 token in GemmArgs::x, M == 1) on the GEMV kernel; same grid rules.
 hipError_t launch_gemv_a16(const GemmArgs& a, hipStream_t st);

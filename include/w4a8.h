@@ -70,6 +70,12 @@ extern "C" {
 #define W4A8_PATH_GEMV 1
 #define W4A8_PATH_SKINNY 2
 #define W4A8_PATH_PREFILL 3
+/* PREFILL computes 256-token x 256-channel output tiles when they fill at
+ * least one round of the compute units, else 256 x 128 tiles.  For tests,
+ * w4a8_gemm_debug (and only it) also takes these two paths, which force the
+ * tile width at any shape; w4a8_select_path never returns them. */
+#define W4A8_PATH_PREFILL_N128 4
+#define W4A8_PATH_PREFILL_N256 5
 
 int w4a8_abi_version(void);
 /* Bumped whenever the packed weight format changes; a packed buffer is only
@@ -188,7 +194,8 @@ int w4a8_gemm(const int8_t* qa, const float* sa, const void* packed, size_t pack
  *   partials  device int32 [m_end - m_begin][N][K/group] (may be NULL)
  *   y_or_null device bfloat16 [M][N] or NULL (then y is not written)
  * path must be AUTO, GEMV (requires M == 1 and K <= 32768), SKINNY
- * (M <= 16) or PREFILL.
+ * (M <= 16), PREFILL, or PREFILL_N128 / PREFILL_N256 (PREFILL with the tile
+ * width forced).
  */
 int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_t packed_bytes,
                     int64_t M, int64_t N, int64_t K, int32_t group, int32_t path,

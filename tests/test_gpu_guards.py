@@ -79,7 +79,7 @@ def _check_y(y, lin, qa_ref, sa_ref, rows=None):
 
 
 def _paths(M):
-    return [3] + ([2] if M <= 16 else []) + ([1] if M == 1 else [])
+    return [3, 4, 5] + ([2] if M <= 16 else []) + ([1] if M == 1 else [])
 
 
 # (M, K, N): the M buckets and tile edges with a ragged N; split K on the

@@ -171,7 +171,9 @@ def test_quant_random_ties(w4):
 # ----------------------------------------------------------------- partials + output
 
 def _paths_for(M):
-    paths = [3]
+    # PREFILL as the shape picks it, then with each tile width forced
+    # (256 x 128 and 256 x 256), so both prefill kernels see every shape
+    paths = [3, 4, 5]
     if M <= 16:
         paths.append(2)
     if M == 1:
@@ -317,7 +319,8 @@ def test_errors_leave_outputs_untouched(w4):
     assert torch.all(y.float() == 7.0)
 
 
-@pytest.mark.parametrize("M,K,N", [(512, 3584, 18944), (300, 1024, 18992)])
+@pytest.mark.parametrize("M,K,N", [(512, 3584, 18944), (300, 1024, 18992), (2048, 1024, 9472),
+                                   (1800, 2048, 9488)])
 def test_prefill_tail_split(w4, M, K, N):
     """Tiles that fill one round and part of another: the partial round's
     tiles (whole column tiles, the last channels) run as K slices whose float
@@ -333,9 +336,14 @@ def test_prefill_tail_split(w4, M, K, N):
     for rows in [(0, 8), (M - 8, M)]:
         _check_y(y, lin, qa_ref, sa_ref, rows)
     P, y2 = w4.gemm_debug(qa, sa, W, path=w4.PATH_PREFILL, rows=(250, 262))
-    assert np.array_equal(P.cpu().numpy(),
-                          oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=250, m1=262))
+    P_ref = oracle.group_partials(qa_ref, lin["q"], lin["z"], m0=250, m1=262)
+    assert np.array_equal(P.cpu().numpy(), P_ref)
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+    # both tile widths forced: their own tail plans, the same partials
+    for path in (w4.PATH_PREFILL_N128, w4.PATH_PREFILL_N256):
+        P, y3 = w4.gemm_debug(qa, sa, W, path=path, rows=(250, 262))
+        assert np.array_equal(P.cpu().numpy(), P_ref), path
+        _check_y(y3, lin, qa_ref, sa_ref, (M - 8, M))
 
 
 @pytest.mark.parametrize("name,K,N", [("k", 3584, 512), ("o", 3584, 3584), ("down", 18944, 3584)])
