@@ -107,7 +107,7 @@ PrefillTail prefill_tail_for(int64_t M, int64_t N, int64_t K, int tile) {
   return prefill_tail(M, N, K, tile);
 }
 size_t tail_workspace(const PrefillTail& t, int64_t M, int64_t N) {
-  if (t.split < 2) return 0;
+  if (t.split < 2) return 0;  // none, or half tiles (split -1)
   return ((size_t)t.split * (size_t)M * (size_t)(N - t.n0) * 4 + 255) / 256 * 256;
 }
 

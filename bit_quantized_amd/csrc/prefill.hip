@@ -404,6 +404,12 @@ prefill_kernel(GemmArgs a) {
 // (64 x 128 wave tiles read 24 KiB per 1 MiB products instead of 16 KiB per
 // 0.5 MiB).  Both the LDS and the path from L2 into the compute unit bound the
 // 256 x 128 tile well before its matrix cores do.
+//
+// When the wide tiles fill whole rounds of the compute units plus a partial
+// round that half as many compute units could not finish faster in halves,
+// the partial round's channels run instead as 256 x 128 tiles of the same
+// kernel (wavefronts of 64 x 64: NU = 4 column tiles each), all in one round:
+// no K split, no partial sums in memory and no second kernel.
 namespace wide {
 
 constexpr int BN = 256;                       // output channels per tile
@@ -415,7 +421,8 @@ constexpr int kBufBytes = kSOff + NCB * 16 * 4;
 
 // One group's weight operands in registers: thread t holds lane t % 64 of
 // code blocks t / 64 and t / 64 + 8 of the tile, their zero-point bytes, and
-// the scale of scale-table entry t % 256.
+// the scale of scale-table entry t % 256.  (Half tiles use the first of the
+// two blocks and entries below 128 only.)
 struct Stage {
   v4i b[2];
   uint32_t zb[2];
@@ -428,8 +435,11 @@ struct Offsets {
   int zshift;
 };
 
+// Channel blocks per tile: 16 for whole tiles (NU = 8), 8 for half tiles.
+template <int NU>
 __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, int64_t cb0,
                                                 int64_t NB, int64_t G) {
+  constexpr int kBlocks = 2 * NU;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Offsets o;
 #pragma unroll
@@ -444,17 +454,18 @@ __device__ __forceinline__ Offsets make_offsets(const GemmArgs& a, int64_t m0, i
     o.z[k] = (uint32_t)(nb * G * kZeroBlockBytes + ((lane & 15) >> 1));
   }
   o.zshift = (lane & 1) * 4;
-  const int64_t nbs = min(cb0 + ((tid >> 4) & (NCB - 1)), NB - 1);
+  const int64_t nbs = min(cb0 + ((tid >> 4) & (kBlocks - 1)), NB - 1);
   o.s = (uint32_t)(nbs * G * 16 + (tid & 15));
   return o;
 }
 
+template <int NU>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Offsets& o, int64_t g,
                                            Stage& st) {
   const uint8_t* codes = a.w.codes + g * kBlockBytes;
   const uint8_t* zeros = a.w.zeros + g * kZeroBlockBytes;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NU / 4; ++k) {
     st.b[k] = *reinterpret_cast<const v4i*>(codes + o.b[k]);
     st.zb[k] = zeros[o.z[k]];
   }
@@ -478,29 +489,31 @@ __device__ __forceinline__ void store_block(uint8_t* buf, const Stage& st, int z
   *reinterpret_cast<v4i*>(buf + kBOff + (u * 2 + 1) * kBlockBytes + lane * 16) = hi;
 }
 // ... and the scale table, transposed to [channel][block] so that a lane's
-// eight scales are contiguous.
+// scales are contiguous.
+template <int NU>
 __device__ __forceinline__ void store_scale(uint8_t* buf, const Stage& st) {
-  const int e = threadIdx.x & (NCB * 16 - 1);  // entry (block e / 16, channel e % 16); two writers
-  reinterpret_cast<float*>(buf + kSOff)[(e & 15) * NCB + (e >> 4)] = st.s;
+  const int e = threadIdx.x & (NCB * 16 - 1);  // entry (block e / 16, channel e % 16)
+  if (NU == 8 || e < 128) reinterpret_cast<float*>(buf + kSOff)[(e & 15) * NCB + (e >> 4)] = st.s;
 }
+template <int NU>
 __device__ __forceinline__ void store_stage(uint8_t* buf, const Stage& st, int zshift) {
   store_block(buf, st, zshift, 0);
-  store_block(buf, st, zshift, 1);
-  store_scale(buf, st);
+  if (NU == 8) store_block(buf, st, zshift, 1);
+  store_scale<NU>(buf, st);
 }
 
-// One group: the wavefront's 4 x 8 tiles, an MFMA pair each, and the rescale
+// One group: the wavefront's 4 x NU tiles, an MFMA pair each, and the rescale
 // of the tile two steps behind into the float accumulators.  A fragments are
-// read once; B fragments column tile by column tile, one ahead.
-// With `next` set, the next group's weights (already loaded into `st`) are
-// unpacked into `next` between the MFMA pairs of this group, where the
-// other wavefront of the SIMD keeps the matrix core busy, rather than in a
-// burst after them.
-template <bool DEBUG>
+// read once; B fragments column tile by column tile, one ahead.  With `next`
+// set, the next group's weights (already loaded into `st`) are unpacked into
+// `next` between the MFMA pairs, where the other wavefront of the SIMD keeps
+// the matrix core busy, rather than in a burst after them.
+template <bool DEBUG, int NU>
 __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* buf, int64_t g,
                                               int64_t m0, int64_t cb0, int64_t NB, int64_t G,
-                                              float (&accf)[4][8][4], uint8_t* next,
+                                              float (&accf)[4][NU][4], uint8_t* next,
                                               const Stage& st, int zshift) {
+  constexpr int T = 4 * NU;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 3, wn = wave >> 2;
   const int r16 = lane & 15, j = lane >> 4;
@@ -511,30 +524,30 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
     a0[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, j));
     a1[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, 4 + j));
   }
-  const float* srow = reinterpret_cast<const float*>(buf + kSOff) + r16 * NCB + wn * 8;
-  const v4i s0 = *reinterpret_cast<const v4i*>(srow), s1 = *reinterpret_cast<const v4i*>(srow + 4);
-  float sv[8];
+  const float* srow = reinterpret_cast<const float*>(buf + kSOff) + r16 * NCB + wn * NU;
+  float sv[NU];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    sv[u] = __int_as_float(s0[u]);
-    sv[u + 4] = __int_as_float(s1[u]);
+  for (int q = 0; q < NU / 4; ++q) {
+    const v4i sq = *reinterpret_cast<const v4i*>(srow + 4 * q);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sv[4 * q + u] = __int_as_float(sq[u]);
   }
-  v4i b0[8], b1[8];
+  v4i b0[NU], b1[NU];
   auto load_b = [&](int u) __attribute__((always_inline)) {
-    const int cb = wn * 8 + u;
+    const int cb = wn * NU + u;
     b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
     b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
   };
   load_b(0);
-  v4i acc[32];
+  v4i acc[T];
 #pragma unroll
-  for (int t = 0; t < 34; ++t) {
-    if (t < 32) {
+  for (int t = 0; t < T + 2; ++t) {
+    if (t < T) {
       const int u = t >> 2, i = t & 3;
-      if (i == 0 && u + 1 < 8) load_b(u + 1);  // one column tile ahead
-      if (next && t == 16) store_block(next, st, zshift, 0);
-      if (next && t == 22) store_block(next, st, zshift, 1);
-      if (next && t == 28) store_scale(next, st);
+      if (i == 0 && u + 1 < NU) load_b(u + 1);  // one column tile ahead
+      if (next && t == T / 2) store_block(next, st, zshift, 0);
+      if (NU == 8 && next && t == 22) store_block(next, st, zshift, 1);
+      if (next && t == T - 4) store_scale<NU>(next, st);
       const v4i zero = {0, 0, 0, 0};
       acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
@@ -542,7 +555,7 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
     if (t >= 2) {
       const int e = t - 2, u = e >> 2, i = e & 3;
       if (DEBUG && a.partials) {
-        const int64_t nb = cb0 + wn * 8 + u;
+        const int64_t nb = cb0 + wn * NU + u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
@@ -556,7 +569,7 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
       // which reads the tile just rescaled: the compiler cannot run the
       // pairs ahead of the rescales (which would keep every tile's int32
       // results live at once) nor delay the rescales behind them.
-      if (t + 1 < 32) {
+      if (t + 1 < T) {
         const int in = (t + 1) & 3;
         asm volatile("" : "+v"(a0[in]) : "v"(accf[i][u][0]), "v"(accf[i][u][1]), "v"(accf[i][u][2]),
                      "v"(accf[i][u][3]));
@@ -565,50 +578,32 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
   }
 }
 
-template <bool DEBUG>
-__global__ void __launch_bounds__(kThreads)
-prefill_wide_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+// One output tile (rows m0.., channel blocks cb0..) over groups [gb, ge):
+// NU = 8 a whole 256 x 256 tile, NU = 4 a half tile of 256 x 128.  With
+// `split`, this K slice's float sums go to the workspace (rows of ldw
+// channels from wn0) instead of y.
+template <bool DEBUG, int NU>
+__device__ __forceinline__ void tile(const GemmArgs& a, uint8_t (&smem)[2][kBufBytes], int64_t m0,
+                                     int64_t cb0, int64_t gb, int64_t ge, bool split, int slice,
+                                     int64_t wn0) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 wavefronts of 64 x 128
+  const int wm = wave & 3, wn = wave >> 2;
   const int r16 = lane & 15, j = lane >> 4;
   const int64_t G = a.K / kGroup;
   const int64_t NB = a.N / kBlockCols;
-  const int64_t tiles_m = (a.M + BM - 1) / BM;
-  const int64_t tiles_n = (NB + NCB - 1) / NCB;
-  // whole tiles, then (with a tail split) the tail tiles' K slices, as in
-  // the 256 x 128 kernel
-  const int64_t tiles = tiles_m * tiles_n;
-  const int64_t main_tiles = a.tail_split > 1 ? tiles - a.tail_tiles : tiles;
-  int64_t t;
-  int slice = blockIdx.y, nslices = gridDim.y;
-  int64_t wn0 = 0;
-  if ((int64_t)blockIdx.x < main_tiles) {
-    t = xcd_tile(blockIdx.x, main_tiles);
-  } else {
-    const int64_t r = blockIdx.x - main_tiles;
-    t = main_tiles + r % a.tail_tiles;
-    slice = (int)(r / a.tail_tiles);
-    nslices = a.tail_split;
-    wn0 = a.tail_n0;
-  }
-  const bool split = nslices > 1;
   const int64_t ldw = a.N - wn0;
-  const int64_t tm = t % tiles_m, tn = t / tiles_m;
-  const int64_t m0 = tm * BM, cb0 = tn * NCB;
-  const int64_t gb = G * slice / nslices, ge = G * (slice + 1) / nslices;
 
-  float accf[4][8][4];
+  float accf[4][NU][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) accf[i][u][r] = 0.0f;
 
-  const Offsets off = make_offsets(a, m0, cb0, NB, G);
+  const Offsets off = make_offsets<NU>(a, m0, cb0, NB, G);
   const __amdgpu_buffer_rsrc_t rqa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.qa), (short)0, (int)(a.M * a.K),
                                         kBufferWord3);
@@ -621,24 +616,24 @@ prefill_wide_kernel(GemmArgs a) {
   } while (0)
   Stage sb;
   WIDE_DMA(0, gb);
-  load_stage(a, off, gb, sb);
-  store_stage(smem[0], sb, off.zshift);
+  load_stage<NU>(a, off, gb, sb);
+  store_stage<NU>(smem[0], sb, off.zshift);
   __syncthreads();
   for (int64_t g = gb; g < ge; g += 2) {
     if (g + 1 < ge) {  // buffer 1 was last read before the previous barrier
       WIDE_DMA(1, g + 1);
-      load_stage(a, off, g + 1, sb);
+      load_stage<NU>(a, off, g + 1, sb);
     }
-    compute_group<DEBUG>(a, smem[0], g, m0, cb0, NB, G, accf, g + 1 < ge ? smem[1] : nullptr, sb,
-                         off.zshift);
+    compute_group<DEBUG, NU>(a, smem[0], g, m0, cb0, NB, G, accf, g + 1 < ge ? smem[1] : nullptr,
+                             sb, off.zshift);
     __syncthreads();
     if (g + 1 >= ge) break;
     if (g + 2 < ge) {
       WIDE_DMA(0, g + 2);
-      load_stage(a, off, g + 2, sb);
+      load_stage<NU>(a, off, g + 2, sb);
     }
-    compute_group<DEBUG>(a, smem[1], g + 1, m0, cb0, NB, G, accf, g + 2 < ge ? smem[0] : nullptr,
-                         sb, off.zshift);
+    compute_group<DEBUG, NU>(a, smem[1], g + 1, m0, cb0, NB, G, accf,
+                             g + 2 < ge ? smem[0] : nullptr, sb, off.zshift);
     __syncthreads();
   }
 #undef WIDE_DMA
@@ -651,8 +646,8 @@ prefill_wide_kernel(GemmArgs a) {
         const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
         if (m >= a.M) continue;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t nb = cb0 + wn * 8 + u;
+        for (int u = 0; u < NU; ++u) {
+          const int64_t nb = cb0 + wn * NU + u;
           if (nb < NB)
             a.workspace[((int64_t)slice * a.M + m) * ldw + nb * 16 + r16 - wn0] = accf[i][u][r];
         }
@@ -672,12 +667,47 @@ prefill_wide_kernel(GemmArgs a) {
       const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
       if (m >= a.M) continue;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t nb = cb0 + wn * 8 + u;
+      for (int u = 0; u < NU; ++u) {
+        const int64_t nb = cb0 + wn * NU + u;
         if (nb < NB) a.y[m * a.N + nb * 16 + r16] = f32_to_bf16_rne(sam[i][r] * accf[i][u][r]);
       }
     }
   }
+}
+
+// Workgroups [0, main) take the whole tiles (XCD-aware order, tokens
+// fastest); the rest take the tail: with a.tail_split > 1, K slice r /
+// tail_tiles of whole tile main + r % tail_tiles; with a.tail_split == -1
+// (half tiles), half tile r of the channels from tail_n0 on.
+template <bool DEBUG>
+__global__ void __launch_bounds__(kThreads)
+prefill_wide_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+  const int64_t G = a.K / kGroup;
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (NB + NCB - 1) / NCB;
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t main_tiles = a.tail_split > 1 || a.tail_split == -1 ? tiles - a.tail_tiles : tiles;
+  if ((int64_t)blockIdx.x < main_tiles) {
+    const int64_t t = xcd_tile(blockIdx.x, main_tiles);
+    const int slice = blockIdx.y, nslices = gridDim.y;
+    const int64_t tm = t % tiles_m, tn = t / tiles_m;
+    tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / nslices, G * (slice + 1) / nslices,
+                   nslices > 1, slice, 0);
+    return;
+  }
+  const int64_t r = blockIdx.x - main_tiles;
+  if (a.tail_split == -1) {
+    const int64_t tm = r % tiles_m, tn = r / tiles_m;
+    tile<DEBUG, 4>(a, smem, tm * BM, a.tail_n0 / kBlockCols + tn * (NCB / 2), 0, G, false, 0, 0);
+    return;
+  }
+  const int64_t t = main_tiles + r % a.tail_tiles;
+  const int slice = (int)(r / a.tail_tiles);
+  const int64_t tm = t % tiles_m, tn = t / tiles_m;
+  tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / a.tail_split,
+                 G * (slice + 1) / a.tail_split, true, slice, a.tail_n0);
 }
 
 }  // namespace wide
@@ -937,18 +967,47 @@ PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, int tile) {
   if (tiles <= cus || tiles % cus == 0) return none;
   const int64_t cols = (tiles % cus + tiles_m - 1) / tiles_m;  // whole column tiles
   const int64_t tail = cols * tiles_m;
+  const int64_t n0 = (tiles_n - cols) * ncb * kBlockCols;
   int64_t s = cus / tail;
   if (s > G / 2) s = G / 2;  // at least two groups per slice
+  // 256 x 256 tiles: the tail's channels may instead run over all of K as
+  // 256 x 128 half tiles when those fit one round (split -1). The last round
+  // then takes about 0.72 of a tile's time (a half tile still loads the whole
+  // activation tile), against 1/s of it plus writing and re-reading the
+  // slices' float sums, which moved at about 4 TB/s each way. Fitted on
+  // MI355X at K = 3584, where a tile took about 67 us: M = 2048, N = 18944
+  // (3 slices) ran 190 us split and 182 us in half tiles; M = 512,
+  // N = 37888 (6 slices) 109 us split and 116 us in half tiles.
+  if (tile == kTile256x256) {
+    const int64_t halves = tiles_m * ((N / kBlockCols - n0 / kBlockCols + ncb / 2 - 1) / (ncb / 2));
+    if (halves <= cus) {
+      const double tile_us = 67.0 * (double)K / 3584.0;
+      const double half_us = 0.72 * tile_us;
+      double split_us = tile_us;
+      if (s >= 2) {
+        const double sums = (double)s * (double)M * (double)(N - n0) * 4.0;
+        split_us = tile_us / (double)s + 2.0 * sums / 4.0e6;
+      }
+      if (half_us < split_us) return PrefillTail{-1, tail, n0};
+    }
+  }
   if (s < 2) return none;
-  return PrefillTail{(int)s, tail, (tiles_n - cols) * ncb * kBlockCols};
+  return PrefillTail{(int)s, tail, n0};
 }
 
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
   if (a.wide && a.w8) return hipErrorInvalidValue;
   const int64_t tiles = tile_count(a.M, a.N, a.wide ? kTile256x256 : kTile256x128);
-  if (a.tail_split > 1 && (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
+  if ((a.tail_split > 1 || a.tail_split == -1) &&
+      (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
     return hipErrorInvalidValue;
-  const int64_t wgs = a.tail_split > 1 ? tiles - a.tail_tiles + a.tail_tiles * a.tail_split : tiles;
+  if (a.tail_split == -1 && (!a.wide || a.tail_n0 % (wide::NCB * kBlockCols) != 0))
+    return hipErrorInvalidValue;
+  int64_t wgs = tiles;
+  if (a.tail_split > 1) wgs = tiles - a.tail_tiles + a.tail_tiles * a.tail_split;
+  if (a.tail_split == -1)  // the tail's channels as 256 x 128 half tiles
+    wgs = tiles - a.tail_tiles +
+          ((a.M + BM - 1) / BM) * ((a.N / kBlockCols - a.tail_n0 / kBlockCols + NCB - 1) / NCB);
   const dim3 grid((unsigned)wgs, (unsigned)a.ksplit);
   if (a.wide) {
     if (a.partials)

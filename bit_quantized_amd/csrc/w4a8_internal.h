@@ -212,7 +212,8 @@ struct GemmArgs {
   bool w8;                // W8A8 weights (codes [N/16][G][2][1024], scales [N]); partials
                           // are then the int32 totals [m_end-m_begin][N]
   // prefill: the last tail_tiles tiles (channels >= tail_n0) each run as
-  // tail_split K slices into workspace [tail_split][M][N - tail_n0]
+  // tail_split K slices into workspace [tail_split][M][N - tail_n0]; or, with
+  // tail_split == -1 (256 x 256 tiles), as 256 x 128 half tiles
   int tail_split = 0;
   int64_t tail_tiles = 0, tail_n0 = 0;
   // prefill (W4A8): 256 x 256 output tiles instead of 256 x 128
@@ -249,7 +250,9 @@ int prefill_ksplit(int64_t M, int64_t N, int64_t K, int tile);
 // Prefill grid beyond prefill_ksplit: when the tiles fill R whole rounds of
 // the compute units plus a partial one, the partial round's tiles (rounded up
 // to whole column tiles) run as `split` K slices each, so the last round is
-// 1/split as long.  split 0: no tail split.
+// 1/split as long.  split 0: no tail split.  split -1 (256 x 256 tiles
+// only): the partial round's channels (from n0) run as 256 x 128 half tiles
+// over all of K instead, in the same launch.
 struct PrefillTail {
   int split;
   int64_t tiles, n0;

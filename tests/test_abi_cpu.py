@@ -285,9 +285,11 @@ def test_prefill_workspace_plans(lib):
       18944 has 296 tiles (one round and 40), 6 slices of 512 x 2560.
     - W4A16 tiles hold 128 tokens: M = 2048 there has 2368 tiles (9 rounds
       and 64), 4 slices of 2048 x 512.
-    - W4A8 at M = 2048 takes 256 x 256 tiles (592: two rounds and 80, 3
-      slices of 2048 x 2560); its 256 x 128 tiles (1184: four rounds and
-      160) would need none, and W8A8 keeps those.
+    - W4A8 at M = 2048 takes 256 x 256 tiles (592: two rounds and 80); the
+      partial round's channels run as 160 half tiles of 256 x 128 over all of
+      K, so nothing goes through the workspace; its 256 x 128 tiles (1184:
+      four rounds and 160, too many to split) would need none either, and
+      W8A8 keeps those.
     - Whole rounds need no workspace; nor do rows that run as several chunks
       (M * K >= 2^31).  The W4A8 size is the larger of the two tile widths'
       plans (the debug entry point can force either)."""
@@ -295,7 +297,7 @@ def test_prefill_workspace_plans(lib):
     assert lib.w4a8_gemm_workspace_bytes(512, 18944, 3584, 128) == slices
     assert lib.w8a8_gemm_workspace_bytes(512, 18944, 3584) == slices
     assert lib.w4a16_linear_workspace_bytes(2048, 18944, 3584, 128) == 4 * 2048 * 512 * 4
-    assert lib.w4a8_gemm_workspace_bytes(2048, 18944, 3584, 128) == 3 * 2048 * 2560 * 4
+    assert lib.w4a8_gemm_workspace_bytes(2048, 18944, 3584, 128) == 0
     assert lib.w8a8_gemm_workspace_bytes(2048, 18944, 3584) == 0
     assert lib.w4a8_gemm_workspace_bytes(1024, 32768, 3584, 128) == 0      # 4 x 256 tiles
     assert lib.w4a8_gemm_workspace_bytes(1 << 24, 16, 128, 128) == 0       # row chunks
