@@ -22,9 +22,9 @@ kernel's launches alone (back to back, as rocprofv3 sees them).
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -761,7 +761,6 @@ def bench_peaks(torch, w4):
 def source_digest():
     """sha256 over the library sources and headers (names and bytes, sorted),
     so a result can be tied to the code it ran."""
-    import glob
     import hashlib
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "bit_quantized_amd", "csrc", "*")) +
@@ -779,6 +778,27 @@ def _read(path):
         return None
 
 
+def dpm_clocks(torch):
+    """Current engine (sclk) and memory (mclk) clock levels of this GPU, read
+    from the driver's sysfs tables (the starred line of pp_dpm_*), or None."""
+    try:
+        props = torch.cuda.get_device_properties(0)
+        bdf = f"{props.pci_bus_id:02x}:{props.pci_device_id:02x}."
+    except Exception:
+        return None
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        if bdf not in os.path.basename(os.path.realpath(card)):
+            continue
+        for clk in ("sclk", "mclk"):
+            table = _read(f"{card}/pp_dpm_{clk}") or ""
+            cur = [ln.strip() for ln in table.splitlines() if ln.rstrip().endswith("*")]
+            if cur:
+                out[clk] = cur[0]
+        break
+    return out or None
+
+
 def gpu_info(torch):
     info = {"device": torch.cuda.get_device_name(0)}
     try:
@@ -787,11 +807,6 @@ def gpu_info(torch):
         info["cus"] = props.multi_processor_count
     except Exception:
         pass
-    try:
-        info["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
-                                     capture_output=True, text=True).stdout.strip() or None
-    except Exception:
-        info["git"] = None
     info["source_sha256"] = source_digest()
     info["rocm"] = _read("/opt/rocm/.info/version")
     info["torch"] = torch.__version__
@@ -805,12 +820,7 @@ def gpu_info(torch):
     info["abi_version"] = lib.w4a8_abi_version()
     info["layout_version"] = lib.w4a8_layout_version()
     info["w8a8_layout_version"] = lib.w8a8_layout_version()
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        info["clocks"] = [ln.strip() for ln in r.stdout.splitlines()
-                          if "clk" in ln.lower() and "level" in ln.lower()][:8] or None
-    except Exception:
-        info["clocks"] = None
+    info["clocks"] = dpm_clocks(torch)
     info["flags"] = {"env": {k: os.environ[k] for k in ("HIP_VISIBLE_DEVICES", "GPU_MAX_HW_QUEUES",
                                                          "OMP_NUM_THREADS") if k in os.environ}}
     return info
