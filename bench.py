@@ -687,6 +687,39 @@ def cpu_baseline_prefill(res, seconds):
             "sample": f"quant of all {M} rows + outputs of {rows} rows in {el:.1f} s"}
 
 
+def cpu_single_thread(runs=10):
+    """The oracle on one thread for the tiny, decode and small-batch
+    workloads (quantise + every output), median wall time over `runs` calls,
+    with the host's CPU model."""
+    import oracle
+    from bit_quantized_amd import synth
+    threads = oracle.threads()
+    oracle.set_threads(1)
+    out = []
+    try:
+        for spec in (synth.TINY, synth.DECODE_UP, synth.SKINNY_DOWN_4, synth.SKINNY_DOWN_16):
+            lin = synth.make_linear(spec)
+            times = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                qa, sa = oracle.quant_act(lin["x"])
+                oracle.linear(qa, sa, lin["q"], lin["z"], lin["s"])
+                times.append(time.perf_counter() - t0)
+            ms = float(np.median(times)) * 1e3
+            act = 4 if spec.act == "f32" else 2
+            nbytes = algorithmic_bytes(spec.M, spec.N, spec.K, act_bytes=act)
+            out.append({"workload": f"{spec.name} M={spec.M} K={spec.K} N={spec.N}",
+                        "runs": runs, "median_ms": round(ms, 3),
+                        "GBps": round(nbytes / (ms * 1e-3) / 1e9, 3),
+                        "GOPS": round(2.0 * spec.M * spec.N * spec.K / (ms * 1e-3) / 1e9, 3)})
+    finally:
+        oracle.set_threads(threads)
+    cpu = _read("/proc/cpuinfo") or ""
+    model = next((ln.split(":", 1)[1].strip() for ln in cpu.splitlines()
+                  if ln.startswith("model name")), None)
+    return {"cores": 1, "kind": "oracle", "cpu_model": model, "timings": out}
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, for scaling hardware byte counters."""
     n = 256 << 20
@@ -866,6 +899,8 @@ def main():
             cpu_dec = cpu_baseline_decode(dec, args.cpu_seconds)
         if pre:
             cpu_pre = cpu_baseline_prefill(pre, max(2.0, args.cpu_seconds / 3))
+        if cpu_dec:
+            cpu_dec["single_thread"] = cpu_single_thread()
 
     from bit_quantized_amd import synth
     if peaks:

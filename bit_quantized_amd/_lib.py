@@ -13,7 +13,9 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libw4a8.so")
+# W4A8_LIB_PATH selects another build of the same library (the host
+# AddressSanitizer build of the CPU-side checks); unset, the in-tree one.
+LIB_PATH = os.environ.get("W4A8_LIB_PATH") or os.path.join(_PKG, "libw4a8.so")
 
 OK = 0
 ERR_INVALID_ARG = -1

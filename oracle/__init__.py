@@ -57,6 +57,8 @@ def load(mutant: int = 0) -> ctypes.CDLL:
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     lib.oracle_version.restype = ctypes.c_int
     lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = ctypes.c_int
     for name, args in {
         "oracle_quant_act_f32": [vp, i64, i64, vp, vp],
         "oracle_quant_act_bf16": [vp, i64, i64, vp, vp],
@@ -250,6 +252,12 @@ def w4a16_linear(x, q, z, s, group=128, rows=None, cols=None, mutant: int = 0):
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run the oracle's later calls on n OpenMP threads (timing only)."""
+    if load().oracle_set_threads(int(n)) != 0:
+        raise ValueError(f"oracle: cannot run on {n} threads")
 
 
 def layout_bytes(N: int, K: int) -> int:

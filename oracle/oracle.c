@@ -64,8 +64,15 @@ int oracle_version(void) { return 1 + 100 * ORACLE_MUTANT; }
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_threads(void) { return omp_get_max_threads(); }
+/* Sets the threads of later calls (n >= 1), for single-threaded timings. */
+int oracle_set_threads(int n) {
+  if (n < 1) return 1;
+  omp_set_num_threads(n);
+  return 0;
+}
 #else
 int oracle_threads(void) { return 1; }
+int oracle_set_threads(int n) { return n == 1 ? 0 : 1; }
 #endif
 
 static float widen_bf16(uint16_t b) {
