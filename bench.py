@@ -206,9 +206,10 @@ def parity_check(w4, lin, x, W, rows=None, cols=None, windows=None):
 
 def layer_windows(M, N):
     """Parity windows for the layer legs: the first row and (M > 1) a middle
-    row from the second row tile, each over the first and the last 64
-    columns (the last column tiles are the ones a tail split slices)."""
-    rows = [(0, 1)] + ([(M // 2, M // 2 + 1)] if M > 1 else [])
+    row from the second row tile and the last row, each over the first and
+    the last 64 columns (the last column tiles are the ones a tail split or
+    the half tiles take)."""
+    rows = [(0, 1)] + ([(M // 2, M // 2 + 1), (M - 1, M)] if M > 1 else [])
     return [(r, c) for r in rows for c in ((0, 64), (N - 64, N))]
 
 
