@@ -20,6 +20,16 @@
 namespace w4a8 {
 namespace {
 
+// Each group's first MFMA starts from kBiasBits in every lane instead of
+// zero, so its int32 result is 0x4B400000 + P.  Read as a float those bits
+// are exactly 1.5 * 2^23 + P whenever |P| < 2^22 (a group product is at most
+// 128 * 127 * 15 < 2^18 in magnitude), and one float subtraction returns P
+// exactly: the same value as an int -> float conversion, from an instruction
+// that issues faster beside the matrix core.
+constexpr int kBiasBits = 0x4B400000;
+constexpr v4i kBiasSeed = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
+__device__ __forceinline__ float unbias(int r) { return __int_as_float(r) - 12582912.0f; }
+
 constexpr int kThreads = 512;           // 8 wavefronts, 2 per SIMD
 constexpr int BM = 256;                 // tokens per tile
 constexpr int BN = 128;                 // output channels per tile
@@ -187,8 +197,7 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
   for (int t = 0; t < 18; ++t) {
     if (t < 16) {
       const int i = t >> 2, u = t & 3;
-      const v4i zero = {0, 0, 0, 0};
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], kBiasSeed, 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
     }
     if (t >= 2) {
@@ -199,11 +208,11 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
         for (int r = 0; r < 4; ++r) {
           const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
           if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
-            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
+            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r] - kBiasBits;
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
+      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * unbias(acc[e][r]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -548,8 +557,7 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
       if (next && t == T / 2) store_block(next, st, zshift, 0);
       if (NU == 8 && next && t == 22) store_block(next, st, zshift, 1);
       if (next && t == T - 4) store_scale<NU>(next, st);
-      const v4i zero = {0, 0, 0, 0};
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], kBiasSeed, 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
     }
     if (t >= 2) {
@@ -560,11 +568,11 @@ __device__ __forceinline__ void compute_group(const GemmArgs& a, const uint8_t* 
         for (int r = 0; r < 4; ++r) {
           const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
           if (nb < NB && m < a.M && m >= a.m_begin && m < a.m_end)
-            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r];
+            a.partials[((m - a.m_begin) * a.N + nb * 16 + r16) * G + g] = acc[e][r] - kBiasBits;
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * (float)acc[e][r];
+      for (int r = 0; r < 4; ++r) accf[i][u][r] += sv[u] * unbias(acc[e][r]);
       // The next MFMA pair takes its A operand through this empty statement,
       // which reads the tile just rescaled: the compiler cannot run the
       // pairs ahead of the rescales (which would keep every tile's int32
