@@ -379,8 +379,7 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       b0[t] = (int)sub_zero_bytes(d & 0x0F0F0F0Fu, zz);
       b1[t] = (int)sub_zero_bytes((d >> 4) & 0x0F0F0F0Fu, zz);
     }
-    v4i acc = {0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, acc, 0, 0, 0);
+    v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, kBiasSeed, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, acc, 0, 0, 0);
     const int r = 4 * q + i;
     if (DEBUG && a.partials && r < nrun) {
@@ -388,11 +387,11 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       for (int t = 0; t < 4; ++t) {
         const int64_t m = 4 * j + t;
         if (m < a.M && m >= a.m_begin && m < a.m_end)
-          a.partials[((m - a.m_begin) * a.N + 16 * nb + r16) * G + (gb + r)] = acc[t];
+          a.partials[((m - a.m_begin) * a.N + 16 * nb + r16) * G + (gb + r)] = acc[t] - kBiasBits;
       }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) accf[t] += s * (float)acc[t];
+    for (int t = 0; t < 4; ++t) accf[t] += s * unbias(acc[t]);
   };
 
   // the first quad's loads (fused: after every wavefront has its

@@ -20,16 +20,6 @@
 namespace w4a8 {
 namespace {
 
-// Each group's first MFMA starts from kBiasBits in every lane instead of
-// zero, so its int32 result is 0x4B400000 + P.  Read as a float those bits
-// are exactly 1.5 * 2^23 + P whenever |P| < 2^22 (a group product is at most
-// 128 * 127 * 15 < 2^18 in magnitude), and one float subtraction returns P
-// exactly: the same value as an int -> float conversion, from an instruction
-// that issues faster beside the matrix core.
-constexpr int kBiasBits = 0x4B400000;
-constexpr v4i kBiasSeed = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
-__device__ __forceinline__ float unbias(int r) { return __int_as_float(r) - 12582912.0f; }
-
 constexpr int kThreads = 512;           // 8 wavefronts, 2 per SIMD
 constexpr int BM = 256;                 // tokens per tile
 constexpr int BN = 128;                 // output channels per tile
