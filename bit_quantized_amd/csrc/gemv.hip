@@ -14,7 +14,9 @@
 //     queue), take its absmax, quantise it into LDS (the rule of
 //     w4a8_quant_act bit for bit, ties to even) with per-quarter code sums added by
 //     integer LDS atomics (exact, so order-free), and raise an LDS flag; they
-//     synchronise among themselves through LDS counters;
+//     synchronise among themselves through LDS counters, and stream their
+//     own (shorter) runs once every quantiser has raised the flag, since a
+//     run reads codes and sums that all of them wrote;
 //   - the other wavefronts put D code blocks of their runs in flight at once,
 //     wait for the flag, and stream.
 // Both waits on the LDS counters are unbounded spins (with s_sleep): they end
@@ -156,6 +158,19 @@ __device__ __forceinline__ float chunk_value(const uint4* r, int e) {
   }
 }
 
+// The flag: every wavefront of the workgroup (streamers, and quantisers or
+// stagers once their own share is written) waits until all kQ quantisers or
+// stagers have made their one increment of s_sync[2], which releases their
+// LDS writes (codes, code sums, staged token).  An unbounded spin with
+// s_sleep: it ends because each of the kQ wavefronts reaches its increment
+// exactly once, on a path with no branch around it and no wait before it
+// other than the quantisers' row-maximum wait, which ends the same way.
+__device__ __forceinline__ void wait_flag(uint32_t* s_sync) {
+  while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+         (unsigned)kQ)
+    __builtin_amdgcn_s_sleep(1);
+}
+
 // kQChunks: token chunks (8 elements) a quantiser thread holds at once; the
 // whole token fits in one batch when K / 8 <= 256 * kQChunks.
 // The operands the first loads need lead the argument list as scalars, so
@@ -280,12 +295,15 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     scale = 1.0f;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
     // kQ increments: every stager reaches this line exactly once; the
-    // streamers' unbounded wait for s_sync[2] == kQ depends on it
+    // unbounded waits for s_sync[2] == kQ (wait_flag) depend on it
     if (lane == 0)
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
     for (int i = 0; i < D; ++i)
       load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    // this stager's run reads the token and sums the others staged: the
+    // streamers' wait (below), which ends after the kQ increments
+    wait_flag(s_sync);
   } else if (wave < kQ) {
     // ---- quantiser: token chunks (8 elements) qt, qt + 256, ... in batches
     // of kQChunks (the first batch is in flight already); the last batch
@@ -376,21 +394,22 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     if (a.sa_ws && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.sa_ws[0] = scale;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wavefront's LDS writes done (lgkmcnt(0))
     // kQ increments: every quantiser reaches this line exactly once; the
-    // streamers' unbounded wait for s_sync[2] == kQ depends on it
+    // unbounded waits for s_sync[2] == kQ (wait_flag) depend on it
     if (lane == 0)
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // then the quantiser streams its own (shorter) run
+    // then the quantiser streams its own (shorter) run, which reads codes
+    // and sums the other quantisers wrote: it waits for them as the
+    // streamers do (below), once its loads are in flight
 #pragma unroll
     for (int i = 0; i < D; ++i)
       load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    wait_flag(s_sync);
   } else {
     // ---- streamer: metadata and D code blocks are in flight; the flag
     // (an unbounded spin that ends once all kQ quantisers or stagers have
     // made their one increment of s_sync[2])
     if constexpr (XT == X_QUANTISED) scale = a.sa[0];
-    while (__hip_atomic_load(&s_sync[2], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
-           (unsigned)kQ)
-      __builtin_amdgcn_s_sleep(1);
+    wait_flag(s_sync);
     if constexpr (A16)
       scale = 1.0f;
     else if constexpr (XT != X_QUANTISED)
@@ -475,7 +494,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           const uint32_t d[4] = {wv[i][0].x, wv[i][0].y, wv[i][0].z, wv[i][0].w};
           const uint32_t l4[4] = {al.x, al.y, al.z, al.w};
           const uint32_t h4[4] = {ah.x, ah.y, ah.z, ah.w};
-          int acc = 0;
+          int acc = kBiasBits;  // read back as a float by unbias below
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             acc = __builtin_amdgcn_sdot4((int)(d[w] & 0x0F0F0F0Fu), (int)l4[w], acc, false);
@@ -484,14 +503,15 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           }
           const uint32_t zbyte = reinterpret_cast<const uint8_t*>(&s_zero[wave][r])[c >> 1];
           const int z = (int)((zbyte >> zshift) & 0xFu);
-          const int p = acc - z * rs[4 * g + j];
+          const int pb = acc - z * rs[4 * g + j];  // kBiasBits + the quarter's product
           if (DEBUG) {
+            const int p = pb - kBiasBits;
             int pg = p + __shfl_xor(p, 16);
             pg += __shfl_xor(pg, 32);
             if (j == 0 && a.partials && a.m_begin == 0 && a.m_end > 0)
               a.partials[((int64_t)16 * (nb0 + ccb) + c) * G + g] = pg;
           }
-          accf += s_scale[wave][r][c] * (float)p;
+          accf += s_scale[wave][r][c] * unbias(pb);
           }
           ++cg;
           const int wrap = (cg == gk) ? 1 : 0;

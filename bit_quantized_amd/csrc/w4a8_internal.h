@@ -37,12 +37,12 @@ inline int64_t w8_packed_bytes(int64_t N, int64_t K) { return w8_scales_offset(N
 
 // ---------------------------------------------------------------- device helpers
 
-// A group's first MFMA starts from kBiasBits in every lane instead of zero,
-// so its int32 result is 0x4B400000 + P.  Read as a float those bits are
-// exactly 1.5 * 2^23 + P whenever |P| < 2^22 (a group product is at most
-// 128 * 127 * 15 < 2^18 in magnitude), and one float subtraction returns P
-// exactly: the same value as an int -> float conversion, from an instruction
-// that issues faster beside the matrix core.
+// An integer product chain that starts from kBiasBits instead of zero (a
+// group's first MFMA, or a chain of v_dot4) ends at 0x4B400000 + P.  Read as
+// a float those bits are exactly 1.5 * 2^23 + P whenever |P| < 2^22 (a
+// group product is at most 128 * 127 * 15 < 2^18 in magnitude), and one
+// float subtraction returns P exactly: the same value as an int -> float
+// conversion, from an instruction that issues at a higher rate.
 constexpr int kBiasBits = 0x4B400000;
 constexpr v4i kBiasSeed = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
 __device__ __forceinline__ float unbias(int r) { return __int_as_float(r) - 12582912.0f; }

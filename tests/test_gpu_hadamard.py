@@ -113,3 +113,29 @@ def test_hadamard_linear(w4, spec):
     ref = oracle.linear(qa_ref, sa_ref, lin["q"], lin["z"], lin["s"], rows=(0, m1))
     ok, err, bound = oracle.tolerance_ok(y.float().cpu().numpy()[:m1], ref, REL)
     assert ok, f"max|y - y_ref| = {err:.3e} > {bound:.3e}"
+
+
+# The M = 1 GEMV quantises (or stages) the token in several batches when K is
+# large, and its quantiser wavefronts then stream runs that read codes and
+# sums the other quantisers wrote: every one of them must wait for all.  The
+# fused step is repeated and compared bit for bit with quantise + GEMM (and,
+# for W4A16, with its own first result), so a wavefront that ran ahead would
+# show as a mismatch.
+@pytest.mark.parametrize("act,had", [("f32", True), ("f32", False), ("bf16_outliers", True),
+                                     ("bf16_outliers", False)])
+def test_gemv_multibatch_token_repeat(w4, act, had):
+    say(f"gemv multibatch token act={act} hadamard={had}")
+    spec = synth.LinearSpec(f"gemv_mb_{act}", 1, 32768, 512, seed=131, act=act)
+    lin = synth.make_linear(spec)
+    W = w4.pack_weights(dev(lin["q"]), dev(lin["z"]), dev(lin["s"]))
+    x = x_tensor(lin["x"])
+    quant = w4.quant_act_hadamard if had else w4.quant_act
+    linear = w4.linear_hadamard if had else w4.linear
+    qa, sa = quant(x)
+    ref = w4.gemm(qa, sa, W)
+    for i in range(12):
+        assert torch.equal(linear(x, W), ref), f"repeat {i}"
+    if not had and act == "bf16_outliers":  # (W4A16 takes bf16 activations)
+        first = w4.w4a16_linear(x, W)
+        for i in range(12):
+            assert torch.equal(w4.w4a16_linear(x, W), first), f"w4a16 repeat {i}"
