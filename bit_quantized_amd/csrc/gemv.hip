@@ -181,7 +181,10 @@ __device__ __forceinline__ void wait_flag(uint32_t* s_sync) {
 // W8: the W8A8 weights (two 1 KiB halves per unit, already in operand order;
 // one scale per channel in `scales`, no zero points): raw int8 dots, int32
 // totals over the run, the scales applied once in the epilogue.
-template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false, bool HAD = false>
+// EARLY: the streamers' first code blocks go out beside the token's
+// requests instead of after the set-up barrier (chosen on the host).
+template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false, bool HAD = false,
+          bool EARLY = false>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint8_t* __restrict__ zeros, const void* __restrict__ xin, int K, int cb_q,
@@ -254,6 +257,9 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   if (wave < kQ) {
 #pragma unroll
     for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(xin, min(i * kQThreads + tid, nch - 1), xr[i]);
+  } else if constexpr (EARLY) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
 
@@ -262,11 +268,10 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
   if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
-  // the streamers' first D code blocks only now, so that every quantiser's
-  // token requests are ahead of them in this compute unit's memory queue
-  // (the token is on every wavefront's critical path; measured: K = 18944
-  // 10.9 -> 10.1 us, K = 3584 -> N = 152064 47.1 -> 45.4 us)
-  if (wave >= kQ) {
+  // otherwise the streamers' first D code blocks only now, so that every
+  // quantiser's token requests are ahead of them in this compute unit's
+  // memory queue (the token is on every wavefront's critical path)
+  if (!EARLY && wave >= kQ) {
 #pragma unroll
     for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   }
@@ -588,10 +593,26 @@ hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
     }
   }
   if (a.hadamard) return hipErrorInvalidValue;
-  if (a.partials)
+  if (a.partials) {
     hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st, a.w.codes,
                        a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
-  else
+    return hipGetLastError();
+  }
+  if constexpr (!KSPLIT) {
+    // One round of workgroups with long runs over a short token: the token's
+    // round trip does not shorten when its requests go first, and the weight
+    // stream then starts later (MI355X, K = 3584 -> N = 18944: 8.06 us early
+    // against 8.31).  Elsewhere the token goes first (K = 18944 -> N = 3584:
+    // 10.1 against 10.9 us; K = 3584 -> N = 3584 5.1 against 5.5 us;
+    // N = 152064, eight rounds: 45.4 against 48.3 us).
+    const int64_t NB = a.N / kBlockCols;
+    const int64_t units = (NB + a.cb - 1) / a.cb * G;
+    if ((int64_t)a.cb <= device_cus() && a.K <= 8192 && units >= 64) {
+      hipLaunchKernelGGL((gemv_kernel<XT, false, false, QC, W8, false, true>), grid, dim3(kThreads),
+                         lds, st, a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
+      return hipGetLastError();
+    }
+  }
     hipLaunchKernelGGL((gemv_kernel<XT, false, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st,
                        a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
   return hipGetLastError();
