@@ -878,8 +878,6 @@ def main():
         return
 
     dec = pre = skinny = layer = w8 = had = a16 = peaks = None
-    if args.only in ("all", "peaks"):
-        peaks = bench_peaks(torch, w4)
     if args.only in ("all", "decode"):
         dec = bench_decode(torch, w4, args)
     if args.only in ("all", "prefill") and not args.no_prefill:
@@ -894,6 +892,11 @@ def main():
         had = bench_hadamard(torch, w4, args)
     if args.only == "w4a16" or (args.only == "all" and not args.no_extra):
         a16 = bench_w4a16(torch, w4, args)
+    # the peak probes last: their int8 MFMA chains run the matrix cores at
+    # full power, and the memory-bound decode step measured about 3 % slower
+    # right after them
+    if args.only in ("all", "peaks"):
+        peaks = bench_peaks(torch, w4)
     cpu_dec = cpu_pre = None
     if not args.no_cpu_baseline and args.only == "all":
         if dec:
