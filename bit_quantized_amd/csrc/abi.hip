@@ -477,16 +477,18 @@ int pick_w8_path(int64_t M, int64_t N, int64_t K) {
 
 int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
-  return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K) : prefill_ksplit(M, N, K, kTile256x128);
+  return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K)
+                                  : prefill_ksplit(M, N, K, prefill_auto_tile(M, N, K));
 }
 
 // int32 split-K partials [ksplit][M][N], then (GEMV only) one 256-byte slot
-// for the scale the fused quantiser computes.
+// for the scale the fused quantiser computes.  The prefill takes the same
+// tile width as W4A8 (256 x 256 when those tiles fill a round).
 size_t w8_workspace_for(int path, int64_t M, int64_t N, int64_t K) {
   const int ks = w8_ksplit(path, M, N, K);
   if (ks <= 1)
     return path == W4A8_PATH_PREFILL
-               ? tail_workspace(prefill_tail_for(M, N, K, kTile256x128), M, N)
+               ? tail_workspace(prefill_tail_for(M, N, K, prefill_auto_tile(M, N, K)), M, N)
                : 0;
   return round256((size_t)ks * (size_t)M * (size_t)N * 4) + (path == W4A8_PATH_GEMV ? 256 : 0);
 }
@@ -608,8 +610,9 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   if (path == W4A8_PATH_PREFILL) {
     // row chunks, as for W4A8; the totals of the debug window per chunk
     const int64_t rows = prefill_chunk_rows(K, 1);
-    const PrefillTail tail =
-        ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K, kTile256x128);
+    const int tile = prefill_auto_tile(M, N, K);
+    a.wide = tile == kTile256x256;
+    const PrefillTail tail = ks > 1 ? PrefillTail{0, 0, 0} : prefill_tail_for(M, N, K, tile);
     a.tail_split = tail.split;
     a.tail_tiles = tail.tiles;
     a.tail_n0 = tail.n0;

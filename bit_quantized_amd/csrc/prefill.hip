@@ -673,11 +673,149 @@ __device__ __forceinline__ void tile(const GemmArgs& a, uint8_t (&smem)[2][kBufB
   }
 }
 
+// W8A8 on the same tiles: the weights ([N/16][G][2][1 KiB], already MFMA
+// operands) go straight into LDS like the activations, each group's MFMA
+// pairs accumulate into int32 totals over the tile's K range, and the
+// per-channel scales apply once at the end.  With no unpack and no
+// per-group rescale the loop is matrix-core and LDS work only.
+template <int NU>
+__device__ __forceinline__ void compute_group_w8(const uint8_t* buf, int (&tot)[4][NU][4]) {
+  constexpr int T = 4 * NU;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  v4i a0[4], a1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // rows wm*64 + 16i + r16: the swizzle is r16 % 8
+    const uint8_t* arow = buf + kAOff + (wm * 64 + i * 16 + r16) * kGroup;
+    a0[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, j));
+    a1[i] = *reinterpret_cast<const v4i*>(arow + 16 * a_chunk(r16, 4 + j));
+  }
+  v4i b0[NU], b1[NU];
+  auto load_b = [&](int u) __attribute__((always_inline)) {
+    const int cb = wn * NU + u;
+    b0[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 0) * kBlockBytes + lane * 16);
+    b1[u] = *reinterpret_cast<const v4i*>(buf + kBOff + (cb * 2 + 1) * kBlockBytes + lane * 16);
+  };
+  load_b(0);
+  // as for W4A8: each tile's pair from zero, then added into the int32
+  // totals two tiles later (an MFMA accumulating into a total that lives
+  // across the loop was given a fresh register every time and spilled)
+  v4i acc[T];
+#pragma unroll
+  for (int t = 0; t < T + 2; ++t) {
+    if (t < T) {
+      const int u = t >> 2, i = t & 3;
+      if (i == 0 && u + 1 < NU) load_b(u + 1);  // one column tile ahead
+      const v4i zero = {0, 0, 0, 0};
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[i], b0[u], zero, 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[i], b1[u], acc[t], 0, 0, 0);
+    }
+    if (t >= 2) {
+      const int e = t - 2, u = e >> 2, i = e & 3;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot[i][u][r] += acc[e][r];
+      if (t + 1 < T) {  // keeps the pairs and the adds interleaved, as for W4A8
+        const int in = (t + 1) & 3;
+        asm volatile("" : "+v"(a0[in]) : "v"(tot[i][u][0]), "v"(tot[i][u][1]), "v"(tot[i][u][2]),
+                     "v"(tot[i][u][3]));
+      }
+    }
+  }
+}
+
+// One W8A8 tile, as tile() for W4A8: with `split`, this K slice's int32
+// totals go to the workspace (rows of ldw channels from wn0).
+template <bool DEBUG, int NU>
+__device__ __forceinline__ void tile_w8(const GemmArgs& a, uint8_t (&smem)[2][kBufBytes], int64_t m0,
+                                        int64_t cb0, int64_t gb, int64_t ge, bool split, int slice,
+                                        int64_t wn0) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave & 3, wn = wave >> 2;
+  const int r16 = lane & 15, j = lane >> 4;
+  const int64_t G = a.K / kGroup;
+  const int64_t NB = a.N / kBlockCols;
+  const int64_t ldw = a.N - wn0;
+
+  int tot[4][NU][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tot[i][u][r] = 0;
+
+  const Offsets off = make_offsets<NU>(a, m0, cb0, NB, G);
+  // weight block wave + 8k of the tile, both halves, lane 16 B
+  uint32_t ob[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    ob[k] = (uint32_t)(min(cb0 + wave + 8 * k, NB - 1) * G * 2 * kBlockBytes + lane * 16);
+  const __amdgpu_buffer_rsrc_t rqa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.qa), (short)0, (int)(a.M * a.K),
+                                        kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rcw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w.codes), (short)0, (int)(a.N * a.K), kBufferWord3);
+#define WIDE_W8_DMA(B, g)                                                                     \
+  do {                                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < kADma; ++i_)                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                               \
+          rqa, &smem[B][kAOff + (kADma * wave + i_) * 1024], 16, off.a[i_],                   \
+          (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * kGroup)), 0, 0);               \
+    _Pragma("unroll") for (int k_ = 0; k_ < NU / 4; ++k_)                                    \
+      _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_)                                       \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                             \
+            rcw, &smem[B][kBOff + ((wave + 8 * k_) * 2 + h_) * kBlockBytes], 16,              \
+            ob[k_] + h_ * kBlockBytes,                                                        \
+            (unsigned)__builtin_amdgcn_readfirstlane((int)((g) * 2 * kBlockBytes)), 0, 0);    \
+  } while (0)
+  WIDE_W8_DMA(0, gb);
+  __syncthreads();
+  for (int64_t g = gb; g < ge; g += 2) {
+    if (g + 1 < ge) WIDE_W8_DMA(1, g + 1);  // buffer 1 was last read before the previous barrier
+    compute_group_w8<NU>(smem[0], tot);
+    __syncthreads();
+    if (g + 1 >= ge) break;
+    if (g + 2 < ge) WIDE_W8_DMA(0, g + 2);
+    compute_group_w8<NU>(smem[1], tot);
+    __syncthreads();
+  }
+#undef WIDE_W8_DMA
+
+  float swv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) swv[u] = a.w.scales[min(cb0 + wn * NU + u, NB - 1) * 16 + r16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm * 64 + i * 16 + 4 * j + r;
+      if (m >= a.M) continue;
+      const float sam = split ? 0.0f : a.sa[m];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int64_t nb = cb0 + wn * NU + u;
+        if (nb >= NB) continue;
+        const int64_t n = nb * 16 + r16;
+        const int p = tot[i][u][r];
+        if (split) {
+          reinterpret_cast<int32_t*>(a.workspace)[((int64_t)slice * a.M + m) * ldw + n - wn0] = p;
+          continue;
+        }
+        if (DEBUG && a.partials && m >= a.m_begin && m < a.m_end)
+          a.partials[(m - a.m_begin) * a.N + n] = p;
+        if (a.y) a.y[m * a.N + n] = f32_to_bf16_rne(sam * (swv[u] * (float)p));
+      }
+    }
+}
+
 // Workgroups [0, main) take the whole tiles (XCD-aware order, tokens
 // fastest); the rest take the tail: with a.tail_split > 1, K slice r /
 // tail_tiles of whole tile main + r % tail_tiles; with a.tail_split == -1
 // (half tiles), half tile r of the channels from tail_n0 on.
-template <bool DEBUG>
+template <bool DEBUG, bool W8>
 __global__ void __launch_bounds__(kThreads)
 prefill_wide_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
@@ -691,21 +829,32 @@ prefill_wide_kernel(GemmArgs a) {
     const int64_t t = xcd_tile(blockIdx.x, main_tiles);
     const int slice = blockIdx.y, nslices = gridDim.y;
     const int64_t tm = t % tiles_m, tn = t / tiles_m;
-    tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / nslices, G * (slice + 1) / nslices,
-                   nslices > 1, slice, 0);
+    if constexpr (W8)
+      tile_w8<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / nslices, G * (slice + 1) / nslices,
+                        nslices > 1, slice, 0);
+    else
+      tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / nslices, G * (slice + 1) / nslices,
+                     nslices > 1, slice, 0);
     return;
   }
   const int64_t r = blockIdx.x - main_tiles;
   if (a.tail_split == -1) {
     const int64_t tm = r % tiles_m, tn = r / tiles_m;
-    tile<DEBUG, 4>(a, smem, tm * BM, a.tail_n0 / kBlockCols + tn * (NCB / 2), 0, G, false, 0, 0);
+    if constexpr (W8)
+      tile_w8<DEBUG, 4>(a, smem, tm * BM, a.tail_n0 / kBlockCols + tn * (NCB / 2), 0, G, false, 0, 0);
+    else
+      tile<DEBUG, 4>(a, smem, tm * BM, a.tail_n0 / kBlockCols + tn * (NCB / 2), 0, G, false, 0, 0);
     return;
   }
   const int64_t t = main_tiles + r % a.tail_tiles;
   const int slice = (int)(r / a.tail_tiles);
   const int64_t tm = t % tiles_m, tn = t / tiles_m;
-  tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / a.tail_split,
-                 G * (slice + 1) / a.tail_split, true, slice, a.tail_n0);
+  if constexpr (W8)
+    tile_w8<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / a.tail_split,
+                      G * (slice + 1) / a.tail_split, true, slice, a.tail_n0);
+  else
+    tile<DEBUG, 8>(a, smem, tm * BM, tn * NCB, G * slice / a.tail_split,
+                   G * (slice + 1) / a.tail_split, true, slice, a.tail_n0);
 }
 
 }  // namespace wide
@@ -994,7 +1143,6 @@ PrefillTail prefill_tail(int64_t M, int64_t N, int64_t K, int tile) {
 }
 
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
-  if (a.wide && a.w8) return hipErrorInvalidValue;
   const int64_t tiles = tile_count(a.M, a.N, a.wide ? kTile256x256 : kTile256x128);
   if ((a.tail_split > 1 || a.tail_split == -1) &&
       (a.ksplit != 1 || a.tail_tiles <= 0 || a.tail_tiles > tiles))
@@ -1007,11 +1155,16 @@ hipError_t launch_prefill(const GemmArgs& a, hipStream_t st) {
     wgs = tiles - a.tail_tiles +
           ((a.M + BM - 1) / BM) * ((a.N / kBlockCols - a.tail_n0 / kBlockCols + NCB - 1) / NCB);
   const dim3 grid((unsigned)wgs, (unsigned)a.ksplit);
-  if (a.wide) {
+  if (a.wide && a.w8) {
     if (a.partials)
-      hipLaunchKernelGGL((wide::prefill_wide_kernel<true>), grid, dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((wide::prefill_wide_kernel<false>), grid, dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
+  } else if (a.wide) {
+    if (a.partials)
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((wide::prefill_wide_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
   } else if (a.w8) {
     if (a.partials)
       hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
