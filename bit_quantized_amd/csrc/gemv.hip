@@ -207,6 +207,19 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int c = lane & 15, j = lane >> 4;
+  // The quantisers' (stagers') token requests go out first of all, before
+  // the run set-up below: that set-up is scalar work which the kernel's 16
+  // wavefronts issue in turn, and the token is on every wavefront's
+  // critical path.
+  const int nch = K / 8;
+  constexpr int RW = XT == X_F32 ? 2 : 1;
+  constexpr int kQThreads = 64 * kQ;
+  uint4 xr[kQChunks][RW];
+  if (wave < kQ) {
+#pragma unroll
+    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(xin, min(i * kQThreads + tid, nch - 1), xr[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // This workgroup: channel blocks [nb0, nb1) x groups [g0, g0 + gk).  The
   // host passes NB = cb_q * gridDim.x + cb_r, so no division is needed here;
   // everything up to the first loads is kept short, because those loads
@@ -243,23 +256,17 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   uint4 s4;
   uint2 z2;
   float scale;
-  const int nch = K / 8;
-  constexpr int RW = XT == X_F32 ? 2 : 1;
-  constexpr int kQThreads = 64 * kQ;
-  uint4 xr[kQChunks][RW];
-
-  // first loads: every wavefront's run metadata (two small loads) and the
-  // quantisers' token chunks
+  // then every wavefront's run metadata (two small loads) and, EARLY, the
+  // streamers' first code blocks
   if constexpr (!W8) {  // (W8: one scale per channel, read in the epilogue)
     s4 = *reinterpret_cast<const uint4*>(hot_s);
     z2 = *reinterpret_cast<const uint2*>(zeros + bz * kZeroBlockBytes);
   }
-  if (wave < kQ) {
+  if constexpr (EARLY) {
+    if (wave >= kQ) {
 #pragma unroll
-    for (int i = 0; i < kQChunks; ++i) load_chunk<XT>(xin, min(i * kQThreads + tid, nch - 1), xr[i]);
-  } else if constexpr (EARLY) {
-#pragma unroll
-    for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+      for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
 
