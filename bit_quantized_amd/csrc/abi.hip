@@ -111,10 +111,19 @@ size_t tail_workspace(const PrefillTail& t, int64_t M, int64_t N) {
   return ((size_t)t.split * (size_t)M * (size_t)(N - t.n0) * 4 + 255) / 256 * 256;
 }
 
+// Whether w4a8_linear runs 2 <= M <= 16 as one launch (the skinny kernel
+// quantising the rows itself): only where the balanced grid does not apply,
+// so that the linear and quant + w4a8_gemm run the same GEMM kernel.
+bool linear_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype) {
+  return stream_plan(M, N, K).C == 0 && skinny_fuses_quant(M, N, K, x_dtype);
+}
+
 // `tile` (PrefillTile) matters for the PREFILL path only.
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K, int tile) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
-  if (path == W4A8_PATH_SKINNY) return skinny_ksplit(M, N, K);
+  if (path == W4A8_PATH_SKINNY) {
+    return stream_plan(M, N, K).C > 0 ? 1 : skinny_ksplit(M, N, K);
+  }
   if (path == W4A8_PATH_PREFILL) return prefill_ksplit(M, N, K, tile);
   return 1;
 }
@@ -198,7 +207,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
                 "(K=%lld, N*K/2=%lld, limit %lld)",
                 (long long)K, (long long)(N * K / 2), (long long)kPrefillMaxBytes);
   if (fused && path != W4A8_PATH_GEMV &&
-      !(path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype) && !debug))
+      !(path == W4A8_PATH_SKINNY && linear_fuses_quant(M, N, K, act.x_dtype) && !debug))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
@@ -296,6 +305,8 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   }
   if (path == W4A8_PATH_GEMV)
     e = launch_gemv(a, st);
+  else if (!fused && stream_plan(M, N, K).C > 0)
+    e = launch_stream(a, st);
   else
     e = launch_skinny(a, st);
   if (e == hipSuccess && ks > 1 && y)
@@ -800,7 +811,7 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
   if (!workspace || workspace_bytes < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   // One launch when the skinny kernel can quantise these rows itself.
-  if (pick_path(M, K) == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, x_dtype))
+  if (pick_path(M, K) == W4A8_PATH_SKINNY && linear_fuses_quant(M, N, K, x_dtype))
     return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
                     W4A8_PATH_SKINNY, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false);
   // Two launches: quantise into the workspace, then the GEMM.

@@ -281,6 +281,16 @@ struct A16Plan {
 };
 A16Plan skinny_a16_plan(int64_t M, int64_t N, int64_t K);
 hipError_t launch_skinny_a16(GemmArgs a, hipStream_t st);
+// 1 <= M <= 16 on the weight-streaming grid of stream.hip (W4A8, quantised
+// activations, N / 16 >= compute units, K <= 4096): C workgroups of one
+// pass over K (S == 1), `lds` bytes of staged activations each; C == 0 where
+// the grid does not apply.
+struct StreamPlan {
+  int C, S;
+  size_t lds;
+};
+StreamPlan stream_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_stream(const GemmArgs& a, hipStream_t st);
 hipError_t launch_prefill(const GemmArgs& a, hipStream_t st);
 // W4A16 prefill (bf16 activations in GemmArgs::x): K split and launch.
 int prefill_a16_ksplit(int64_t M, int64_t N, int64_t K);

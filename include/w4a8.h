@@ -212,10 +212,12 @@ int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
  * per row with MP = M rounded up to a power of two >= 2, N large enough that
  * K is not split and small enough that its 16-channel blocks fit one round
  * of workgroups (N/16 <= the compute units; every workgroup quantises all
- * rows again); the SKINNY kernel then quantises the rows into LDS.
- * Otherwise the codes are written to the workspace and the GEMM of the
- * selected path follows (two launches).  The result is bitwise identical to
- * w4a8_quant_act followed by w4a8_gemm.
+ * rows again), and not a shape that SKINNY runs on its weight-streaming grid
+ * (N/16 >= the compute units and K <= 4096: whole 16-channel blocks per
+ * workgroup, the activations staged once per workgroup); the SKINNY kernel
+ * then quantises the rows into LDS.  Otherwise the codes are written to the
+ * workspace and the GEMM of the selected path follows (two launches).  The
+ * result is bitwise identical to w4a8_quant_act followed by w4a8_gemm.
  *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
  *   y   device bfloat16 bits [M][N]
  *   workspace  device scratch of w4a8_linear_workspace_bytes(M, N, K, group)

@@ -54,6 +54,7 @@ CASES = [
     ("gemv_split_k", 1, 18944, 512, "w4a8"),
     ("skinny_fused", 4, 3584, 2048, "w4a8"),
     ("skinny_two_launch_split_k", 16, 18944, 1024, "w4a8"),
+    ("skinny_stream_grid", 8, 3584, 18944, "w4a8"),
     ("prefill_narrow_split_k", 512, 3584, 512, "w4a8"),
     ("prefill_wide_half_tile_tail", 2048, 1024, 18944, "w4a8"),
     ("w8a8_prefill", 300, 1024, 4096, "w8a8"),

@@ -85,10 +85,12 @@ def _paths(M):
 # (M, K, N): the M buckets and tile edges with a ragged N; split K on the
 # GEMV and the M <= 16 kernel; the prefill's tail slices with a ragged last
 # column tile; a GEMV grid of several rounds; 256 x 256 tiles whose partial
-# round runs as 256 x 128 half tiles
+# round runs as 256 x 128 half tiles; the M <= 16 weight-streaming grid
+# (N / 16 >= compute units, K <= 4096) with a ragged block split
 SHAPES = [(1, 384, 208), (2, 384, 208), (5, 384, 208), (16, 384, 208), (17, 384, 208),
           (33, 384, 208), (129, 384, 208), (300, 384, 208), (1, 18944, 512), (8, 10240, 512),
-          (300, 1024, 18992), (1, 3584, 38912), (2048, 1024, 9472)]
+          (300, 1024, 18992), (1, 3584, 38912), (2048, 1024, 9472),
+          (3, 1280, 4112), (16, 4096, 9600)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES, ids=[f"M{m}_K{k}_N{n}" for m, k, n in SHAPES])

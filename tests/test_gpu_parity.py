@@ -385,6 +385,8 @@ LINEAR_SPECS = [
     synth.LinearSpec("lin_2l_m16_f32", 16, 5120, 2048, seed=73, act="f32"),
     synth.LinearSpec("lin_2l_m8_ksplit", 8, 10240, 512, seed=74),
     synth.LinearSpec("lin_2l_m16_lds", 16, 18944, 512, seed=75),
+    synth.LinearSpec("lin_stream_m4_up", 4, 3584, 18944, seed=76),
+    synth.LinearSpec("lin_stream_m11_f32", 11, 2048, 8192, seed=77, act="f32"),
 ]
 
 
