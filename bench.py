@@ -504,11 +504,13 @@ def bench_w4a16(torch, w4, args):
 
 
 def bench_skinny(torch, w4, args):
-    """Skinny decode (2 <= M <= 16): K=18944 -> N=3584, as quant + GEMM
-    through w4a8_linear, against the HBM roofline."""
+    """Skinny decode (2 <= M <= 16): K=18944 -> N=3584 (the configuration
+    named for it), then the same batches on the up projection K=3584 ->
+    N=18944 (the weight-streaming grid), as quant + GEMM through w4a8_linear,
+    against the HBM roofline."""
     from bit_quantized_amd import synth
     out = []
-    for spec in (synth.SKINNY_DOWN_4, synth.SKINNY_DOWN_16):
+    for spec in (synth.SKINNY_DOWN_4, synth.SKINNY_DOWN_16, synth.SKINNY_UP_4, synth.SKINNY_UP_16):
         lin, x, Ws = setup_linear(torch, w4, spec, args.copies)
         M, K, N = spec.M, spec.K, spec.N
         parity = parity_check(w4, lin, x, Ws[0])

@@ -161,6 +161,8 @@ void launch_typed(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipSt
     launch_rows<T, HAD, 1024>(x, M, K, qa, sa, st);
   else if (M > 64 && chunks <= 8 * 256)
     launch_rows<T, HAD, 256>(x, M, K, qa, sa, st);
+  else if (M > 64 && chunks <= 8 * 512)
+    launch_rows<T, HAD, 512>(x, M, K, qa, sa, st);
   else
     hipLaunchKernelGGL((quant_act_kernel<T, HAD>), dim3((unsigned)M), dim3(kQuantThreads), 0, st, x,
                        K, qa, sa);

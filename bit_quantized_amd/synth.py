@@ -67,6 +67,9 @@ TINY = LinearSpec("tiny", 4, 256, 256, seed=0, act="f32")
 DECODE_UP = LinearSpec("decode_up", 1, 3584, 18944, seed=1)
 SKINNY_DOWN_4 = LinearSpec("skinny_down_m4", 4, 18944, 3584, seed=2)
 SKINNY_DOWN_16 = LinearSpec("skinny_down_m16", 16, 18944, 3584, seed=2)
+# the same batches on the MLP up projection (the shape of the decode GEMV)
+SKINNY_UP_4 = LinearSpec("skinny_up_m4", 4, 3584, 18944, seed=2)
+SKINNY_UP_16 = LinearSpec("skinny_up_m16", 16, 3584, 18944, seed=2)
 PREFILL_UP = LinearSpec("prefill_up", 2048, 3584, 18944, seed=3)
 
 

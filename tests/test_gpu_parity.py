@@ -121,9 +121,10 @@ QUANT_EDGES = [(3, 8192, "bf16_outliers"), (2, 8320, "bf16_outliers"), (5, 16384
                (5, 16512, "f32"), (4, 32896, "bf16_outliers"), (1, 65536, "bf16_outliers"),
                (2, 65664, "f32"), (64, 1152, "bf16_outliers"), (65, 256, "bf16_outliers"),
                # many rows: 256 threads per row, 2, 4 and 8 chunks per thread, then
-               # the two-pass kernel past 16384 values
+               # 512 threads per row up to 32768 values, then the two-pass kernel
                (300, 3584, "bf16_outliers"), (100, 8192, "f32"), (70, 16384, "bf16_outliers"),
-               (66, 16512, "bf16_outliers")]
+               (66, 16512, "bf16_outliers"), (96, 18944, "bf16_outliers"), (65, 32768, "f32"),
+               (67, 32896, "bf16_outliers")]
 
 
 @pytest.mark.parametrize("M,K,act", QUANT_EDGES, ids=[f"M{m}_K{k}_{a[:4]}" for m, k, a in QUANT_EDGES])
