@@ -388,6 +388,8 @@ LINEAR_SPECS = [
     synth.LinearSpec("lin_2l_m16_lds", 16, 18944, 512, seed=75),
     synth.LinearSpec("lin_stream_m4_up", 4, 3584, 18944, seed=76),
     synth.LinearSpec("lin_stream_m11_f32", 11, 2048, 8192, seed=77, act="f32"),
+    # N/16 equal to the compute units: the streaming grid, not the fused route
+    synth.LinearSpec("lin_stream_m4_nb256", 4, 3584, 4096, seed=78),
 ]
 
 
