@@ -118,6 +118,25 @@ bool linear_fuses_quant(int64_t M, int64_t N, int64_t K, int x_dtype) {
   return stream_plan(M, N, K).C == 0 && skinny_fuses_quant(M, N, K, x_dtype);
 }
 
+size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Whether the two-launch linears hand the skinny kernel its codes in the
+// tiled [K / 16][16 rows][16 B] layout (12 <= M <= 16, where the row-major
+// codes cost the kernel eight lane exchanges per unit): the same codes and
+// the same GEMM arithmetic, so the output is bitwise that of quant + gemm.
+// Measured at K = 18944 -> N = 3584: 18.5 -> 16.9 us at M = 16, 16.2 ->
+// 15.9 at M = 12; slower below (15.6 -> 15.8 at M = 10), where the lanes
+// of the absent rows no longer cost their exchanges.
+bool linear_tiles_codes(int64_t M, int64_t N, int64_t K) {
+  return M >= 12 && M <= 16 && K <= 65536 && pick_path(M, K) == W4A8_PATH_SKINNY &&
+         stream_plan(M, N, K).C == 0;
+}
+
+// Bytes of the codes region of a two-launch linear's workspace.
+size_t linear_codes_bytes(int64_t M, int64_t N, int64_t K) {
+  return round256((size_t)(linear_tiles_codes(M, N, K) ? 16 : M) * K);
+}
+
 // `tile` (PrefillTile) matters for the PREFILL path only.
 int ksplit_for(int path, int64_t M, int64_t N, int64_t K, int tile) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
@@ -154,7 +173,6 @@ size_t gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
   return need;
 }
 
-size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Activations for a GEMM: either quantised (qa, sa) or raw x that the M == 1
 // GEMV quantises in its prologue.
@@ -163,6 +181,7 @@ struct ActIn {
   const float* sa;
   const void* x;
   int x_dtype;
+  bool tiled = false;  // qa in the layout of launch_quant_tiled
 };
 
 int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
@@ -209,6 +228,9 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   if (fused && path != W4A8_PATH_GEMV &&
       !(path == W4A8_PATH_SKINNY && linear_fuses_quant(M, N, K, act.x_dtype) && !debug))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
+  if (act.tiled && (fused || debug || path != W4A8_PATH_SKINNY || !linear_tiles_codes(M, N, K)))
+    return fail(W4A8_ERR_INVALID_ARG, "tiled codes are read by the 12 <= M <= 16 skinny kernel only");
+  const size_t qa_bytes = (size_t)(act.tiled ? 16 : M) * K;
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
       return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
@@ -225,7 +247,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
     return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   const size_t ybytes = (size_t)M * (size_t)N * 2;
   const size_t xbytes = (size_t)M * K * (act.x_dtype == W4A8_F32 ? 4 : 2);
-  if (y && ((!fused && (overlaps(y, ybytes, act.qa, (size_t)M * K) ||
+  if (y && ((!fused && (overlaps(y, ybytes, act.qa, qa_bytes) ||
                         overlaps(y, ybytes, act.sa, (size_t)M * 4))) ||
             (fused && overlaps(y, ybytes, act.x, xbytes)) || overlaps(y, ybytes, packed, need) ||
             (ws_need && overlaps(y, ybytes, workspace, ws_need))))
@@ -255,6 +277,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
   a.w8 = false;
   a.wide = path == W4A8_PATH_PREFILL && tile == kTile256x256;
   a.hadamard = fused && hadamard;
+  a.qa_tiled = act.tiled;
   const float* sa_for_reduce = act.sa;
   if (path == W4A8_PATH_GEMV) {
     const GemvShape gs = gemv_shape(N, K);
@@ -318,7 +341,7 @@ int run_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t
 // (qa, sa) followed by the GEMM's workspace.
 size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
   if (pick_path(M, K) == W4A8_PATH_GEMV) return workspace_for(W4A8_PATH_GEMV, M, N, K, 0);
-  return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+  return linear_codes_bytes(M, N, K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
 }
 
 // ------------------------------------------------------------------ W4A16
@@ -486,6 +509,18 @@ int pick_w8_path(int64_t M, int64_t N, int64_t K) {
   return M <= 16 ? W4A8_PATH_SKINNY : W4A8_PATH_PREFILL;
 }
 
+// w8a8_linear's two-launch route at 14 <= M <= 16 hands the M <= 16 kernel
+// the tiled codes, as the W4A8 linear does (linear_tiles_codes).  Measured
+// at K = 18944 -> N = 3584: 22.2 -> 20.9 us at M = 16, but 19.4 -> 19.7 at
+// M = 12 (the W8A8 kernel does less arithmetic per unit, so the exchanges
+// the layout saves weigh less than the absent rows' loads).
+bool w8_linear_tiles_codes(int64_t M, int64_t N, int64_t K) {
+  return M >= 14 && M <= 16 && K <= 65536 && pick_w8_path(M, N, K) == W4A8_PATH_SKINNY;
+}
+size_t w8_linear_codes_bytes(int64_t M, int64_t N, int64_t K) {
+  return round256((size_t)(w8_linear_tiles_codes(M, N, K) ? 16 : M) * K);
+}
+
 int w8_ksplit(int path, int64_t M, int64_t N, int64_t K) {
   if (path == W4A8_PATH_GEMV) return gemv_shape(N, K).ksplit;
   return path == W4A8_PATH_SKINNY ? skinny_ksplit(M, N, K)
@@ -518,7 +553,7 @@ size_t w8_gemm_workspace_any(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t w8_linear_workspace(int64_t M, int64_t N, int64_t K) {
-  return round256((size_t)M * K) + round256((size_t)M * 4) + w8_gemm_workspace_any(M, N, K);
+  return w8_linear_codes_bytes(M, N, K) + round256((size_t)M * 4) + w8_gemm_workspace_any(M, N, K);
 }
 
 int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int64_t M, int64_t N,
@@ -556,6 +591,9 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   if (fused && (debug || !(path == W4A8_PATH_GEMV ||
                             (path == W4A8_PATH_SKINNY && skinny_fuses_quant(M, N, K, act.x_dtype)))))
     return fail(W4A8_ERR_INVALID_ARG, "no in-kernel quantisation for this path and shape");
+  if (act.tiled && (fused || debug || path != W4A8_PATH_SKINNY || !w8_linear_tiles_codes(M, N, K)))
+    return fail(W4A8_ERR_INVALID_ARG, "tiled codes are read by the 14 <= M <= 16 skinny kernel only");
+  const size_t qa_bytes = (size_t)(act.tiled ? 16 : M) * K;
   if (debug) {
     if (m_begin < 0 || m_end > M || m_begin > m_end)
       return fail(W4A8_ERR_INVALID_ARG, "row window [%lld, %lld) outside [0, %lld)",
@@ -572,7 +610,7 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
     return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   const size_t ybytes = (size_t)M * (size_t)N * 2;
   const size_t xbytes = (size_t)M * K * (act.x_dtype == W4A8_F32 ? 4 : 2);
-  if (y && ((!fused && (overlaps(y, ybytes, act.qa, (size_t)M * K) ||
+  if (y && ((!fused && (overlaps(y, ybytes, act.qa, qa_bytes) ||
                         overlaps(y, ybytes, act.sa, (size_t)M * 4))) ||
             (fused && overlaps(y, ybytes, act.x, xbytes)) || overlaps(y, ybytes, packed, need) ||
             (ws_need && overlaps(y, ybytes, workspace, ws_need))))
@@ -606,6 +644,7 @@ int run_w8_gemm(const ActIn& act, const void* packed, size_t packed_bytes_, int6
   a.ksplit = ks;
   a.cb = a.ks = 0;
   a.w8 = true;
+  a.qa_tiled = act.tiled;
   const float* sa_for_reduce = act.sa;
   if (path == W4A8_PATH_GEMV) {
     const GemvShape gs = gemv_shape(N, K);
@@ -734,8 +773,9 @@ int w4a8_unpack_weights(const void* packed, size_t packed_bytes_, int64_t N, int
                        "unpack launch");
 }
 
+// tiled: qa in the layout of launch_quant_tiled (16 K bytes, M <= 16).
 static int quant_act_any(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa,
-                         float* sa, void* stream, bool hadamard) {
+                         float* sa, void* stream, bool hadamard, bool tiled = false) {
   if (!x || !qa || !sa) return fail(W4A8_ERR_INVALID_ARG, "null pointer");
   if (x_dtype != W4A8_BF16 && x_dtype != W4A8_F32)
     return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
@@ -746,13 +786,15 @@ static int quant_act_any(const void* x, int32_t x_dtype, int64_t M, int64_t K, i
   if (!aligned16(x) || !aligned16(qa) || !aligned16(sa))
     return fail(W4A8_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
   const size_t xb = (size_t)M * K * (x_dtype == W4A8_BF16 ? 2 : 4);
-  if (overlaps(qa, (size_t)M * K, x, xb) || overlaps(sa, (size_t)M * 4, x, xb) ||
-      overlaps(qa, (size_t)M * K, sa, (size_t)M * 4))
+  const size_t qb = (size_t)(tiled ? 16 : M) * K;
+  if (overlaps(qa, qb, x, xb) || overlaps(sa, (size_t)M * 4, x, xb) ||
+      overlaps(qa, qb, sa, (size_t)M * 4))
     return fail(W4A8_ERR_INVALID_ARG, "outputs alias the input or each other");
   (void)hipGetLastError();
-  return device_status(
-      launch_quant(x, x_dtype, M, K, qa, sa, static_cast<hipStream_t>(stream), hadamard),
-      "quant launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return device_status(tiled ? launch_quant_tiled(x, x_dtype, M, K, qa, sa, st, hadamard)
+                             : launch_quant(x, x_dtype, M, K, qa, sa, st, hadamard),
+                       "quant launch");
 }
 
 int w4a8_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
@@ -821,19 +863,20 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
     return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
   if (overlaps(y, (size_t)M * N * 2, x, xbytes))
     return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  const bool tiled = linear_tiles_codes(M, N, K);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qa = reinterpret_cast<int8_t*>(ws);
-  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
-  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
+  float* sa = reinterpret_cast<float*>(ws + linear_codes_bytes(M, N, K));
+  uint8_t* gws = ws + linear_codes_bytes(M, N, K) + round256((size_t)M * 4);
   // Validate the GEMM before launching the quantiser, so a rejected call
   // launches nothing.
-  rc = run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
-                0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+  rc = run_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K, group,
+                W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
                 /*validate_only=*/true);
   if (rc) return rc;
-  rc = w4a8_quant_act(x, x_dtype, M, K, qa, sa, stream);
+  rc = quant_act_any(x, x_dtype, M, K, qa, sa, stream, false, tiled);
   if (rc) return rc;
-  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group,
+  return run_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K, group,
                   W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
@@ -842,7 +885,7 @@ int w4a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
 // inverse rotation (two launches on every path).
 size_t w4a8_linear_hadamard_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (check_weight_shape(N, K, group) || M <= 0) return 0;
-  return round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+  return linear_codes_bytes(M, N, K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
 }
 
 int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed,
@@ -855,7 +898,8 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed,
     return fail(W4A8_ERR_INVALID_ARG, "unknown activation dtype %d", (int)x_dtype);
   if (M <= 0 || M > ((int64_t)1 << 24))
     return fail(W4A8_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
-  const size_t need = round256((size_t)M * K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
+  const size_t need =
+      linear_codes_bytes(M, N, K) + round256((size_t)M * 4) + gemm_workspace_any(M, N, K);
   if (!workspace || workspace_bytes < need)
     return fail(W4A8_ERR_BUFFER_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(W4A8_ERR_MISALIGNED, "workspace must be 16-byte aligned");
@@ -872,18 +916,19 @@ int w4a8_linear_hadamard(const void* x, int32_t x_dtype, const void* packed,
     return run_gemm(ActIn{nullptr, nullptr, x, x_dtype}, packed, packed_bytes_, M, N, K, group,
                     W4A8_PATH_GEMV, 0, 0, nullptr, y, workspace, workspace_bytes, stream, false,
                     false, /*hadamard=*/true);
+  const bool tiled = linear_tiles_codes(M, N, K);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qa = reinterpret_cast<int8_t*>(ws);
-  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
-  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
-  rc = run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
-                0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+  float* sa = reinterpret_cast<float*>(ws + linear_codes_bytes(M, N, K));
+  uint8_t* gws = ws + linear_codes_bytes(M, N, K) + round256((size_t)M * 4);
+  rc = run_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K, group,
+                W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
                 /*validate_only=*/true);
   if (rc) return rc;
-  rc = w4a8_quant_act_hadamard(x, x_dtype, M, K, qa, sa, stream);
+  rc = quant_act_any(x, x_dtype, M, K, qa, sa, stream, true, tiled);
   if (rc) return rc;
-  return run_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, group, W4A8_PATH_AUTO,
-                  0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
+  return run_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K, group,
+                  W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
 // ------------------------------------------------------------------ W8A8
@@ -985,18 +1030,19 @@ int w8a8_linear(const void* x, int32_t x_dtype, const void* packed, size_t packe
     return fail(W4A8_ERR_INVALID_ARG, "workspace aliases an input");
   if (overlaps(y, (size_t)M * N * 2, x, xbytes))
     return fail(W4A8_ERR_INVALID_ARG, "output aliases the activations");
+  const bool tiled = w8_linear_tiles_codes(M, N, K);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* qa = reinterpret_cast<int8_t*>(ws);
-  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * K));
-  uint8_t* gws = ws + round256((size_t)M * K) + round256((size_t)M * 4);
-  rc = run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0, 0,
-                   nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
+  float* sa = reinterpret_cast<float*>(ws + w8_linear_codes_bytes(M, N, K));
+  uint8_t* gws = ws + w8_linear_codes_bytes(M, N, K) + round256((size_t)M * 4);
+  rc = run_w8_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K,
+                   W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false,
                    /*validate_only=*/true);
   if (rc) return rc;
-  rc = w4a8_quant_act(x, x_dtype, M, K, qa, sa, stream);
+  rc = quant_act_any(x, x_dtype, M, K, qa, sa, stream, false, tiled);
   if (rc) return rc;
-  return run_w8_gemm(ActIn{qa, sa, nullptr, 0}, packed, packed_bytes_, M, N, K, W4A8_PATH_AUTO, 0,
-                     0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
+  return run_w8_gemm(ActIn{qa, sa, nullptr, 0, tiled}, packed, packed_bytes_, M, N, K,
+                     W4A8_PATH_AUTO, 0, 0, nullptr, y, gws, need - (size_t)(gws - ws), stream, false);
 }
 
 // ------------------------------------------------------------------ W4A16

@@ -13,15 +13,9 @@ namespace {
 constexpr int kThreads = 1024;  // 16 wavefronts, one workgroup per compute unit
 constexpr int kWaves = kThreads / 64;
 constexpr int D = 4;            // units a wavefront keeps in flight
-constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 descriptor format
-constexpr int kNontemporal = 2;           // cache policy bit: nt
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kBufferWord3);
-}
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -160,12 +154,21 @@ constexpr int kA16Slack = 1536;  // LDS past the staged rows that padded quads m
 // row-major bf16 rows, four 16-byte loads per lane per unit (step t's eight
 // values, exactly the MFMA layout), so the rows need no LDS and K no split.
 // Units past a wavefront's run and rows >= M read as zeros.
+//
+// TILED (MP == 16, int8 codes from the caller, no debug): qa is in the
+// [K / 16][16 rows][16 B] layout of launch_quant_tiled, so each lane's two
+// A operands of a unit are two 16-byte loads at consecutive lane addresses
+// (one contiguous KiB per wavefront), with no exchange between lanes (the
+// row-major layout needs eight ds_bpermute per unit).  Rows M..15 of the
+// layout are never written, and their lanes load nothing.  A layout with
+// whole 128-byte row lines per group ([K / 128][16 rows][128 B]) was
+// slower: its loads split into 16 pieces of 64 bytes.
 
 // The operands the first loads need also lead the argument list as scalars,
 // so that they arrive preloaded in scalar registers (kernel-argument preload)
 // rather than behind a memory round trip; they overwrite the same fields of
 // the by-value GemmArgs, which supplies everything else.
-template <bool DEBUG, int MP, int NPT, typename T, bool W8, bool A16 = false>
+template <bool DEBUG, int MP, int NPT, typename T, bool W8, bool A16 = false, bool TILED = false>
 __global__ void __launch_bounds__(kThreads)
 skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
               const uint8_t* __restrict__ zeros, const int8_t* __restrict__ qa,
@@ -189,6 +192,7 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
   constexpr int kSlotLoads = STAGE ? 0 : (DIRECT16 ? 4 : S::kSlotLoads);
   constexpr int QL = kQuadLoads > 0 ? kQuadLoads : 1;
   constexpr int SL = kSlotLoads > 0 ? kSlotLoads : 1;
+  static_assert(!TILED || (MP == 16 && NPT == 0 && !A16 && !DEBUG), "tiled codes: M <= 16 GEMM only");
   __shared__ float red[kWaves][4][64];
   __shared__ float s_wmax[kWaves];
   __shared__ float s_sa[16];
@@ -244,7 +248,8 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       W8 ? rsrc_of(a.w.scales, 0)
          : rsrc_of(a.w.zeros + blk0 * kZeroBlockBytes, (int64_t)nrun * kZeroBlockBytes);
   const __amdgpu_buffer_rsrc_t ra =
-      DIRECT16 ? rsrc_of(a.x, a.M * a.K * 2) : rsrc_of(a.qa, FUSED ? 0 : a.M * a.K);
+      DIRECT16 ? rsrc_of(a.x, a.M * a.K * 2)
+               : rsrc_of(a.qa, FUSED ? 0 : (TILED ? 16 : a.M) * a.K);
   const int oob = 0x7FFFFFF0;  // beyond every descriptor
 
   // activation row segment this lane fetches (row >= M: none)
@@ -285,6 +290,14 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       for (int t = 0; t < 4; ++t)
         act[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                              ra, o == oob ? oob : o + 128 * (t >> 1) + 16 * (t & 1), 0, 0));
+    } else if constexpr (TILED) {
+      // unit gb + u of the layout: 2 KiB, half h at + 1024 h (rows >= M
+      // read zeros, with no memory request)
+      const int o = u < nrun && r16 < a.M ? (gb + u) * 2 * kBlockBytes + 16 * lane : oob;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        act[h] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ra, o == oob ? oob : o + h * kBlockBytes, 0, 0));
     } else if constexpr (kSlotLoads > 0) {
 #pragma unroll
       for (int h = 0; h < kSlotLoads; ++h)
@@ -344,6 +357,9 @@ skinny_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scale
       const int off = lds_a + (4 * q + i) * kGroup;
       a0 = *reinterpret_cast<const v4i*>(qs + off);
       a1 = *reinterpret_cast<const v4i*>(qs + off + 64);
+    } else if constexpr (TILED) {
+      a0 = au[0];
+      a1 = au[1];
     } else if constexpr (MP == 16) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -596,6 +612,9 @@ template <int MP, bool W8>
 void launch_mp(const GemmArgs& a, dim3 grid, hipStream_t st) {
   if (a.partials)
     hipLaunchKernelGGL((skinny_kernel<true, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, SKINNY_ARGS(a));
+  else if (MP == 16 && a.qa_tiled)
+    hipLaunchKernelGGL((skinny_kernel<false, 16, 0, uint8_t, W8, false, true>), grid, dim3(kThreads), 0, st,
+                       SKINNY_ARGS(a));
   else
     hipLaunchKernelGGL((skinny_kernel<false, MP, 0, uint8_t, W8>), grid, dim3(kThreads), 0, st, SKINNY_ARGS(a));
 }
@@ -732,6 +751,7 @@ hipError_t launch_skinny(GemmArgs a, hipStream_t st) {
   dim3 grid((unsigned)(a.N / kBlockCols), (unsigned)a.ksplit);
   if (a.x && (fused_chunks(a.M, a.N, a.K, a.x_dtype) == 0 || a.ksplit != 1 || a.partials))
     return hipErrorInvalidValue;
+  if (a.qa_tiled && (a.x || a.partials || a.M <= 8 || a.M > 16)) return hipErrorInvalidValue;
   if (a.w8)
     launch_any<true>(a, grid, st);
   else

@@ -70,8 +70,6 @@ __host__ __device__ constexpr int share_prefix(int w) {
 }
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr int kBufferWord3 = 0x00020000;    // raw byte buffer, gfx9 descriptor format
-constexpr int kNontemporal = 2;             // cache policy bit: nt
 __device__ __forceinline__ uint4 ntload16(const uint8_t* p) {
   const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
   return make_uint4(t.x, t.y, t.z, t.w);

@@ -28,7 +28,6 @@ constexpr int kAOff = 0;                              // activation tile [BM][12
 constexpr int kBOff = kAOff + BM * kGroup;            // unpacked q - z, [NCB][2][64 lanes][16 B]
 constexpr int kSOff = kBOff + NCB * 2 * kBlockBytes;  // scales [NCB][16]
 constexpr int kBufBytes = kSOff + NCB * 16 * 4;
-constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 descriptor format
 constexpr int kADmaRows = 1024 / kGroup;                      // tile rows per 1 KiB load (8)
 constexpr int kADma = BM / kADmaRows / (kThreads / 64);       // such loads per wavefront (4)
 

@@ -93,31 +93,72 @@ quant_act_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   }
 }
 
-// Rows of up to 8 * THREADS * NPT activations: every thread loads its NPT
-// chunks of eight at once and keeps them in registers, so the row is read
-// once (and rotated once) and the block waits for memory once.  1024
-// threads per row serve few rows, where each block's latency is the whole
-// cost; 256 serve many rows, which fill the machine by themselves.
-template <typename T, int NPT, bool HAD, int kRowThreads>
+// Eight activations as float from their raw 16-byte loads (bf16: one
+// load, f32: two).
+template <typename T>
+struct Raw8 {
+  static constexpr int kLoads = sizeof(T) / 2;
+  static __device__ __forceinline__ void widen(const uint4* r, float* v) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+// Byte offset of the eight codes of chunk ch (input channels 8 ch ..) of
+// row m.  Row-major: m K + 8 ch.  TILED, [K / 16][16 rows][16 B] for at
+// most 16 rows: 256 (ch / 2) + 16 m + 8 (ch % 2).  A 16-byte load per lane
+// at 2048 g + 1024 h + 16 lane then gives lane 16 j + r the channels
+// 128 g + 64 h + 16 j .. + 16 of row r: the int8 MFMA's A operand for half
+// of group g, one contiguous KiB per wavefront, with no exchange between
+// lanes.
+template <bool TILED>
+__device__ __forceinline__ int64_t code_offset(int64_t m, int64_t K, int ch) {
+  if constexpr (TILED)
+    return (int64_t)(ch >> 1) * 256 + m * 16 + (ch & 1) * 8;
+  else
+    return m * K + (int64_t)ch * 8;
+}
+
+// Rows of up to 8 * THREADS * NPT activations: every thread issues its NPT
+// chunk loads back to back (through a descriptor over the row, so a chunk
+// past the row reads zeros instead of branching around its load, which
+// would make each load wait for the one before), keeps them in registers,
+// and the block waits for memory once.  1024 threads per row serve few
+// rows, where each block's latency is the whole cost; 256 serve many rows,
+// which fill the machine by themselves.
+template <typename T, int NPT, bool HAD, int kRowThreads, bool TILED>
 __global__ void __launch_bounds__(kRowThreads)
 quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
                  float* __restrict__ sa) {
   __shared__ float red[kRowThreads / 64];
+  constexpr int L = Raw8<T>::kLoads;
   const int64_t m = blockIdx.x;
-  const T* row = x + m * K;
   const int chunks = (int)(K / 8);
-  float v[NPT][8];
-  float amax = 0.0f;
+  const __amdgpu_buffer_rsrc_t rx = rsrc_of(x + m * K, K * (int64_t)sizeof(T));
+  uint4 raw[NPT][L];
 #pragma unroll
   for (int c = 0; c < NPT; ++c) {
     const int ch = threadIdx.x + c * kRowThreads;
-    if (ch < chunks) {
-      Chunk8<T>::load(row + (int64_t)ch * 8, v[c]);
-    } else {
+    const int off = ch < chunks ? ch * 8 * (int)sizeof(T) : kOob;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[c][i] = 0.0f;
-    }
+    for (int l = 0; l < L; ++l)
+      raw[c][l] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off == kOob ? kOob : off + 16 * l, 0, 0));
   }
+  __builtin_amdgcn_sched_barrier(0);  // all loads in flight before the first wait
+  float v[NPT][8];
+#pragma unroll
+  for (int c = 0; c < NPT; ++c) Raw8<T>::widen(raw[c], v[c]);
   if (HAD) {
     // whole groups are either all present or all absent (K % 128 == 0), so
     // the lanes of a group agree on every branch here
@@ -125,6 +166,7 @@ quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
     for (int c = 0; c < NPT; ++c)
       if (threadIdx.x + c * kRowThreads < chunks) hadamard_chunk(v[c]);
   }
+  float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < NPT; ++c)
 #pragma unroll
@@ -132,26 +174,26 @@ quant_row_kernel(const T* __restrict__ x, int64_t K, int8_t* __restrict__ qa,
   amax = block_max<kRowThreads>(amax, red);
   const float scale = amax / 127.0f;
   if (threadIdx.x == 0) sa[m] = scale;
-  int8_t* out = qa + m * K;
 #pragma unroll
   for (int c = 0; c < NPT; ++c) {
     const int ch = threadIdx.x + c * kRowThreads;
-    if (ch < chunks) *reinterpret_cast<uint2*>(out + (int64_t)ch * 8) = quant8(v[c], amax, scale);
+    if (ch < chunks)
+      *reinterpret_cast<uint2*>(qa + code_offset<TILED>(m, K, ch)) = quant8(v[c], amax, scale);
   }
 }
 
-template <typename T, bool HAD, int THREADS>
+template <typename T, bool HAD, int THREADS, bool TILED = false>
 void launch_rows(const T* x, int64_t M, int64_t K, int8_t* qa, float* sa, hipStream_t st) {
   const int64_t chunks = K / 8;
   const dim3 grid((unsigned)M), block(THREADS);
   if (chunks <= THREADS)
-    hipLaunchKernelGGL((quant_row_kernel<T, 1, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 1, HAD, THREADS, TILED>), grid, block, 0, st, x, K, qa, sa);
   else if (chunks <= 2 * THREADS)
-    hipLaunchKernelGGL((quant_row_kernel<T, 2, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 2, HAD, THREADS, TILED>), grid, block, 0, st, x, K, qa, sa);
   else if (chunks <= 4 * THREADS)
-    hipLaunchKernelGGL((quant_row_kernel<T, 4, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 4, HAD, THREADS, TILED>), grid, block, 0, st, x, K, qa, sa);
   else
-    hipLaunchKernelGGL((quant_row_kernel<T, 8, HAD, THREADS>), grid, block, 0, st, x, K, qa, sa);
+    hipLaunchKernelGGL((quant_row_kernel<T, 8, HAD, THREADS, TILED>), grid, block, 0, st, x, K, qa, sa);
 }
 
 template <typename T, bool HAD>
@@ -182,6 +224,25 @@ hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t
       launch_typed<float, true>(static_cast<const float*>(x), M, K, qa, sa, st);
     else
       launch_typed<float, false>(static_cast<const float*>(x), M, K, qa, sa, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tiled(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa,
+                              float* sa, hipStream_t st, bool hadamard) {
+  if (M < 1 || M > 16 || K / 8 > 8 * 1024) return hipErrorInvalidValue;
+  if (x_dtype == 0) {
+    auto p = static_cast<const uint16_t*>(x);
+    if (hadamard)
+      launch_rows<uint16_t, true, 1024, true>(p, M, K, qa, sa, st);
+    else
+      launch_rows<uint16_t, false, 1024, true>(p, M, K, qa, sa, st);
+  } else {
+    auto p = static_cast<const float*>(x);
+    if (hadamard)
+      launch_rows<float, true, 1024, true>(p, M, K, qa, sa, st);
+    else
+      launch_rows<float, false, 1024, true>(p, M, K, qa, sa, st);
   }
   return hipGetLastError();
 }

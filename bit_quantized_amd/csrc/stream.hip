@@ -41,16 +41,9 @@ constexpr int D = 4;                      // code blocks a wavefront keeps in fl
 constexpr int kMaxRun = 12;               // units per wavefront
 constexpr int kMaxGroups = 32;            // K / 128 (2 KiB of staged activations each)
 constexpr int kMaxRounds = 8;             // workgroups per compute unit, at most
-constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 descriptor format
-constexpr int kNontemporal = 2;           // cache policy bit: nt
-constexpr int kOob = 0x7FFFFFF0;          // beyond every descriptor
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kBufferWord3);
-}
 
 // The leading scalars arrive preloaded in SGPRs (kernel-argument preload).
 // N / 16 = cb_q * gridDim.x + cb_r: workgroup b takes cb_q blocks, one more

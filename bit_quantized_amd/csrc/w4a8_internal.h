@@ -37,6 +37,17 @@ inline int64_t w8_packed_bytes(int64_t N, int64_t K) { return w8_scales_offset(N
 
 // ---------------------------------------------------------------- device helpers
 
+// Raw byte-buffer descriptors: a load at an offset past `bytes` returns
+// zeros and issues no memory request, so a bounds check becomes an offset
+// (kOob lies beyond every descriptor) instead of a branch around the load.
+constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 descriptor format
+constexpr int kNontemporal = 2;           // cache policy bit: nt
+constexpr int kOob = 0x7FFFFFF0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
 // An integer product chain that starts from kBiasBits instead of zero (a
 // group's first MFMA, or a chain of v_dot4) ends at 0x4B400000 + P.  Read as
 // a float those bits are exactly 1.5 * 2^23 + P whenever |P| < 2^22 (a
@@ -198,6 +209,11 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, uint8_t* q
 // matrix before quantising (the online rotation of QuaRot).
 hipError_t launch_quant(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa, float* sa,
                         hipStream_t st, bool hadamard = false);
+// The same codes and scales for 1 <= M <= 16 rows (K <= 65536), qa in the
+// [K / 16][16 rows][16 B] layout the M <= 16 GEMM reads as MFMA operands
+// (16 K bytes; rows M..15 left unwritten).
+hipError_t launch_quant_tiled(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* qa,
+                              float* sa, hipStream_t st, bool hadamard = false);
 hipError_t launch_w8_pack(const int8_t* qw, const float* sw, int64_t N, int64_t K, uint8_t* packed,
                           hipStream_t st);
 hipError_t launch_w8_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* qw, float* sw,
@@ -232,6 +248,9 @@ struct GemmArgs {
   // each group of 128 by the Walsh-Hadamard matrix first (hadamard_chunk), as
   // w4a8_quant_act_hadamard
   bool hadamard = false;
+  // qa in the [K / 16][16 rows][16 B] layout of launch_quant_tiled (skinny
+  // kernel, 12 <= M <= 16, no debug)
+  bool qa_tiled = false;
 };
 
 // Largest K the GEMV keeps in LDS (activation codes + per-quarter sums).

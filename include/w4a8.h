@@ -216,8 +216,11 @@ int w4a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
  * (N/16 >= the compute units and K <= 4096: whole 16-channel blocks per
  * workgroup, the activations staged once per workgroup); the SKINNY kernel
  * then quantises the rows into LDS.  Otherwise the codes are written to the
- * workspace and the GEMM of the selected path follows (two launches).  The
- * result is bitwise identical to w4a8_quant_act followed by w4a8_gemm.
+ * workspace and the GEMM of the selected path follows (two launches); for
+ * 12 <= M <= 16 on the SKINNY kernel (not its weight-streaming grid) the
+ * workspace holds them in an internal 16-row tiled layout that the kernel
+ * reads as matrix-core operands.  The result is bitwise identical to
+ * w4a8_quant_act followed by w4a8_gemm.
  *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
  *   y   device bfloat16 bits [M][N]
  *   workspace  device scratch of w4a8_linear_workspace_bytes(M, N, K, group)
@@ -394,7 +397,8 @@ int w8a8_gemm_debug(const int8_t* qa, const float* sa, const void* packed, size_
  * from raw activations; bitwise identical to w4a8_quant_act + w8a8_gemm.
  * At M == 1 (the GEMV) and for M <= 16 whose rows fit (the same limits as
  * w4a8_linear) it is one launch: the kernel quantises the rows into LDS
- * itself.
+ * itself.  Otherwise two launches through the workspace, which holds the
+ * codes for 14 <= M <= 16 in the 16-row tiled layout of w4a8_linear.
  *   x   device [M][K], bfloat16 (W4A8_BF16) or float (W4A8_F32)
  *   workspace  device scratch of w8a8_linear_workspace_bytes(M, N, K) bytes,
  *     required on every path

@@ -142,6 +142,24 @@ def test_linear_rejections(lib):
     assert lib.w4a8_linear_workspace_bytes(4, 256, 256, 128) >= 4 * 256 + 16
 
 
+def test_linear_workspace_codes_region(lib):
+    """The two-launch linear's workspace: the codes (16 K bytes in the tiled
+    layout at 12 <= M <= 16 on the M <= 16 kernel, else M K), the scales, then
+    the GEMM's own workspace."""
+    def r(v):
+        return (v + 255) // 256 * 256
+    gw = lib.w4a8_gemm_workspace_bytes
+    for M, K, N in ((16, 18944, 3584), (12, 18944, 3584), (13, 8192, 2048)):
+        assert lib.w4a8_linear_workspace_bytes(M, N, K, 128) == r(16 * K) + r(4 * M) + gw(M, N, K, 128)
+        assert lib.w4a8_linear_hadamard_workspace_bytes(M, N, K, 128) == \
+            r(16 * K) + r(4 * M) + gw(M, N, K, 128)
+    for M, K, N in ((8, 18944, 3584), (11, 18944, 3584), (17, 18944, 3584)):
+        assert lib.w4a8_linear_workspace_bytes(M, N, K, 128) == r(M * K) + r(4 * M) + gw(M, N, K, 128)
+    w8 = lib.w8a8_gemm_workspace_bytes
+    assert lib.w8a8_linear_workspace_bytes(16, 3584, 18944) == r(16 * 18944) + r(64) + w8(16, 3584, 18944)
+    assert lib.w8a8_linear_workspace_bytes(13, 3584, 18944) == r(13 * 18944) + r(52) + w8(13, 3584, 18944)
+
+
 def test_pack_into_rejections(lib):
     f = lib.w4a8_pack_weights_into
     big = 1 << 30
