@@ -53,12 +53,13 @@ CASES = [
     ("gemv_fused", 1, 3584, 4096, "w4a8"),
     ("gemv_split_k", 1, 18944, 512, "w4a8"),
     ("skinny_fused", 4, 3584, 2048, "w4a8"),
-    ("skinny_two_launch_split_k", 16, 18944, 1024, "w4a8"),
+    ("skinny_two_launch_split_k_tiled", 16, 18944, 1024, "w4a8"),
     ("skinny_stream_grid", 8, 3584, 18944, "w4a8"),
     ("prefill_narrow_split_k", 512, 3584, 512, "w4a8"),
     ("prefill_wide_half_tile_tail", 2048, 1024, 18944, "w4a8"),
     ("w8a8_prefill", 300, 1024, 4096, "w8a8"),
     ("w8a8_gemv", 1, 3584, 4096, "w8a8"),
+    ("w8a8_skinny_tiled", 16, 18944, 1024, "w8a8"),
     ("w4a16_skinny", 4, 3584, 2048, "w4a16"),
     ("w4a16_prefill", 300, 1024, 2048, "w4a16"),
     ("hadamard_gemv", 1, 3584, 2048, "hadamard"),
