@@ -97,15 +97,27 @@ def graph_launches_ms(torch, launch, n):
     return graph_steps_ms(torch, launch, min(n, 8), n) / n
 
 
+WARM_MS = 30.0  # least device time of untimed replays before a timed one
+
+
 def graph_steps_ms(torch, step, warmup, steps, spread=None):
     """Capture `steps` calls of step(i) in one HIP graph, replay it, and time
     the replay between a synchronize and events on the replay stream.  The
     untimed warmup replays that same graph max(1, ceil(warmup / steps))
-    times first (at least `warmup` steps): the first replay of a new graph
-    runs several per cent slower than later ones, a one-time cost that a
-    serving loop replaying its captured step never pays again.  With
-    spread=R the graph is replayed R more times after the timed replay, and
-    those replay times are kept for replay_spread(step, steps)."""
+    times first (at least `warmup` steps), and further until WARM_MS of
+    replays have run: the first replay of a new graph runs several per cent
+    slower than later ones, a one-time cost that a serving loop replaying
+    its captured step never pays again, and after the host-side work before
+    a measurement (the parity check against the oracle) the first few
+    milliseconds of kernels run at a lower clock.  After a synchronize, one
+    more untimed replay leads the timed one on the stream, and the events
+    bracket only the timed replay: its launch (about 10 us from the replay
+    call to the first kernel) overlaps the lead replay, as each step's does
+    in a serving loop that replays its captured step back to back, so the
+    events time exactly the K steps on the device.  With spread=R the graph
+    is replayed R more times after the timed replay, back to back, with an
+    event between consecutive replays, and those replay times are kept for
+    replay_spread(step, steps)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):                 # eager warmup outside capture
@@ -117,25 +129,29 @@ def graph_steps_ms(torch, step, warmup, steps, spread=None):
     with torch.cuda.graph(gt):
         for i in range(steps):
             step(i)
-    for _ in range(max(1, -(-warmup // steps))):
+    t0, n = time.perf_counter(), 0
+    while n < max(1, -(-warmup // steps)) or \
+            ((time.perf_counter() - t0) * 1e3 < WARM_MS and n < 100000):
         gt.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += 1
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gt.replay()                                # untimed lead replay
     e0.record()
     gt.replay()
     e1.record()
     torch.cuda.synchronize()
     first = e0.elapsed_time(e1)
     if spread:
-        times = []
-        for _ in range(spread):
-            e0.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(spread + 1)]
+        gt.replay()                            # untimed lead replay
+        ev[0].record()
+        for r in range(spread):
             gt.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        _SPREAD[id(step)] = times
+            ev[r + 1].record()
+        torch.cuda.synchronize()
+        _SPREAD[id(step)] = [ev[r].elapsed_time(ev[r + 1]) for r in range(spread)]
     return first
 
 
@@ -278,8 +294,8 @@ def bench_decode(torch, w4, args):
                      "kernel": f"w4a8 fused quant + {path} (M={M}, K={K}, N={N})",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(kern_ms * 1e3, 3),
-                     "timing": f"{args.steps} launches replayed from one HIP graph (after one untimed "
-                               "replay of it)"},
+                     "timing": f"{args.steps} launches replayed from one HIP graph (after untimed "
+                               "replays of it, the last leading the timed one on the stream)"},
         "floor": floor,
         "two_launch": {"us_per_step": round(two_ms * 1e3, 3),
                        "quant_kernel_us": round(quant_ms * 1e3, 3),
@@ -327,8 +343,8 @@ def bench_prefill(torch, w4, args):
                      "traffic": measured_traffic("w4a8_prefill_up_M2048_K3584_N18944_traffic.txt"),
                      "kernel": f"w4a8 prefill (M={M}, K={K}, N={N})",
                      "ops_per_launch": ops, "avg_launch_us": round(kern_ms * 1e3, 2),
-                     "timing": f"{n} launches replayed from one HIP graph (after one untimed "
-                               "replay of it)"},
+                     "timing": f"{n} launches replayed from one HIP graph (after untimed "
+                               "replays of it, the last leading the timed one on the stream)"},
     }
 
 
@@ -959,7 +975,9 @@ def main():
                    "input_sha256_16": synth.digest(dec["lin"]), "weight_copies": args.copies,
                    "bytes_per_step": dec["step_bytes"],
                    "timing": "one timed replay of a HIP graph of K steps, after max(1, ceil(W / K)) "
-                             "untimed replays of the same graph",
+                             "untimed replays of the same graph and at least %g ms of them; after "
+                             "a synchronize one untimed replay leads the timed one on the stream "
+                             "and events bracket the timed replay alone" % WARM_MS,
                    "parallelism": "single GPU"},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu_dec,
