@@ -86,11 +86,12 @@ def _paths(M):
 # GEMV and the M <= 16 kernel; the prefill's tail slices with a ragged last
 # column tile; a GEMV grid of several rounds; 256 x 256 tiles whose partial
 # round runs as 256 x 128 half tiles; the M <= 16 weight-streaming grid
-# (N / 16 >= compute units, K <= 4096) with a ragged block split
+# (N / 16 >= compute units, K <= 4096) with a ragged block split; the
+# two-launch linear with the codes in the 16-row tiled layout (12 <= M <= 16)
 SHAPES = [(1, 384, 208), (2, 384, 208), (5, 384, 208), (16, 384, 208), (17, 384, 208),
           (33, 384, 208), (129, 384, 208), (300, 384, 208), (1, 18944, 512), (8, 10240, 512),
           (300, 1024, 18992), (1, 3584, 38912), (2048, 1024, 9472),
-          (3, 1280, 4112), (16, 4096, 9600)]
+          (3, 1280, 4112), (16, 4096, 9600), (14, 18944, 208)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES, ids=[f"M{m}_K{k}_N{n}" for m, k, n in SHAPES])
@@ -140,7 +141,7 @@ def test_w4a8_guards(w4, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 384, 208), (4, 1024, 272), (17, 384, 208),
-                                   (300, 1024, 18992)])
+                                   (300, 1024, 18992), (16, 18944, 208)])
 def test_w8a8_and_w4a16_guards(w4, M, K, N):
     say(f"guards w8a8/w4a16 M={M} K={K} N={N}")
     spec = synth.LinearSpec(f"guard8_{M}_{K}_{N}", M, K, N, seed=700 + M + K + N)
