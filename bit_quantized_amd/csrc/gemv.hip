@@ -58,6 +58,7 @@ constexpr int kQ = 4;                       // quantiser wavefronts
 constexpr int kQWeight = 2;                 // run share of a quantiser (a streamer's is 4)
 constexpr int kShareTotal = kQ * kQWeight + (kWaves - kQ) * 4;
 constexpr int D = 4;                        // code blocks a wavefront keeps in flight
+constexpr int kDeepD = 6;                   // ... over a long token (see launch_ks)
 constexpr int kMaxRun = 12;                 // units per wavefront
 constexpr int kMaxCb = 12;                  // channel blocks per workgroup
 
@@ -182,7 +183,7 @@ __device__ __forceinline__ void wait_flag(uint32_t* s_sync) {
 // EARLY: the streamers' first code blocks go out beside the token's
 // requests instead of after the set-up barrier (chosen on the host).
 template <int XT, bool DEBUG, bool KSPLIT, int kQChunks, bool W8 = false, bool HAD = false,
-          bool EARLY = false>
+          bool EARLY = false, int DR = D>
 __global__ void __launch_bounds__(kThreads)
 gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
             const uint8_t* __restrict__ zeros, const void* __restrict__ xin, int K, int cb_q,
@@ -248,7 +249,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(codes + (nrun > 0 ? first : 0) * H * kBlockBytes), (short)0, oob,
       kBufferWord3);
-  uint4 wv[D][H];
+  uint4 wv[DR][H];
   int lu = u0, lg = 0, rel = 0;  // next unit to load (lg: its group within the slice)
   if constexpr (KSPLIT) lg = nrun > 0 ? u0 % gk : 0;
   uint4 s4;
@@ -263,7 +264,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
   if constexpr (EARLY) {
     if (wave >= kQ) {
 #pragma unroll
-      for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+      for (int i = 0; i < DR; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // the loads above issue before the set-up below
@@ -273,12 +274,12 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     for (int t = tid; t < 4 * G; t += kThreads) rs[t] = 0;
   if (tid < 4) s_sync[tid] = 0u;
   __syncthreads();
-  // otherwise the streamers' first D code blocks only now, so that every
+  // otherwise the streamers' first DR code blocks only now, so that every
   // quantiser's token requests are ahead of them in this compute unit's
   // memory queue (the token is on every wavefront's critical path)
   if (!EARLY && wave >= kQ) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
+    for (int i = 0; i < DR; ++i) load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
   }
 
   if (wave < kQ && A16) {
@@ -315,7 +316,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     if (lane == 0)
       __hip_atomic_fetch_add(&s_sync[2], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-    for (int i = 0; i < D; ++i)
+    for (int i = 0; i < DR; ++i)
       load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
     // this stager's run reads the token and sums the others staged: the
     // streamers' wait (below), which ends after the kQ increments
@@ -417,11 +418,11 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     // and sums the other quantisers wrote: it waits for them as the
     // streamers do (below), once its loads are in flight
 #pragma unroll
-    for (int i = 0; i < D; ++i)
+    for (int i = 0; i < DR; ++i)
       load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
     wait_flag(s_sync);
   } else {
-    // ---- streamer: metadata and D code blocks are in flight; the flag
+    // ---- streamer: metadata and DR code blocks are in flight; the flag
     // (an unbounded spin that ends once all kQ quantisers or stagers have
     // made their one increment of s_sync[2])
     if constexpr (XT == X_QUANTISED) scale = a.sa[0];
@@ -444,9 +445,9 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
     int ccb = nrun > 0 ? u0 / gk : 0, cg = nrun > 0 ? u0 % gk : 0;  // compute position
     int cur = ccb;
     const int zshift = (c & 1) * 4;
-    for (int ub = 0; ub < nrun; ub += D) {
+    for (int ub = 0; ub < nrun; ub += DR) {
 #pragma unroll
-      for (int i = 0; i < D; ++i) {
+      for (int i = 0; i < DR; ++i) {
         const int r = ub + i;  // position in the run
         if (r < nrun) {
           if (ccb != cur) {
@@ -534,7 +535,7 @@ gemv_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
           cg -= wrap * gk;
           ccb += wrap;
         }
-        // refill this slot with the unit D ahead
+        // refill this slot with the unit DR ahead
         load_next<H>(rsrc, oob, u1, G, gk, lane, lu, lg, rel, wv[i]);
       }
     }
@@ -602,6 +603,19 @@ hipError_t launch_ks(const GemmArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemv_kernel<XT, true, KSPLIT, QC, W8>), grid, dim3(kThreads), lds, st, a.w.codes,
                        a.w.scales, a.w.zeros, xin, (int)a.K, a.cb_q, a.cb_r, a);
     return hipGetLastError();
+  }
+  if constexpr (!KSPLIT && (XT == X_BF16 || XT == X_F32) && !W8 && QC >= 4) {
+    // A long token (at least 16384 inputs) keeps the streamers waiting for
+    // the flag longest: a deeper ring puts more of their runs in flight
+    // meanwhile (MI355X, K = 18944 -> N = 3584: 9.06 against 9.49 us).  On
+    // shorter tokens the extra requests only queue ahead of the token's
+    // (K = 3584 -> N = 18944: 8.62 against 7.94 us).
+    if (a.K >= 16384) {
+      hipLaunchKernelGGL((gemv_kernel<XT, false, false, QC, false, false, false, kDeepD>), grid,
+                         dim3(kThreads), lds, st, a.w.codes, a.w.scales, a.w.zeros, xin, (int)a.K,
+                         a.cb_q, a.cb_r, a);
+      return hipGetLastError();
+    }
   }
   if constexpr (!KSPLIT) {
     // One round of workgroups with long runs over a short token: the token's
